@@ -1,0 +1,230 @@
+"""Plain fp64 CPU oracle for the TTT-Linear / TTT-MLP mini-batch inner-loop scan.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this module. The product path (the HIP library and its
+Python binding) never calls it, and it shares no code with that path.
+
+What it computes (sources, by page title and section):
+
+* "Test-Time Training(TTT)과 LLM 메모리" (juhoplayground), section "TTT layer":
+  the layer keeps fast weights W as its hidden state, takes the self-supervised
+  loss l(W; x_t) = || f(theta_K x_t; W) - theta_V x_t ||^2 (Eq. 4), takes the step
+  W_t = W_{t-1} - eta * grad l (Eq. 2) and outputs z_t = f(theta_Q x_t; W_t) (Eq. 5).
+  The conceptual loop given there updates W *before* producing z_t.
+  TTT-Linear: f is linear with a square W; TTT-MLP: a two-layer MLP with a 4x
+  hidden width and GELU. Both include LayerNorm and a residual. The practical
+  devices are mini-batch TTT with b = 16, the dual form, a learnable W0 and a
+  learnable per-token eta.
+* Same page, section "재현성과 공개 구현": the stabilising form f(x) = x + LN(f_res(x)).
+* "LLM : 빠른 논문 리뷰 : End-to-End Test-Time Training for Long Context"
+  (aiflower), section 2.3, Eq. 5: in a mini-batch all gradients are taken at the
+  weights the mini-batch started from, and W is carried into the next mini-batch.
+
+Plain reading of open points (each also listed in the design notes):
+* eta is applied as given per token, as a plain (un-normalised) sum; eta_scale
+  multiplies every eta (1/b gives the 1/b form written in Eq. 5 of the E2E paper).
+* Inside a chunk, z_t uses W_t = W_start - sum_{s<=t} eta_s grad l_s(W_start),
+  i.e. token t's own step is included (update before output).
+* LayerNorm uses the biased variance and sigma = sqrt(var + eps).
+* gamma, beta (the LayerNorm affine) are outer-loop parameters, fixed in the scan.
+* No biases inside the fast MLP / linear map.
+* GELU is the exact erf form by default; the tanh form is an option.
+
+Layout (row vectors): Q, K, V are [N, T, d] with N = independent (batch, head)
+pairs. TTT-MLP: W1 [N, d, h], W2 [N, h, d], g(x) = GELU(x W1) W2. TTT-Linear:
+W [N, d, d], g(x) = x W. eta is [N, T]; gamma, beta are [N, d].
+
+The gradient of one token's loss is derived by hand below. It is written with
+ordinary differentiable torch ops, so torch.autograd can differentiate the whole
+scan again (gradients of gradients) for the outer-loop backward oracle.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+_TANH_C = math.sqrt(2.0 / math.pi)
+_TANH_A = 0.044715
+
+
+@dataclass(frozen=True)
+class OracleConfig:
+    """Static description of one scan.
+
+    kind: "mlp" or "linear".
+    chunk: mini-batch size b (T must be a multiple of it).
+    ln_eps: epsilon inside the LayerNorm square root.
+    gelu: "erf" (exact) or "tanh".
+    eta_scale: multiplies every per-token eta.
+    layer_norm / residual: both True for the layer as defined; switching both off
+        gives the plain map f(x) = g(x) used by the attention-equivalence checks.
+    """
+
+    kind: str = "mlp"
+    chunk: int = 16
+    ln_eps: float = 1e-6
+    gelu: str = "erf"
+    eta_scale: float = 1.0
+    layer_norm: bool = True
+    residual: bool = True
+
+
+# ----------------------------------------------------------------------------
+# Elementwise pieces
+# ----------------------------------------------------------------------------
+
+def gelu(x: torch.Tensor, kind: str = "erf") -> torch.Tensor:
+    """GELU(x) = x * Phi(x) (erf form) or the usual tanh approximation."""
+    if kind == "erf":
+        return 0.5 * x * (1.0 + torch.erf(x / _SQRT2))
+    if kind == "tanh":
+        return 0.5 * x * (1.0 + torch.tanh(_TANH_C * (x + _TANH_A * x ** 3)))
+    raise ValueError(kind)
+
+
+def gelu_prime(x: torch.Tensor, kind: str = "erf") -> torch.Tensor:
+    """d GELU / dx. erf form: Phi(x) + x * phi(x)."""
+    if kind == "erf":
+        cdf = 0.5 * (1.0 + torch.erf(x / _SQRT2))
+        pdf = torch.exp(-0.5 * x * x) * _INV_SQRT_2PI
+        return cdf + x * pdf
+    if kind == "tanh":
+        u = _TANH_C * (x + _TANH_A * x ** 3)
+        th = torch.tanh(u)
+        du = _TANH_C * (1.0 + 3.0 * _TANH_A * x * x)
+        return 0.5 * (1.0 + th) + 0.5 * x * (1.0 - th * th) * du
+    raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------
+# The fast-weight map f and one token's loss gradient
+# ----------------------------------------------------------------------------
+
+def inner_forward(x: torch.Tensor, W: tuple, cfg: OracleConfig):
+    """g(x; W) for row vectors x [N, d]. Returns (g, cache)."""
+    if cfg.kind == "mlp":
+        W1, W2 = W
+        a = torch.einsum("nd,ndh->nh", x, W1)
+        c = gelu(a, cfg.gelu)
+        g = torch.einsum("nh,nhd->nd", c, W2)
+        return g, (a, c)
+    (Wl,) = W
+    return torch.einsum("nd,nde->ne", x, Wl), None
+
+
+def layer_norm(z: torch.Tensor, gamma, beta, eps: float):
+    """LayerNorm over the last axis, biased variance. Returns (out, xhat, sigma)."""
+    mu = z.mean(dim=-1, keepdim=True)
+    var = ((z - mu) ** 2).mean(dim=-1, keepdim=True)
+    sigma = torch.sqrt(var + eps)
+    xhat = (z - mu) / sigma
+    return gamma * xhat + beta, xhat, sigma
+
+
+def f_apply(x: torch.Tensor, W: tuple, gamma, beta, cfg: OracleConfig) -> torch.Tensor:
+    """f(x; W) = x + LN(g(x; W)) (or the plain g(x; W) when LN/residual are off)."""
+    g, _ = inner_forward(x, W, cfg)
+    out = layer_norm(g, gamma, beta, cfg.ln_eps)[0] if cfg.layer_norm else g
+    return x + out if cfg.residual else out
+
+
+def token_loss_and_grad(x, y, W: tuple, gamma, beta, cfg: OracleConfig):
+    """l = ||f(x;W) - y||^2 and its gradient w.r.t. each fast weight.
+
+    Hand derivation (row vectors, per head):
+      z = g(x;W);  xhat = (z - mu)/sigma;  r = x + gamma*xhat + beta - y;  l = sum r^2
+      dl/dxhat = 2 r * gamma =: gg
+      dl/dz = (gg - mean(gg) - xhat * mean(gg * xhat)) / sigma =: delta2
+      MLP:    dl/dW2 = c^T delta2,   delta1 = (delta2 W2^T) * GELU'(a),  dl/dW1 = x^T delta1
+      Linear: dl/dW  = x^T delta2
+    The loss carries no 1/2 factor (Eq. 4 is the plain squared norm).
+    """
+    z, cache = inner_forward(x, W, cfg)
+    if cfg.layer_norm:
+        ln_out, xhat, sigma = layer_norm(z, gamma, beta, cfg.ln_eps)
+    else:
+        ln_out = z
+    pred = x + ln_out if cfg.residual else ln_out
+    r = pred - y
+    loss = (r * r).sum(dim=-1)
+    if cfg.layer_norm:
+        gg = 2.0 * r * gamma
+        delta2 = (gg - gg.mean(dim=-1, keepdim=True)
+                  - xhat * (gg * xhat).mean(dim=-1, keepdim=True)) / sigma
+    else:
+        delta2 = 2.0 * r
+    if cfg.kind == "mlp":
+        W1, W2 = W
+        a, c = cache
+        gW2 = torch.einsum("nh,nd->nhd", c, delta2)
+        delta1 = torch.einsum("nd,nhd->nh", delta2, W2) * gelu_prime(a, cfg.gelu)
+        gW1 = torch.einsum("nd,nh->ndh", x, delta1)
+        return loss, (gW1, gW2)
+    return loss, (torch.einsum("nd,ne->nde", x, delta2),)
+
+
+# ----------------------------------------------------------------------------
+# The scan
+# ----------------------------------------------------------------------------
+
+def scan(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig):
+    """Mini-batch TTT scan, primal and token by token.
+
+    For chunk i (tokens (i-1)b+1 .. ib), with W_start the weights carried in:
+      for each token t of the chunk, in order:
+        grad_t = grad l_t(W_start)                     (all gradients at the chunk start)
+        P     += eta_scale * eta_t * grad_t            (running sum, t included)
+        W_t    = W_start - P                           (materialised)
+        z_t    = f(Q_t; W_t)
+      carry W_start <- W_start - P.
+    Returns Z [N, T, d], the final weights (tuple) and the per-token loss [N, T]
+    l_t(W_start) (the reconstruction loss at the weights the gradient is taken at).
+    """
+    N, T, d = Q.shape
+    b = cfg.chunk
+    if T % b != 0:
+        raise ValueError("T must be a multiple of the chunk size")
+    W = tuple(w for w in W0)
+    Z = []
+    losses = []
+    for i in range(T // b):
+        W_start = W
+        P = tuple(torch.zeros_like(w) for w in W_start)
+        for t in range(i * b, (i + 1) * b):
+            loss, grads = token_loss_and_grad(K[:, t], V[:, t], W_start, gamma, beta, cfg)
+            step = cfg.eta_scale * eta[:, t].reshape(N, 1, 1)
+            P = tuple(p + step * gw for p, gw in zip(P, grads))
+            W_t = tuple(ws - p for ws, p in zip(W_start, P))
+            Z.append(f_apply(Q[:, t], W_t, gamma, beta, cfg))
+            losses.append(loss)
+        W = tuple(ws - p for ws, p in zip(W_start, P))
+    return torch.stack(Z, dim=1), W, torch.stack(losses, dim=1)
+
+
+def scan_outer_grads(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig,
+                     dZ, dW_T: tuple | None = None):
+    """Outer-loop backward by automatic differentiation through the scan.
+
+    L = sum(dZ * Z) + sum_k sum(dW_T[k] * W_T[k]). Because the scan's update is
+    itself a gradient, differentiating L w.r.t. W0, Q, K, V and eta takes gradients
+    of gradients (the outer loop of "LLM : 빠른 논문 리뷰 : End-to-End Test-Time
+    Training for Long Context", section 2.2). Returns a dict of fp64 tensors:
+    dQ, dK, dV, deta, dW0 (tuple), dgamma, dbeta.
+    """
+    leaves = [t.detach().clone().requires_grad_(True) for t in (Q, K, V, eta, gamma, beta)]
+    Wl = [w.detach().clone().requires_grad_(True) for w in W0]
+    q, k, v, e, gm, bt = leaves
+    Z, W_T, _ = scan(q, k, v, e, tuple(Wl), gm, bt, cfg)
+    L = (Z * dZ).sum()
+    if dW_T is not None:
+        for w, dw in zip(W_T, dW_T):
+            L = L + (w * dw).sum()
+    grads = torch.autograd.grad(L, leaves + Wl)
+    return {
+        "dQ": grads[0], "dK": grads[1], "dV": grads[2], "deta": grads[3],
+        "dgamma": grads[4], "dbeta": grads[5], "dW0": tuple(grads[6:]),
+    }

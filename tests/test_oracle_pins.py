@@ -1,0 +1,418 @@
+"""Pins of the fp64 CPU oracle against facts fixed by the pages and by mathematics.
+
+Each check is independent of the oracle's own formulas: library routines
+(torch.nn.functional.layer_norm / gelu, torch.autograd), finite differences,
+closed forms and hand-worked values (tests/golden/). A plausible mistake in the
+oracle (a dropped LayerNorm term, a wrong sign, the wrong weights for the gradient,
+an exclusive instead of inclusive prefix, a transposed operand) fails at least one.
+"""
+import json
+import math
+import os
+
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import OracleConfig, gelu, gelu_prime, scan, scan_outer_grads, token_loss_and_grad
+from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DT = torch.float64
+
+
+def _rand_inputs(N, T, d, h, kind, seed=0, w_scale=0.3, eta_base=0.2):
+    g = torch.Generator().manual_seed(seed)
+    Q = torch.randn(N, T, d, generator=g, dtype=DT)
+    K = torch.randn(N, T, d, generator=g, dtype=DT)
+    V = torch.randn(N, T, d, generator=g, dtype=DT)
+    eta = eta_base * torch.sigmoid(torch.randn(N, T, generator=g, dtype=DT))
+    if kind == "mlp":
+        W0 = (w_scale * torch.randn(N, d, h, generator=g, dtype=DT),
+              w_scale * torch.randn(N, h, d, generator=g, dtype=DT))
+    else:
+        W0 = (torch.eye(d, dtype=DT) + w_scale * torch.randn(N, d, d, generator=g, dtype=DT),)
+    gamma = 1.0 + 0.1 * torch.randn(N, d, generator=g, dtype=DT)
+    beta = 0.1 * torch.randn(N, d, generator=g, dtype=DT)
+    return Q, K, V, eta, W0, gamma, beta
+
+
+# ---------------------------------------------------------------------------
+# Independent reference pieces built from library routines
+# ---------------------------------------------------------------------------
+
+def lib_f(x, W, gamma, beta, kind, eps, gelu_kind="erf", layer_norm=True, residual=True):
+    """f(x;W) = x + LN(g(x;W)) from torch.nn.functional, one head: x [d] or [n, d]."""
+    if kind == "mlp":
+        g = F.gelu(x @ W[0], approximate="none" if gelu_kind == "erf" else "tanh") @ W[1]
+    else:
+        g = x @ W[0]
+    out = F.layer_norm(g, (g.shape[-1],), gamma, beta, eps) if layer_norm else g
+    return x + out if residual else out
+
+
+def lib_scan(Q, K, V, eta, W0, gamma, beta, kind, b, eps, eta_scale=1.0, gelu_kind="erf",
+             layer_norm=True, residual=True):
+    """Mini-batch TTT with autograd gradients at the chunk-start weights (one head at a time).
+    With b = 1 this is the sequential loop of Eq. 2/4/5 (loss, then step, then output)."""
+    N, T, d = Q.shape
+    Zs, WTs = [], []
+    for n in range(N):
+        W = [w[n].clone() for w in W0]
+        zs = []
+        for c0 in range(0, T, b):
+            Wstart = [w.clone().requires_grad_(True) for w in W]
+            grads = []
+            for t in range(c0, c0 + b):
+                pred = lib_f(K[n, t], Wstart, gamma[n], beta[n], kind, eps, gelu_kind,
+                             layer_norm, residual)
+                loss = ((pred - V[n, t]) ** 2).sum()
+                grads.append(torch.autograd.grad(loss, Wstart))
+            P = [torch.zeros_like(w) for w in W]
+            for j, t in enumerate(range(c0, c0 + b)):
+                P = [p + eta_scale * eta[n, t] * gw for p, gw in zip(P, grads[j])]
+                Wt = [ws.detach() - p for ws, p in zip(Wstart, P)]
+                zs.append(lib_f(Q[n, t], Wt, gamma[n], beta[n], kind, eps, gelu_kind,
+                                layer_norm, residual).detach())
+            W = [ws.detach() - p for ws, p in zip(Wstart, P)]
+        Zs.append(torch.stack(zs))
+        WTs.append(W)
+    return torch.stack(Zs), tuple(torch.stack([w[k] for w in WTs]) for k in range(len(W0)))
+
+
+def rel(a, b):
+    return ((a - b).norm() / b.norm()).item()
+
+
+# ---------------------------------------------------------------------------
+# Elementwise pieces
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["erf", "tanh"])
+def test_gelu_matches_library(kind):
+    x = torch.linspace(-8, 8, 2001, dtype=DT)
+    ref = F.gelu(x, approximate="none" if kind == "erf" else "tanh")
+    assert torch.allclose(gelu(x, kind), ref, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind", ["erf", "tanh"])
+def test_gelu_prime_finite_difference(kind):
+    x = torch.linspace(-6, 6, 1201, dtype=DT)
+    h = 1e-5
+    fd = (gelu(x + h, kind) - gelu(x - h, kind)) / (2 * h)
+    assert torch.allclose(gelu_prime(x, kind), fd, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# One token's gradient (the K-side chain of every chunk)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_token_grad_central_finite_differences(kind):
+    d, h = 4, 16
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(1, 2, d, h, kind, seed=3)
+    cfg = OracleConfig(kind=kind, chunk=1)
+    x, y = K[:, 0], V[:, 0]
+    _, grads = token_loss_and_grad(x, y, W0, gamma, beta, cfg)
+
+    def loss_at(W):
+        return token_loss_and_grad(x, y, W, gamma, beta, cfg)[0].item()
+
+    for k, w in enumerate(W0):
+        step = 1e-6 * max(1.0, w.abs().max().item())
+        fd = torch.zeros_like(w)
+        flat = w.reshape(-1)
+        for i in range(flat.numel()):
+            Wp = [ww.clone() for ww in W0]
+            Wm = [ww.clone() for ww in W0]
+            Wp[k].view(-1)[i] += step
+            Wm[k].view(-1)[i] -= step
+            fd.view(-1)[i] = (loss_at(tuple(Wp)) - loss_at(tuple(Wm))) / (2 * step)
+        assert rel(grads[k], fd) <= 1e-7, (k, rel(grads[k], fd))
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+@pytest.mark.parametrize("gelu_kind", ["erf", "tanh"])
+def test_token_grad_matches_autograd_of_library_layer(kind, gelu_kind):
+    d, h = 8, 32
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(3, 1, d, h, kind, seed=4)
+    cfg = OracleConfig(kind=kind, chunk=1, gelu=gelu_kind, ln_eps=1e-5)
+    loss, grads = token_loss_and_grad(K[:, 0], V[:, 0], W0, gamma, beta, cfg)
+    for n in range(3):
+        Wn = [w[n].clone().requires_grad_(True) for w in W0]
+        pred = lib_f(K[n, 0], Wn, gamma[n], beta[n], kind, 1e-5, gelu_kind)
+        ln = ((pred - V[n, 0]) ** 2).sum()
+        ag = torch.autograd.grad(ln, Wn)
+        assert abs(ln.item() - loss[n].item()) <= 1e-12 * max(1.0, abs(ln.item()))
+        for k in range(len(W0)):
+            assert rel(grads[k][n], ag[k]) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_layernorm_scale_invariance_orthogonality(kind):
+    """With eps = 0, LN(g) is invariant to scaling the last weight matrix, so the
+    loss gradient w.r.t. that matrix is orthogonal to it (Frobenius)."""
+    d, h = 8, 32
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(4, 16, d, h, kind, seed=5)
+    cfg = OracleConfig(kind=kind, chunk=16, ln_eps=0.0)
+    last = W0[-1]
+    total = torch.zeros_like(last)
+    for t in range(16):
+        _, grads = token_loss_and_grad(K[:, t], V[:, t], W0, gamma, beta, cfg)
+        ip = (grads[-1] * last).sum(dim=(1, 2))
+        assert ip.abs().max().item() <= 1e-10 * grads[-1].norm().item() * last.norm().item()
+        total = total + eta[:, t].reshape(-1, 1, 1) * grads[-1]
+    ip = (total * last).sum(dim=(1, 2))
+    assert ip.abs().max().item() <= 1e-10 * total.norm().item() * last.norm().item()
+
+
+# ---------------------------------------------------------------------------
+# The scan
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_eta_zero_gives_initial_map(kind):
+    d, h, T = 8, 32, 32
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=6)
+    cfg = OracleConfig(kind=kind, chunk=8)
+    Z, WT, _ = scan(Q, K, V, torch.zeros_like(eta), W0, gamma, beta, cfg)
+    for n in range(2):
+        ref = lib_f(Q[n], [w[n] for w in W0], gamma[n], beta[n], kind, cfg.ln_eps)
+        assert torch.allclose(Z[n], ref, rtol=1e-13, atol=1e-13)
+    for w, w0 in zip(WT, W0):
+        assert torch.equal(w, w0)
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_fixed_point_targets_leave_weights_unchanged(kind):
+    """V := f(K; W0) makes every inner gradient vanish, whatever eta is."""
+    d, h, T = 8, 32, 32
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=7)
+    V = torch.stack([lib_f(K[n], [w[n] for w in W0], gamma[n], beta[n], kind, 1e-6)
+                     for n in range(2)])
+    cfg = OracleConfig(kind=kind, chunk=8)
+    Z, WT, loss = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    for n in range(2):
+        ref = lib_f(Q[n], [w[n] for w in W0], gamma[n], beta[n], kind, 1e-6)
+        assert torch.allclose(Z[n], ref, rtol=1e-11, atol=1e-11)
+    for w, w0 in zip(WT, W0):
+        assert torch.allclose(w, w0, rtol=0, atol=1e-12)
+    assert loss.abs().max().item() <= 1e-20
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_b1_equals_sequential_loop(kind):
+    """b = 1 recovers the per-token update (section 2.3 of the E2E paper review):
+    compare with the loss -> step -> output loop written with autograd."""
+    d, h, T = 4, 16, 12
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=8)
+    cfg = OracleConfig(kind=kind, chunk=1)
+    Z, WT, _ = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    Zr, WTr = lib_scan(Q, K, V, eta, W0, gamma, beta, kind, 1, cfg.ln_eps)
+    assert rel(Z, Zr) <= 1e-12
+    for a, b in zip(WT, WTr):
+        assert rel(a, b) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+@pytest.mark.parametrize("gelu_kind", ["erf", "tanh"])
+def test_minibatch_matches_autograd_reference(kind, gelu_kind):
+    d, h, T, b = 4, 16, 12, 4
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=9)
+    cfg = OracleConfig(kind=kind, chunk=b, eta_scale=0.25, gelu=gelu_kind, ln_eps=1e-5)
+    Z, WT, _ = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    Zr, WTr = lib_scan(Q, K, V, eta, W0, gamma, beta, kind, b, 1e-5, eta_scale=0.25,
+                       gelu_kind=gelu_kind)
+    assert rel(Z, Zr) <= 1e-12
+    for a, b_ in zip(WT, WTr):
+        assert rel(a, b_) <= 1e-12
+
+
+def test_minibatch_differs_from_online():
+    """Gradients at the chunk start are not the per-token rule (guards against a scan
+    that silently re-evaluates the gradient at W_{t-1})."""
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(1, 8, 4, 16, "mlp", seed=10)
+    Z4 = scan(Q, K, V, eta, W0, gamma, beta, OracleConfig(chunk=4))[0]
+    Z1 = scan(Q, K, V, eta, W0, gamma, beta, OracleConfig(chunk=1))[0]
+    assert torch.equal(Z4[:, 0], Z1[:, 0])   # first token: identical by construction
+    assert rel(Z4[:, 1:4], Z1[:, 1:4]) > 1e-6
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def test_golden_theorem1_linear_attention():
+    g = _golden("theorem1_linear_attention.json")
+    q = torch.tensor(g["q"], dtype=DT)[None]
+    k = torch.tensor(g["k"], dtype=DT)[None]
+    v = torch.tensor(g["v"], dtype=DT)[None]
+    eta = torch.tensor(g["eta"], dtype=DT)[None]
+    T, d = q.shape[1:]
+    cfg = OracleConfig(kind="linear", chunk=T, layer_norm=False, residual=False)
+    Z, _, _ = scan(q, k, v, eta, (torch.zeros(1, d, d, dtype=DT),), None, None, cfg)
+    assert torch.allclose(Z[0], torch.tensor(g["expected_z"], dtype=DT), rtol=0, atol=1e-14)
+
+
+def test_theorem1_random_and_online_breaks_it():
+    """Theorem 1 on random data: batch GD from W0 = 0 with eta = 1/2 equals causal
+    linear attention; the online rule (b = 1) does not."""
+    N, T, d = 3, 16, 6
+    g = torch.Generator().manual_seed(11)
+    q, k, v = (torch.randn(N, T, d, generator=g, dtype=DT) for _ in range(3))
+    eta = torch.full((N, T), 0.5, dtype=DT)
+    W0 = (torch.zeros(N, d, d, dtype=DT),)
+    lin = torch.einsum("ntd,nsd->nts", q, k).tril() @ v
+    cfg = OracleConfig(kind="linear", chunk=T, layer_norm=False, residual=False)
+    assert rel(scan(q, k, v, eta, W0, None, None, cfg)[0], lin) <= 1e-13
+    cfg1 = OracleConfig(kind="linear", chunk=1, layer_norm=False, residual=False)
+    assert rel(scan(q, k, v, eta, W0, None, None, cfg1)[0], lin) > 1e-3
+
+
+def test_golden_delta_rule():
+    g = _golden("delta_rule_online.json")
+    q, k, v = (torch.tensor(g[n], dtype=DT)[None] for n in ("q", "k", "v"))
+    eta = torch.tensor(g["eta"], dtype=DT)[None]
+    cfg = OracleConfig(kind="linear", chunk=1, layer_norm=False, residual=False)
+    Z, WT, _ = scan(q, k, v, eta, (torch.zeros(1, 1, 1, dtype=DT),), None, None, cfg)
+    assert torch.allclose(Z[0], torch.tensor(g["expected_z"], dtype=DT), rtol=0, atol=1e-14)
+    assert torch.allclose(WT[0][0], torch.tensor(g["expected_W_T"], dtype=DT), atol=1e-14)
+
+
+def test_delta_rule_random():
+    N, T, d = 2, 10, 5
+    g = torch.Generator().manual_seed(12)
+    q, k, v = (torch.randn(N, T, d, generator=g, dtype=DT) for _ in range(3))
+    eta = 0.1 * torch.rand(N, T, generator=g, dtype=DT)
+    W = torch.randn(N, d, d, generator=g, dtype=DT)
+    cfg = OracleConfig(kind="linear", chunk=1, layer_norm=False, residual=False)
+    Z, WT, _ = scan(q, k, v, eta, (W.clone(),), None, None, cfg)
+    for n in range(N):
+        Wn = W[n].clone()
+        for t in range(T):
+            kt, vt = k[n, t:t + 1], v[n, t:t + 1]
+            Wn = Wn - 2 * eta[n, t] * kt.T @ (kt @ Wn - vt)
+            assert torch.allclose(Z[n, t], (q[n, t:t + 1] @ Wn)[0], rtol=1e-12, atol=1e-12)
+        assert torch.allclose(WT[0][n], Wn, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_weights_carry_across_a_split(kind):
+    """scan(2b) == scan(b) followed by scan(b) from the carried weights, bitwise."""
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, 16, 8, 32, kind, seed=13)
+    cfg = OracleConfig(kind=kind, chunk=8)
+    Z, WT, L = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    Za, Wa, La = scan(Q[:, :8], K[:, :8], V[:, :8], eta[:, :8], W0, gamma, beta, cfg)
+    Zb, Wb, Lb = scan(Q[:, 8:], K[:, 8:], V[:, 8:], eta[:, 8:], Wa, gamma, beta, cfg)
+    assert torch.equal(Z, torch.cat([Za, Zb], 1))
+    assert torch.equal(L, torch.cat([La, Lb], 1))
+    for a, b in zip(WT, Wb):
+        assert torch.equal(a, b)
+
+
+def test_heads_are_independent():
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(4, 16, 8, 32, "mlp", seed=14)
+    cfg = OracleConfig(chunk=8)
+    Z, WT, _ = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    p = torch.tensor([2, 0, 3, 1])
+    Zp, WTp, _ = scan(Q[p], K[p], V[p], eta[p], tuple(w[p] for w in W0), gamma[p], beta[p], cfg)
+    assert torch.allclose(Zp, Z[p], rtol=1e-14, atol=1e-14)
+    for a, b in zip(WTp, WT):
+        assert torch.allclose(a, b[p], rtol=1e-14, atol=1e-14)
+
+
+def test_eta_scale_is_a_uniform_rescale():
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, 16, 8, 32, "mlp", seed=15)
+    Za = scan(Q, K, V, eta, W0, gamma, beta, OracleConfig(chunk=16, eta_scale=1 / 16))[0]
+    Zb = scan(Q, K, V, eta / 16, W0, gamma, beta, OracleConfig(chunk=16))[0]
+    assert rel(Za, Zb) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Outer-loop backward (gradients of gradients)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_outer_grads_finite_differences(kind):
+    """Autograd through the scan against central differences at T = 64, along 10
+    random directions per input (W0, Q, K, V, eta)."""
+    N, T, d, h, b = 1, 64, 4, 16, 16
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(N, T, d, h, kind, seed=16, w_scale=0.4)
+    g = torch.Generator().manual_seed(17)
+    dZ = torch.randn(N, T, d, generator=g, dtype=DT)
+    dWT = tuple(torch.randn(w.shape, generator=g, dtype=DT) for w in W0)
+    cfg = OracleConfig(kind=kind, chunk=b, ln_eps=1e-5)
+    grads = scan_outer_grads(Q, K, V, eta, W0, gamma, beta, cfg, dZ, dWT)
+
+    def L(Qx, Kx, Vx, ex, Wx, gx, bx):
+        Z, WT, _ = scan(Qx, Kx, Vx, ex, Wx, gx, bx, cfg)
+        return (Z * dZ).sum().item() + sum((w * dw).sum().item() for w, dw in zip(WT, dWT))
+
+    base = dict(Q=Q, K=K, V=V, eta=eta, gamma=gamma, beta=beta)
+    names = ["Q", "K", "V", "eta", "gamma", "beta"] + [f"W0_{i}" for i in range(len(W0))]
+    for name in names:
+        for _ in range(10):
+            if name.startswith("W0"):
+                i = int(name[3:])
+                u = torch.randn(W0[i].shape, generator=g, dtype=DT)
+                an = (grads["dW0"][i] * u).sum().item()
+            else:
+                u = torch.randn(base[name].shape, generator=g, dtype=DT)
+                an = (grads["d" + name] * u).sum().item()
+            eps = 1e-6
+            vals = []
+            for s in (eps, -eps):
+                args = dict(base)
+                Ws = list(W0)
+                if name.startswith("W0"):
+                    Ws[i] = W0[i] + s * u
+                else:
+                    args[name] = base[name] + s * u
+                vals.append(L(args["Q"], args["K"], args["V"], args["eta"], tuple(Ws),
+                              args["gamma"], args["beta"]))
+            fd = (vals[0] - vals[1]) / (2 * eps)
+            assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), (name, an, fd)
+
+
+# ---------------------------------------------------------------------------
+# The seeded input generator (shared by both sides)
+# ---------------------------------------------------------------------------
+
+def test_synth_is_deterministic_and_subset_consistent():
+    w = WORKLOADS[3].with_(T=64)
+    a = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 5])
+    b = make_inputs(w, batch_idx=[1], head_idx=[5], T=32)
+    c = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 5])
+    for k in ("Q", "K", "V", "eta"):
+        assert torch.equal(a[k], c[k])
+        assert torch.equal(a[k][1, 1, :32], b[k][0, 0])
+    for x, y in zip(a["W0"], b["W0"]):
+        assert torch.equal(x[1], y[0])
+    assert a["Q"].dtype == torch.bfloat16 and a["eta"].dtype == torch.float32
+
+
+def test_synth_distributions():
+    w = WORKLOADS[3]
+    inp = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=4096)
+    q = inp["Q"].double()
+    assert abs(q.var().item() * w.d - 1.0) < 0.02
+    eta = inp["eta"].double()
+    assert 0.0 < eta.min().item() and eta.max().item() < w.eta_base
+    assert abs(eta.mean().item() - 0.5 * w.eta_base) < 0.01 * w.eta_base
+    assert abs(inp["W0"][0].double().std().item() - 0.02) < 0.001
+    # AR(1) drift: lag-1 correlation close to rho, marginal variance kept at 1/d
+    w4 = WORKLOADS[4]
+    k = make_inputs(w4, batch_idx=[0], head_idx=[0], T=8192)["K"].double()[0, 0]
+    corr = (k[1:] * k[:-1]).mean() / (k * k).mean()
+    assert abs(corr.item() - 0.999) < 0.002
+    assert 0.5 < k.var().item() * w4.d < 1.5
+
+
+def test_flatten_heads_broadcasts_w0_over_batch():
+    w = WORKLOADS[2].with_(T=32)
+    inp = make_inputs(w, batch_idx=[0, 2], head_idx=[1, 3, 4])
+    flat = flatten_heads(inp)
+    assert flat["Q"].shape == (6, 32, 64)
+    assert torch.equal(flat["W0"][0][0], flat["W0"][0][3])
+    assert torch.equal(flat["Q"][4], inp["Q"][1, 1].double())
