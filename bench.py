@@ -1,0 +1,185 @@
+"""Benchmark: TTT-MLP forward scan throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: TTT-MLP scan, B=8, H=12, T=8192, d=64, hidden=256, chunk 16, bf16 Q/K/V/Z,
+fp32 fast weights (synthetic, seeded inputs resident in HBM before timing starts).
+A step is one ttt_scan_fwd call over the whole batch. Prints one JSON line with
+token*heads/s, the dominant kernel's achieved fraction of the MI355X dense bf16 MFMA
+peak (algorithmic FLOPs / measured kernel time), and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3
+WORKLOAD_ID = 3
+
+
+def flops_per_token_head(d: int, h: int, b: int) -> int:
+    # seven d*h-sized products (2 FLOP per MAC) + the four b-sized dual-form products
+    return 14 * d * h + 4 * b * (d + h)
+
+
+def bytes_per_token_head(d: int, io_bytes: int, nW: int, T: int) -> float:
+    # Q, K, V in, Z out (io dtype), eta (fp32), W0 read + W_T written, amortised over T
+    return 4 * d * io_bytes + 4 + 2 * nW * 4 / T
+
+
+def _source_hash(kernel: str) -> str:
+    src = os.path.join(ROOT, "test_weight_sequence_amd", "csrc",
+                       "ttt_fwd_mfma.hip" if kernel == "ttt_fwd_mfma_d64" else "ttt_fwd_generic.hip")
+    with open(src, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, n_launch_units: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != _source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_heads: int, T: int) -> dict:
+    import torch
+    from oracle import OracleConfig, scan
+    from test_weight_sequence_amd.synth import flatten_heads, make_inputs
+    torch.set_num_threads(max(1, torch.get_num_threads()))
+    cores = torch.get_num_threads()
+    hi = list(range(n_heads))
+    inp = flatten_heads(make_inputs(w, batch_idx=[0], head_idx=hi, T=T))
+    cfg = OracleConfig(kind=w.kind, chunk=w.chunk)
+    t0 = time.perf_counter()
+    scan(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"], inp["beta"], cfg)
+    dt = time.perf_counter() - t0
+    return {"value": n_heads * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle on {n_heads} heads x T={T} of the same workload "
+                      f"({dt:.1f} s wall, torch intra-op threads={cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-T", type=int, default=1024)
+    ap.add_argument("--force-generic", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the scan's heads would be "
+              "sharded across GPUs with no communication, which is not built here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[WORKLOAD_ID]
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
+                     io=w.io, force_generic=args.force_generic)
+    kernel = ops.fwd_kernel_name(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w)
+    d = {k: (tuple(x.to(dev) for x in v) if isinstance(v, tuple) else v.to(dev))
+         for k, v in inp.items()}
+    del inp
+    ws = ops.new_workspace(cfg, ops.TTT_OP_FWD, dev)
+    Z = torch.empty(w.B, w.H, w.T, w.d, dtype=cfg.io_dtype, device=dev)
+    WT = tuple(torch.empty(s, device=dev) for s in cfg.weight_shapes((w.B, w.H)))
+
+    # One step = one ttt_scan_fwd call; arguments are marshalled once, outside the
+    # timed region.
+    import ctypes
+    cfg_struct = cfg.c()
+    cfg_c = ctypes.byref(cfg_struct)
+    P = ctypes.c_void_p
+    ptrs = [P(d[k].data_ptr()) for k in ("Q", "K", "V", "eta", "gamma", "beta")]
+    ptrs.append(ctypes.byref(ops.CWeights(d["W0"][0].data_ptr(), d["W0"][1].data_ptr())))
+    ptrs.append(P(Z.data_ptr()))
+    wt_arg = ctypes.byref(ops.CWeights(WT[0].data_ptr(), WT[1].data_ptr()))
+    ws_ptr = P(ws.data_ptr())
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    fwd = ops.lib().ttt_scan_fwd
+
+    def step():
+        return fwd(cfg_c, *ptrs, wt_arg, None, None, ws_ptr, ws.numel(), stream)
+
+    for _ in range(args.warmup):
+        rc = step()
+        if rc != 0:
+            raise ops.TTTError(rc, "ttt_scan_fwd")
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_step = wall * 1e3 / args.steps
+    k_avg = statistics.fmean(kms)
+    units = w.B * w.H * w.T
+    value = units / (ms_step * 1e-3)
+    flop = units * flops_per_token_head(w.d, w.hidden, w.chunk)
+    achieved = flop / (k_avg * 1e-3) / 1e12
+    mfma = kernel == "ttt_fwd_mfma_d64"
+    peak = PEAK_BF16_TFLOPS
+    io_bytes = 2 if w.io == "bf16" else 4
+    traffic = _traffic(kernel, units)
+    out = {
+        "metric": "TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)",
+        "value": value,
+        "unit": "token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mfma else "f32",
+        "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) W0, eta=0.1*sigmoid(N(0,1)))",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
+                   "hidden": w.hidden, "chunk": w.chunk, "io": w.io, "state": "fp32",
+                   "kernel": kernel},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel_ms": k_avg, "kernel_ms_min": min(kms),
+                     "flop_per_launch": flop,
+                     "algorithmic_bytes_per_launch": units * bytes_per_token_head(
+                         w.d, io_bytes, 2 * w.d * w.hidden, w.T)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads, args.cpu_T)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * ttt.h -- C ABI of libttt.so, the MI355X (gfx950) TTT inner-loop scan.
+ *
+ * The operation (per independent (batch, head) pair) is the mini-batch test-time
+ * training scan of a TTT-Linear or TTT-MLP fast-weight layer, as defined on the page
+ * "Test-Time Training(TTT)과 LLM 메모리" (juhoplayground), section "TTT layer"
+ * (update Eq. 2, loss Eq. 4, output Eq. 5, TTT-Linear / TTT-MLP, mini-batch b = 16,
+ * dual form, learnable W0 and eta), with the stabilising form f(x) = x + LN(f_res(x))
+ * from section "재현성과 공개 구현" of the same page, and the mini-batch rule of
+ * "LLM : 빠른 논문 리뷰 : End-to-End Test-Time Training for Long Context"
+ * (aiflower), section 2.3, Eq. 5 (all gradients of a mini-batch taken at the weights
+ * the mini-batch starts from; weights carried into the next mini-batch):
+ *
+ *   g(x;W) = GELU(x W1) W2   (MLP: W1 [d, hidden], W2 [hidden, d], hidden = 4d)
+ *   g(x;W) = x W             (Linear: W [d, d])
+ *   f(x;W) = x + LN(g(x;W)),  LN(z) = gamma * (z - mean) / sqrt(var + eps) + beta
+ *   l_t(W) = || f(K_t;W) - V_t ||^2
+ *   in chunk i, for token t:  W_t = W_start - eta_scale * sum_{s in chunk, s <= t} eta_s grad l_s(W_start)
+ *                             z_t = f(Q_t; W_t);   W carried = W at the chunk's last token.
+ *
+ * Row-vector convention. All arithmetic on the weights is fp32 on the device.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers to tensors are DEVICE pointers; all tensors are dense and row-major
+ *    (last axis fastest). Q, K, V, Z (and dQ, dK, dV, dZ) are [B, H, T, d] in the
+ *    I/O dtype (fp32 or bf16); eta is [B, H, T] fp32; gamma, beta are [H, d] fp32;
+ *    fast weights are fp32: W0 is [H, ...] shared over B, or [B, H, ...] with
+ *    TTT_W0_PER_SEQ; W_T is always [B, H, ...].
+ *  - Ownership: the caller allocates and frees every buffer (tensors and
+ *    workspace). The library never allocates device memory and keeps no pointer
+ *    after a call returns.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    Every call only enqueues work on it and returns; nothing synchronises the
+ *    stream except ttt_read_status.
+ *  - Errors: every argument, shape, dtype, alignment (16 bytes) and workspace check
+ *    runs on the host before anything is enqueued, so a non-OK return means nothing
+ *    ran. A failed launch returns TTT_ERR_HIP. A non-finite loss or output detected
+ *    inside a kernel is OR-ed into a status word in the workspace (sticky until
+ *    ttt_reset_status); ttt_read_status reports it as TTT_ERR_NONFINITE.
+ *  - No C++ exception crosses this interface. Calls that share a workspace must be
+ *    ordered on one stream.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_NULL = 1,        /* a required pointer is NULL                            */
+  TTT_ERR_SHAPE = 2,       /* non-positive size, T not a multiple of chunk, ...     */
+  TTT_ERR_DTYPE = 3,       /* unknown io_dtype                                      */
+  TTT_ERR_UNSUPPORTED = 4, /* a combination no kernel is built for                  */
+  TTT_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned               */
+  TTT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than ttt_workspace_size     */
+  TTT_ERR_HIP = 7,         /* a HIP runtime call failed                             */
+  TTT_ERR_NONFINITE = 8,   /* a kernel saw a NaN/Inf loss or output                 */
+  TTT_ERR_ARG = 9          /* any other bad argument (unknown op, pos_in_chunk ...) */
+} ttt_status;
+
+enum { TTT_LINEAR = 0, TTT_MLP = 1 };
+enum { TTT_F32 = 0, TTT_BF16 = 1 };
+enum { TTT_GELU_ERF = 0, TTT_GELU_TANH = 1 };
+/* ttt_config.flags */
+enum {
+  TTT_W0_PER_SEQ = 1 << 0,    /* W0 (and dW0) are [B, H, ...] instead of [H, ...]         */
+  TTT_FORCE_GENERIC = 1 << 1  /* use the portable fp32 kernel even where a tuned one exists */
+};
+/* op codes for ttt_workspace_size */
+enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2 };
+
+typedef struct {
+  int32_t kind;      /* TTT_LINEAR or TTT_MLP                                         */
+  int32_t B, H, T;   /* batch, heads, tokens (T ignored by ttt_decode_step)           */
+  int32_t d;         /* head dimension: 16 <= d <= 128, multiple of 16                */
+  int32_t hidden;    /* MLP hidden width, must be 4*d; ignored for TTT_LINEAR         */
+  int32_t chunk;     /* mini-batch size b, 1 <= b <= 16; T % b == 0 for scans          */
+  int32_t io_dtype;  /* TTT_F32 or TTT_BF16 for Q, K, V, Z, dQ, dK, dV, dZ             */
+  int32_t gelu;      /* TTT_GELU_ERF (exact) or TTT_GELU_TANH                          */
+  int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC                             */
+  float ln_eps;      /* LayerNorm epsilon inside the square root (e.g. 1e-6)           */
+  float eta_scale;   /* multiplies every eta_t (1 = plain sum; 1/b = averaged sum)     */
+} ttt_config;
+
+/* Fast weights, fp32 device pointers. MLP: w1 [.., d, hidden], w2 [.., hidden, d].
+ * Linear: w1 [.., d, d], w2 unused (may be NULL). */
+typedef struct {
+  float* w1;
+  float* w2;
+} ttt_weights;
+
+/* Host-only check of a configuration (no HIP call). */
+ttt_status ttt_validate(const ttt_config* cfg);
+
+/* Bytes of workspace the op needs (TTT_OP_FWD / TTT_OP_BWD / TTT_OP_DECODE).
+ * Host only. The first 256 bytes of every workspace hold the status word; the
+ * caller zero-fills a new workspace once (or calls ttt_reset_status). */
+ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes);
+
+/* Bytes of the `saved` buffer ttt_scan_fwd fills for ttt_scan_bwd: the fp32 fast
+ * weights at the start of every chunk, [B, H, T/chunk, weights]. Host only. */
+ttt_status ttt_saved_size(const ttt_config* cfg, size_t* bytes);
+
+/* Forward scan over T tokens for every (batch, head).
+ *  Q, K, V [B,H,T,d] io dtype; eta [B,H,T]; ln_gamma, ln_beta [H,d]; W0 as above.
+ *  Z [B,H,T,d] io dtype (written).
+ *  W_T   (nullable): final weights, [B,H,...] (written).
+ *  loss  (nullable): [B,H,T] fp32, l_t at the chunk-start weights (written).
+ *  saved (nullable): ttt_saved_size bytes, needed by ttt_scan_bwd (written).
+ *  Definition: the page "Test-Time Training(TTT)과 LLM 메모리", section "TTT layer",
+ *  Eq. 2/4/5 with mini-batches as in the E2E paper review, section 2.3, Eq. 5. */
+ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const float* ln_gamma, const float* ln_beta,
+                        const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                        void* saved, void* workspace, size_t ws_bytes, void* stream);
+
+/* Outer-loop backward through the scan (gradients of gradients, the outer loop of
+ * the E2E paper review, section 2.2): given dZ [B,H,T,d] (io dtype) and optionally
+ * dW_T ([B,H,...] fp32, nullable = zero), writes dQ, dK, dV [B,H,T,d] (io dtype),
+ * deta [B,H,T] fp32 and dW0 (fp32, shaped like W0; summed over B unless
+ * TTT_W0_PER_SEQ). dgamma, dbeta ([H,d] fp32, summed over B) are nullable.
+ * `saved` must come from ttt_scan_fwd on the same inputs and config. */
+ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const float* ln_gamma, const float* ln_beta,
+                        const void* saved, const void* dZ, const ttt_weights* dW_T, void* dQ,
+                        void* dK, void* dV, float* deta, const ttt_weights* dW0, float* dgamma,
+                        float* dbeta, void* workspace, size_t ws_bytes, void* stream);
+
+/* One decode token per (batch, head) (the E2E paper review, section 2.3.2: a
+ * gradient step is committed only when the decoded tokens fill a mini-batch).
+ *  q, k, v [B,H,d] io dtype; eta [B,H] fp32; ln_gamma, ln_beta [H,d].
+ *  W_start [B,H,...] fp32 in/out: weights at the start of the current chunk.
+ *  acc     [B,H,...] fp32 in/out: eta_scale * sum of eta_s grad l_s(W_start) over the
+ *          chunk's tokens so far (caller zero-fills it at a chunk start).
+ *  pos_in_chunk: 0..chunk-1, tracked by the caller. At pos_in_chunk == chunk-1 the
+ *          step commits: W_start -= acc and acc = 0.
+ *  z [B,H,d] io dtype (written) = f(q; W_start - acc), acc including this token.
+ *  A scan of T tokens followed by decode steps equals a scan of the longer sequence. */
+ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, const void* v,
+                           const float* eta, const float* ln_gamma, const float* ln_beta,
+                           const ttt_weights* W_start, const ttt_weights* acc,
+                           int32_t pos_in_chunk, void* z, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* Synchronises `stream`, then reads the workspace status word: TTT_OK, or
+ * TTT_ERR_NONFINITE if any kernel since the last reset saw a NaN/Inf. */
+ttt_status ttt_read_status(const void* workspace, void* stream);
+
+/* Enqueues a zero-fill of the workspace status word on `stream`. */
+ttt_status ttt_reset_status(void* workspace, void* stream);
+
+/* Name of the kernel variant ttt_scan_fwd would launch for cfg ("" if invalid). */
+const char* ttt_fwd_kernel_name(const ttt_config* cfg);
+
+const char* ttt_status_str(ttt_status s);
+int32_t ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H_ */

@@ -1,0 +1,304 @@
+// C-ABI host layer of libttt.so: argument validation (host only), workspace sizing
+// and kernel dispatch. Nothing here allocates device memory; every check runs before
+// anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ttt_internal.h"
+
+using namespace ttt;
+
+namespace {
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ttt_status check_common(const ttt_config* c, bool need_T) {
+  if (!c) return TTT_ERR_NULL;
+  if (c->kind != TTT_LINEAR && c->kind != TTT_MLP) return TTT_ERR_UNSUPPORTED;
+  if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
+  if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH) return TTT_ERR_UNSUPPORTED;
+  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC)) return TTT_ERR_ARG;
+  if (c->B < 1 || c->H < 1 || c->d < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
+  if (need_T && c->T < 1) return TTT_ERR_SHAPE;
+  if (c->d < 16 || c->d > 128 || c->d % 16 != 0) return TTT_ERR_UNSUPPORTED;
+  if (c->kind == TTT_MLP && c->hidden != 4 * c->d) return TTT_ERR_UNSUPPORTED;
+  if (c->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;
+  if (need_T && c->T % c->chunk != 0) return TTT_ERR_SHAPE;
+  if (!std::isfinite(c->ln_eps) || c->ln_eps < 0.f) return TTT_ERR_ARG;
+  if (!std::isfinite(c->eta_scale)) return TTT_ERR_ARG;
+  // sizes must fit the 32-bit grid and 64-bit offsets comfortably
+  const double elems = static_cast<double>(c->B) * c->H * (need_T ? c->T : 1) * c->d;
+  if (static_cast<double>(c->B) * c->H > 2147483647.0 || elems > 9.0e15) return TTT_ERR_SHAPE;
+  const int hid = c->kind == TTT_MLP ? c->hidden : c->d;
+  if (fwd_generic_lds_bytes(c->kind, c->d, hid, c->chunk) > kMaxLds) return TTT_ERR_UNSUPPORTED;
+  return TTT_OK;
+}
+
+int hidden_of(const ttt_config* c) { return c->kind == TTT_MLP ? c->hidden : c->d; }
+
+size_t weights_per_head(const ttt_config* c) { return n_weights(c->kind, c->d, hidden_of(c)); }
+
+ScanParams scan_params(const ttt_config* c) {
+  ScanParams p{};
+  p.kind = c->kind;
+  p.B = c->B;
+  p.H = c->H;
+  p.T = c->T;
+  p.d = c->d;
+  p.hid = hidden_of(c);
+  p.chunk = c->chunk;
+  p.io = c->io_dtype;
+  p.gelu = c->gelu;
+  p.flags = c->flags;
+  p.eps = c->ln_eps;
+  p.eta_scale = c->eta_scale;
+  return p;
+}
+
+bool use_mfma(const ttt_config* c) {
+  if (c->flags & TTT_FORCE_GENERIC) return false;
+  ScanParams p = scan_params(c);
+  return fwd_mfma_supported(p);
+}
+
+size_t fwd_ws_bytes(const ttt_config* c) {
+  if (use_mfma(c)) return kStatusBytes;
+  return kStatusBytes + static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
+}
+
+size_t bwd_ws_bytes(const ttt_config* c) {
+  const size_t heads = static_cast<size_t>(c->B) * c->H;
+  return kStatusBytes +
+         heads * bwd_work_floats_per_head(c->kind, c->d, hidden_of(c), c->chunk) * sizeof(float) +
+         heads * 2 * c->d * sizeof(float);
+}
+
+ttt_status map_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+const char* ttt_status_str(ttt_status s) {
+  switch (s) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL: return "null pointer";
+    case TTT_ERR_SHAPE: return "bad shape";
+    case TTT_ERR_DTYPE: return "bad dtype";
+    case TTT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TTT_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+    case TTT_ERR_HIP: return "HIP runtime error";
+    case TTT_ERR_NONFINITE: return "non-finite value seen by a kernel";
+    case TTT_ERR_ARG: return "bad argument";
+  }
+  return "unknown status";
+}
+
+ttt_status ttt_validate(const ttt_config* cfg) { return check_common(cfg, true); }
+
+ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) {
+  if (!bytes) return TTT_ERR_NULL;
+  const bool need_T = op != TTT_OP_DECODE;
+  ttt_status st = check_common(cfg, need_T);
+  if (st != TTT_OK) return st;
+  switch (op) {
+    case TTT_OP_FWD: *bytes = fwd_ws_bytes(cfg); return TTT_OK;
+    case TTT_OP_BWD: *bytes = bwd_ws_bytes(cfg); return TTT_OK;
+    case TTT_OP_DECODE: *bytes = kStatusBytes; return TTT_OK;
+    default: return TTT_ERR_ARG;
+  }
+}
+
+ttt_status ttt_saved_size(const ttt_config* cfg, size_t* bytes) {
+  if (!bytes) return TTT_ERR_NULL;
+  ttt_status st = check_common(cfg, true);
+  if (st != TTT_OK) return st;
+  *bytes = static_cast<size_t>(cfg->B) * cfg->H * (cfg->T / cfg->chunk) * weights_per_head(cfg) *
+           sizeof(float);
+  return TTT_OK;
+}
+
+const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
+  if (check_common(cfg, true) != TTT_OK) return "";
+  return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
+}
+
+ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const float* ln_gamma, const float* ln_beta,
+                        const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                        void* saved, void* workspace, size_t ws_bytes, void* stream) {
+  ttt_status st = check_common(cfg, true);
+  if (st != TTT_OK) return st;
+  const bool mlp = cfg->kind == TTT_MLP;
+  if (!Q || !K || !V || !eta || !ln_gamma || !ln_beta || !W0 || !W0->w1 || !Z) return TTT_ERR_NULL;
+  if (mlp && !W0->w2) return TTT_ERR_NULL;
+  if (W_T && (!W_T->w1 || (mlp && !W_T->w2))) return TTT_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, eta, ln_gamma, ln_beta, W0->w1, Z};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+  if (mlp && !aligned16(W0->w2)) return TTT_ERR_ALIGN;
+  if (W_T && (!aligned16(W_T->w1) || (mlp && !aligned16(W_T->w2)))) return TTT_ERR_ALIGN;
+  if ((loss && !aligned16(loss)) || (saved && !aligned16(saved))) return TTT_ERR_ALIGN;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < fwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
+
+  ScanParams p = scan_params(cfg);
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.eta = eta;
+  p.gamma = ln_gamma;
+  p.beta = ln_beta;
+  p.w0_1 = W0->w1;
+  p.w0_2 = mlp ? W0->w2 : nullptr;
+  p.Z = Z;
+  p.wt_1 = W_T ? W_T->w1 : nullptr;
+  p.wt_2 = (W_T && mlp) ? W_T->w2 : nullptr;
+  p.loss = loss;
+  p.saved = static_cast<float*>(saved);
+  p.status = static_cast<unsigned*>(workspace);
+  p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
+}
+
+ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const float* ln_gamma, const float* ln_beta,
+                        const void* saved, const void* dZ, const ttt_weights* dW_T, void* dQ,
+                        void* dK, void* dV, float* deta, const ttt_weights* dW0, float* dgamma,
+                        float* dbeta, void* workspace, size_t ws_bytes, void* stream) {
+  ttt_status st = check_common(cfg, true);
+  if (st != TTT_OK) return st;
+  const bool mlp = cfg->kind == TTT_MLP;
+  if (!Q || !K || !V || !eta || !ln_gamma || !ln_beta || !saved || !dZ || !dQ || !dK || !dV ||
+      !deta || !dW0 || !dW0->w1)
+    return TTT_ERR_NULL;
+  if (mlp && !dW0->w2) return TTT_ERR_NULL;
+  if (dW_T && (!dW_T->w1 || (mlp && !dW_T->w2))) return TTT_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, eta, ln_gamma, ln_beta, saved, dZ, dQ, dK, dV, deta, dW0->w1};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+  if (mlp && !aligned16(dW0->w2)) return TTT_ERR_ALIGN;
+  if (dW_T && (!aligned16(dW_T->w1) || (mlp && !aligned16(dW_T->w2)))) return TTT_ERR_ALIGN;
+  if ((dgamma && !aligned16(dgamma)) || (dbeta && !aligned16(dbeta))) return TTT_ERR_ALIGN;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < bwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
+  if (bwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk) > kMaxLds)
+    return TTT_ERR_UNSUPPORTED;
+
+  BwdParams p{};
+  p.kind = cfg->kind;
+  p.B = cfg->B;
+  p.H = cfg->H;
+  p.T = cfg->T;
+  p.d = cfg->d;
+  p.hid = hidden_of(cfg);
+  p.chunk = cfg->chunk;
+  p.io = cfg->io_dtype;
+  p.gelu = cfg->gelu;
+  p.flags = cfg->flags;
+  p.eps = cfg->ln_eps;
+  p.eta_scale = cfg->eta_scale;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.eta = eta;
+  p.gamma = ln_gamma;
+  p.beta = ln_beta;
+  p.saved = static_cast<const float*>(saved);
+  p.dZ = dZ;
+  p.dwt_1 = dW_T ? dW_T->w1 : nullptr;
+  p.dwt_2 = (dW_T && mlp) ? dW_T->w2 : nullptr;
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.deta = deta;
+  p.dw0_1 = dW0->w1;
+  p.dw0_2 = mlp ? dW0->w2 : nullptr;
+  p.dgamma = dgamma;
+  p.dbeta = dbeta;
+  p.status = static_cast<unsigned*>(workspace);
+  const size_t heads = static_cast<size_t>(cfg->B) * cfg->H;
+  p.work = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
+  p.dgb = p.work + heads * bwd_work_floats_per_head(cfg->kind, cfg->d, p.hid, cfg->chunk);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_bwd_generic(p, s);
+  if (e != hipSuccess) return TTT_ERR_HIP;
+  return map_hip(launch_bwd_finalize(p, s));
+}
+
+ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, const void* v,
+                           const float* eta, const float* ln_gamma, const float* ln_beta,
+                           const ttt_weights* W_start, const ttt_weights* acc,
+                           int32_t pos_in_chunk, void* z, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  ttt_status st = check_common(cfg, false);
+  if (st != TTT_OK) return st;
+  const bool mlp = cfg->kind == TTT_MLP;
+  if (!q || !k || !v || !eta || !ln_gamma || !ln_beta || !W_start || !acc || !z ||
+      !W_start->w1 || !acc->w1)
+    return TTT_ERR_NULL;
+  if (mlp && (!W_start->w2 || !acc->w2)) return TTT_ERR_NULL;
+  if (pos_in_chunk < 0 || pos_in_chunk >= cfg->chunk) return TTT_ERR_ARG;
+  const void* ptrs[] = {q, k, v, eta, ln_gamma, ln_beta, W_start->w1, acc->w1, z};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+  if (mlp && (!aligned16(W_start->w2) || !aligned16(acc->w2))) return TTT_ERR_ALIGN;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < kStatusBytes) return TTT_ERR_WORKSPACE;
+  DecodeParams p{};
+  p.kind = cfg->kind;
+  p.B = cfg->B;
+  p.H = cfg->H;
+  p.d = cfg->d;
+  p.hid = hidden_of(cfg);
+  p.chunk = cfg->chunk;
+  p.io = cfg->io_dtype;
+  p.gelu = cfg->gelu;
+  p.flags = cfg->flags;
+  p.pos = pos_in_chunk;
+  p.eps = cfg->ln_eps;
+  p.eta_scale = cfg->eta_scale;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.eta = eta;
+  p.gamma = ln_gamma;
+  p.beta = ln_beta;
+  p.ws_1 = W_start->w1;
+  p.ws_2 = mlp ? W_start->w2 : nullptr;
+  p.acc_1 = acc->w1;
+  p.acc_2 = mlp ? acc->w2 : nullptr;
+  p.z = z;
+  p.status = static_cast<unsigned*>(workspace);
+  return map_hip(launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+ttt_status ttt_read_status(const void* workspace, void* stream) {
+  if (!workspace) return TTT_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return TTT_ERR_HIP;
+  unsigned word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return TTT_ERR_HIP;
+  return (word & kStatusNonFinite) ? TTT_ERR_NONFINITE : TTT_OK;
+}
+
+ttt_status ttt_reset_status(void* workspace, void* stream) {
+  if (!workspace) return TTT_ERR_NULL;
+  return map_hip(launch_reset_status(static_cast<unsigned*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

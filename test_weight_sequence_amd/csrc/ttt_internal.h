@@ -1,0 +1,98 @@
+// Internal interface between the C-ABI host layer (ttt_abi.cpp) and the kernel
+// translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ttt.h"
+
+namespace ttt {
+
+constexpr unsigned kStatusNonFinite = 1u;
+constexpr size_t kStatusBytes = 256;  // status word region at the start of a workspace
+constexpr int kMaxChunk = 16;
+constexpr int kThreads = 256;         // threads per workgroup of the portable kernels
+
+// Everything a kernel needs about one call; plain values and device pointers.
+struct ScanParams {
+  int kind, B, H, T, d, hid, chunk, io, gelu, flags;
+  float eps, eta_scale;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* gamma;
+  const float* beta;
+  const float* w0_1;
+  const float* w0_2;
+  void* Z;
+  float* wt_1;
+  float* wt_2;
+  float* loss;
+  float* saved;    // [B*H, T/chunk, nW] chunk-start weights, or null
+  float* wbuf;     // [B*H, nW] fp32 working weights (portable kernel)
+  unsigned* status;
+};
+
+struct BwdParams {
+  int kind, B, H, T, d, hid, chunk, io, gelu, flags;
+  float eps, eta_scale;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* gamma;
+  const float* beta;
+  const float* saved;
+  const void* dZ;
+  const float* dwt_1;   // nullable
+  const float* dwt_2;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* deta;
+  float* dw0_1;
+  float* dw0_2;
+  float* dgamma;        // nullable
+  float* dbeta;         // nullable
+  float* work;          // per-head scratch: dW accumulators and chunk intermediates
+  float* dgb;           // [B*H, 2, d] per-head dgamma/dbeta partials
+  unsigned* status;
+};
+
+struct DecodeParams {
+  int kind, B, H, d, hid, chunk, io, gelu, flags, pos;
+  float eps, eta_scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* gamma;
+  const float* beta;
+  float* ws_1;
+  float* ws_2;
+  float* acc_1;
+  float* acc_2;
+  void* z;
+  unsigned* status;
+};
+
+inline size_t n_weights(int kind, int d, int hid) {
+  return kind == TTT_MLP ? static_cast<size_t>(2) * d * hid : static_cast<size_t>(d) * d;
+}
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t s);
+size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
+bool fwd_mfma_supported(const ScanParams& p);
+hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t s);
+hipError_t launch_bwd_generic(const BwdParams& p, hipStream_t s);
+size_t bwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
+size_t bwd_work_floats_per_head(int kind, int d, int hid, int chunk);
+hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_reset_status(unsigned* status, hipStream_t s);
+
+}  // namespace ttt

@@ -1,0 +1,166 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function that
+include/ttt.h declares, and its host-side validation rejects bad arguments before
+anything is enqueued (no HIP call is made on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_weight_sequence_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "ttt.h")) as fh:
+        src = fh.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = ops.lib()
+    names = _declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(ops.EXPORTS) <= set(names)
+
+
+def test_abi_version_and_status_strings():
+    L = ops.lib()
+    assert L.ttt_abi_version() == 1
+    for code in range(10):
+        assert L.ttt_status_str(code).decode() != "unknown status"
+    assert L.ttt_status_str(99).decode() == "unknown status"
+
+
+def cfg3(**kw):
+    base = dict(kind="mlp", B=8, H=12, T=8192, d=64, hidden=256, chunk=16, io="bf16")
+    base.update(kw)
+    return ops.Config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(kind="linear", io="f32"), 0),
+    (dict(d=16, hidden=64, io="f32"), 0),
+    (dict(d=128, hidden=512), 0),
+    (dict(T=8200), 2),               # T not a multiple of the chunk
+    (dict(B=0), 2),
+    (dict(T=0), 2),
+    (dict(hidden=128), 4),           # MLP hidden must be 4d
+    (dict(d=8, hidden=32), 4),
+    (dict(d=144, hidden=576), 4),
+    (dict(d=40, hidden=160), 4),     # not a multiple of 16
+    (dict(chunk=32), 4),
+    (dict(chunk=0), 2),
+    (dict(ln_eps=-1.0), 9),
+    (dict(ln_eps=float("nan")), 9),
+    (dict(eta_scale=float("inf")), 9),
+])
+def test_validate(kw, code):
+    assert ops.validate(cfg3(**kw)) == code
+
+
+def test_validate_bad_enums_and_flags():
+    L = ops.lib()
+    c = cfg3().c()
+    c.io_dtype = 7
+    assert L.ttt_validate(ctypes.byref(c)) == 3
+    c = cfg3().c()
+    c.kind = 5
+    assert L.ttt_validate(ctypes.byref(c)) == 4
+    c = cfg3().c()
+    c.gelu = 3
+    assert L.ttt_validate(ctypes.byref(c)) == 4
+    c = cfg3().c()
+    c.flags = 1 << 7
+    assert L.ttt_validate(ctypes.byref(c)) == 9
+    assert L.ttt_validate(None) == 1
+
+
+def test_workspace_and_saved_sizes():
+    c = cfg3()
+    assert ops.workspace_size(c, ops.TTT_OP_DECODE) == 256
+    gen = ops.workspace_size(ops.Config(**{**c.__dict__, "force_generic": True}))
+    assert gen == 256 + 8 * 12 * 2 * 64 * 256 * 4
+    assert ops.workspace_size(c, ops.TTT_OP_BWD) > 256
+    assert ops.saved_size(c) == 8 * 12 * 512 * 2 * 64 * 256 * 4
+    lin = ops.Config(kind="linear", B=4, H=12, T=2048, d=64, io="f32", force_generic=True)
+    assert ops.workspace_size(lin) == 256 + 48 * 64 * 64 * 4
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(c, 17)
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(cfg3(T=3))
+
+
+def test_kernel_selection_names():
+    assert ops.fwd_kernel_name(cfg3(force_generic=True)) == "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(cfg3(io="f32")) == "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(cfg3(T=7)) == ""
+
+
+class _FakeTensor:
+    """Stands in for a device tensor: only data_ptr() is read, and every call below is
+    rejected by host validation before any pointer could be dereferenced."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return 1 << 40
+
+
+def _fwd_call(cfg, ptrs, ws_bytes=1 << 40, W0=(0x10000, 0x20000)):
+    L = ops.lib()
+    P = ctypes.c_void_p
+    w = ctypes.byref(ops.CWeights(*W0))
+    return L.ttt_scan_fwd(ctypes.byref(cfg.c()), *[P(x) for x in ptrs], w, P(0x80000), None,
+                          None, None, P(0x90000), ws_bytes, None)
+
+
+def test_fwd_rejects_null_misaligned_and_small_workspace():
+    c = cfg3()
+    good = [0x1000 * (i + 1) for i in range(6)]
+    assert _fwd_call(c, [0] + good[1:]) == 1
+    assert _fwd_call(c, good, W0=(0x10000, 0)) == 1
+    assert _fwd_call(c, [0x1008] + good[1:]) == 5
+    assert _fwd_call(c, good, ws_bytes=16) == 6
+    assert _fwd_call(cfg3(T=17), good) == 2
+
+
+def test_decode_rejects_bad_position():
+    L = ops.lib()
+    P = ctypes.c_void_p
+    c = cfg3()
+    w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
+    args = [P(0x1000 * (i + 1)) for i in range(6)]
+    for pos in (-1, 16):
+        assert L.ttt_decode_step(ctypes.byref(c.c()), *args, w, w, pos, P(0x70000), P(0x90000),
+                                 256, None) == 9
+    assert L.ttt_decode_step(ctypes.byref(c.c()), *args, w, w, 3, P(0x70000), None, 256,
+                             None) == 6
+
+
+def test_bwd_rejects_missing_saved_buffer():
+    L = ops.lib()
+    P = ctypes.c_void_p
+    c = cfg3()
+    w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
+    args = [P(0x1000 * (i + 1)) for i in range(6)]
+    code = L.ttt_scan_bwd(ctypes.byref(c.c()), *args, None, P(0x40000), None, P(0x50000),
+                          P(0x60000), P(0x70000), P(0x71000), w, None, None, P(0x90000),
+                          1 << 40, None)
+    assert code == 1
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "_LIB_PATH", "/nonexistent/libttt.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP scan (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs. Tolerances (relative L2 over the whole tensor): 1e-4 for fp32
+I/O, 2e-2 for bf16 I/O (fp32 state in both)."""
+import math
+
+import pytest
+import torch
+
+from helpers import TOL, note, oracle_heads, ops_config, rel_l2, to_dev
+from oracle import OracleConfig, f_apply
+from test_weight_sequence_amd import ops
+from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, d, **kw):
+    return ops.scan_fwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["W0"], d["gamma"], d["beta"],
+                        **kw)
+
+
+def _check_heads(res, inp, pairs, w, tol, cfg_kw=None, B_axis=True):
+    Z, WT, L = oracle_heads(inp, pairs, w.kind, w.chunk, **(cfg_kw or {}))
+    gz = torch.stack([res["Z"][b, h] for b, h in pairs]).cpu()
+    assert rel_l2(gz, Z) <= tol, rel_l2(gz, Z)
+    for k, wt in enumerate(WT):
+        g = torch.stack([res["W_T"][k][b, h] for b, h in pairs]).cpu()
+        assert rel_l2(g, wt) <= tol, (k, rel_l2(g, wt))
+    if res.get("loss") is not None:
+        gl = torch.stack([res["loss"][b, h] for b, h in pairs]).cpu()
+        assert rel_l2(gl, L) <= tol, rel_l2(gl, L)
+    return rel_l2(gz, Z)
+
+
+def _kernels_for(w):
+    names = ["generic"]
+    cfg = ops_config(w)
+    if ops.fwd_kernel_name(cfg) != "ttt_fwd_generic":
+        names.append("tuned")
+    return names
+
+
+def test_cfg1_mlp_fp32_full():
+    w = WORKLOADS[1]
+    note(f"cfg1 full {w}")
+    inp = make_inputs(w)
+    res = _run(ops_config(w), to_dev(inp), want_loss=True)
+    _check_heads(res, inp, [(0, 0)], w, TOL["f32"])
+
+
+def test_cfg2_linear_fp32_full():
+    w = WORKLOADS[2]
+    note(f"cfg2 full {w}")
+    inp = make_inputs(w)
+    res = _run(ops_config(w), to_dev(inp), want_loss=True)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _check_heads(res, inp, pairs, w, TOL["f32"])
+
+
+@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+def test_cfg3_full_size_sampled_heads(kernel):
+    """Full config-3 launch (B=8, H=12, T=8192); the oracle checks three heads at full T."""
+    w = WORKLOADS[3]
+    cfg = ops_config(w, force_generic=(kernel == "generic"))
+    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
+        pytest.skip("no tuned kernel for this configuration")
+    note(f"cfg3 full {kernel} -> {ops.fwd_kernel_name(cfg)}")
+    inp = make_inputs(w)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    _check_heads(res, inp, [(0, 0), (3, 7), (7, 11)], w, TOL["bf16"])
+
+
+@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+def test_cfg3_all_heads_short(kernel):
+    w = WORKLOADS[3]
+    cfg = ops_config(w, T=256, force_generic=(kernel == "generic"))
+    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
+        pytest.skip("no tuned kernel for this configuration")
+    note(f"cfg3 T=256 all heads {kernel}")
+    inp = make_inputs(w, T=256)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _check_heads(res, inp, pairs, w, TOL["bf16"])
+
+
+def test_cfg4_d128_reduced_T():
+    """Config-4 head shape (d=128, hidden=512, AR(1) drifting inputs) on two heads, T=512."""
+    w = WORKLOADS[4]
+    note("cfg4 d=128 T=512 heads 0,23")
+    inp = make_inputs(w, head_idx=[0, 23], T=512)
+    cfg = ops_config(w, T=512, H=2)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    _check_heads(res, inp, [(0, 0), (0, 1)], w, TOL["bf16"])
+
+
+@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+def test_cfg5_fwd_full_size_sampled_heads(kernel):
+    w = WORKLOADS[5]
+    cfg = ops_config(w, force_generic=(kernel == "generic"))
+    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
+        pytest.skip("no tuned kernel for this configuration")
+    note(f"cfg5 fwd full {kernel}")
+    inp = make_inputs(w)
+    res = _run(cfg, to_dev(inp))
+    _check_heads(res, inp, [(1, 2), (3, 15)], w, TOL["bf16"])
+
+
+def _rand_case(kind, B, H, T, d, chunk, io, seed, per_seq=False):
+    g = torch.Generator().manual_seed(seed)
+    hid = 4 * d if kind == "mlp" else d
+    sc = math.sqrt(1.0 / d)
+    mk = lambda *s: torch.randn(*s, generator=g) * sc
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    inp = {"Q": mk(B, H, T, d).to(dt), "K": mk(B, H, T, d).to(dt), "V": mk(B, H, T, d).to(dt),
+           "eta": 0.2 * torch.sigmoid(torch.randn(B, H, T, generator=g))}
+    lead = (B, H) if per_seq else (H,)
+    if kind == "mlp":
+        inp["W0"] = (0.2 * torch.randn(*lead, d, hid, generator=g),
+                     0.2 * torch.randn(*lead, hid, d, generator=g))
+    else:
+        inp["W0"] = (torch.eye(d) + 0.1 * torch.randn(*lead, d, d, generator=g),)
+    inp["gamma"] = 1.0 + 0.2 * torch.randn(H, d, generator=g)
+    inp["beta"] = 0.1 * torch.randn(H, d, generator=g)
+    return inp
+
+
+def _oracle_all(inp, kind, chunk, per_seq=False, **kw):
+    B, H = inp["Q"].shape[:2]
+    if per_seq:
+        flat = flatten_heads({**inp, "W0": tuple(w[0] for w in inp["W0"])})
+        flat["W0"] = tuple(w.to(torch.float64).reshape(B * H, *w.shape[2:]) for w in inp["W0"])
+    else:
+        flat = flatten_heads(inp)
+    cfg = OracleConfig(kind=kind, chunk=chunk, **kw)
+    return flat, cfg
+
+
+@pytest.mark.parametrize("kind,d,chunk,T,gelu,eta_scale,per_seq", [
+    ("mlp", 16, 1, 24, "erf", 1.0, False),
+    ("mlp", 48, 4, 44, "tanh", 0.25, True),
+    ("mlp", 64, 16, 48, "erf", 1.0 / 16, False),
+    ("mlp", 128, 8, 40, "erf", 1.0, True),
+    ("linear", 32, 3, 33, "erf", 1.0, False),
+    ("linear", 128, 16, 32, "erf", 0.5, True),
+])
+def test_edge_shapes_fp32(kind, d, chunk, T, gelu, eta_scale, per_seq):
+    B, H = 2, 3
+    inp = _rand_case(kind, B, H, T, d, chunk, "f32", seed=d * 7 + chunk, per_seq=per_seq)
+    cfg = ops.Config(kind=kind, B=B, H=H, T=T, d=d, hidden=4 * d, chunk=chunk, io="f32",
+                     gelu=gelu, eta_scale=eta_scale, w0_per_seq=per_seq)
+    note(f"edge {cfg}")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    flat, ocfg = _oracle_all(inp, kind, chunk, per_seq, gelu=gelu, eta_scale=eta_scale)
+    from oracle import scan
+    Z, WT, L = scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"], flat["gamma"],
+                    flat["beta"], ocfg)
+    assert rel_l2(res["Z"].reshape(B * H, T, d), Z) <= TOL["f32"]
+    assert rel_l2(res["loss"].reshape(B * H, T), L) <= TOL["f32"]
+    for g, o in zip(res["W_T"], WT):
+        assert rel_l2(g.reshape(o.shape), o) <= TOL["f32"]
+
+
+def test_eta_zero_gives_initial_map():
+    w = WORKLOADS[3]
+    inp = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 1, 2], T=64)
+    inp["eta"] = torch.zeros_like(inp["eta"])
+    cfg = ops_config(w, T=64, B=2, H=3)
+    note("eta=0")
+    res = _run(cfg, to_dev(inp))
+    flat = flatten_heads(inp)
+    ref = torch.stack([f_apply(flat["Q"][n], tuple(x[n:n + 1].expand(64, *x.shape[1:])
+                                                   for x in flat["W0"]),
+                               flat["gamma"][n], flat["beta"][n], OracleConfig())
+                       for n in range(6)])
+    assert rel_l2(res["Z"].reshape(6, 64, 64), ref) <= TOL["bf16"]
+    for g, w0 in zip(res["W_T"], inp["W0"]):
+        assert torch.equal(g.cpu(), w0.unsqueeze(0).expand(2, *w0.shape))
+
+
+def test_split_scan_equals_unsplit():
+    w = WORKLOADS[1]
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    cfg = ops_config(w)
+    note("split scan")
+    full = _run(cfg, d)
+    half = w.T // 2
+    cut = lambda x, a, b: x[:, :, a:b].contiguous()
+    c2 = ops_config(w, T=half)
+    r1 = _run(c2, {**d, "Q": cut(d["Q"], 0, half), "K": cut(d["K"], 0, half),
+                   "V": cut(d["V"], 0, half), "eta": cut(d["eta"], 0, half)})
+    c3 = ops.Config(**{**c2.__dict__, "w0_per_seq": True})
+    r2 = _run(c3, {**d, "Q": cut(d["Q"], half, w.T), "K": cut(d["K"], half, w.T),
+                   "V": cut(d["V"], half, w.T), "eta": cut(d["eta"], half, w.T),
+                   "W0": r1["W_T"]})
+    joined = torch.cat([r1["Z"], r2["Z"]], dim=2)
+    assert torch.equal(joined, full["Z"])
+    for a, b in zip(r2["W_T"], full["W_T"]):
+        assert torch.equal(a, b)
+
+
+def _tok(x, t):
+    """Token t of a [B, H, T, ...] tensor in a fresh (16-byte aligned) allocation."""
+    return x[:, :, t].clone()
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_decode_loop_equals_scan(wid):
+    w = WORKLOADS[wid]
+    T = 64
+    inp = make_inputs(w, batch_idx=[0], head_idx=[0, 1] if w.H > 1 else [0], T=T)
+    B, H = inp["Q"].shape[:2]
+    cfg = ops_config(w, T=T, B=B, H=H)
+    d = to_dev(inp)
+    note(f"decode loop cfg{wid}")
+    scan_res = _run(cfg, d)
+    Ws = tuple(x.unsqueeze(0).expand(B, *x.shape).contiguous().clone() for x in d["W0"])
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    zs = []
+    for t in range(T):
+        zs.append(ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
+                                  _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc,
+                                  t % w.chunk))
+    Zd = torch.stack(zs, dim=2)
+    assert rel_l2(Zd, scan_res["Z"]) <= TOL[w.io]
+    for a, b in zip(Ws, scan_res["W_T"]):
+        assert rel_l2(a, b) <= TOL[w.io]
+    for a in acc:
+        assert torch.count_nonzero(a).item() == 0
+
+
+def test_scan_then_decode_continues_the_sequence():
+    """Prefill T0 tokens with the scan, decode the rest: equals the oracle on all T."""
+    w = WORKLOADS[1]
+    T0, T = 64, 96
+    inp = make_inputs(w, T=T)
+    d = to_dev(inp)
+    note("scan then decode")
+    pre = _run(ops_config(w, T=T0), {**d, **{k: d[k][:, :, :T0].contiguous()
+                                             for k in ("Q", "K", "V", "eta")}})
+    cfg = ops_config(w, T=T)
+    Ws = tuple(x.clone() for x in pre["W_T"])
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
+                          _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, (t - T0) % w.chunk)
+          for t in range(T0, T)]
+    Z = torch.cat([pre["Z"], torch.stack(zs, dim=2)], dim=2)
+    Zo, WTo, _ = oracle_heads(inp, [(0, 0)], w.kind, w.chunk)
+    assert rel_l2(Z[0], Zo) <= TOL["f32"]
+    for a, b in zip(Ws, WTo):
+        assert rel_l2(a[0], b) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("wid", [1, 3])
+def test_runs_are_bitwise_deterministic(wid):
+    w = WORKLOADS[wid]
+    T = min(w.T, 512)
+    inp = to_dev(make_inputs(w, T=T))
+    cfg = ops_config(w, T=T)
+    note(f"determinism cfg{wid}")
+    a = _run(cfg, inp, want_loss=True)
+    b = _run(cfg, inp, want_loss=True)
+    assert torch.equal(a["Z"], b["Z"]) and torch.equal(a["loss"], b["loss"])
+    for x, y in zip(a["W_T"], b["W_T"]):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("force_generic", [True, False])
+def test_nonfinite_input_sets_status(force_generic):
+    w = WORKLOADS[3]
+    inp = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
+    inp["K"][0, 1, 37, 5] = float("nan")
+    cfg = ops_config(w, T=64, B=1, H=2, force_generic=force_generic)
+    note(f"nan injection generic={force_generic}")
+    res = _run(cfg, to_dev(inp))
+    ws = res["workspace"]
+    assert ops.read_status(ws) == 8
+    ops.reset_status(ws)
+    assert ops.read_status(ws) == 0
+    clean = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
+    _run(cfg, to_dev(clean), workspace=ws)
+    assert ops.read_status(ws) == 0
