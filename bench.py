@@ -80,8 +80,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--cpu-T", type=int, default=1024)
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-T", type=int, default=4096)
     ap.add_argument("--force-generic", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
