@@ -23,6 +23,7 @@ ARCH = "gfx950"
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
 

@@ -7,6 +7,11 @@
 
 #include "ttt_internal.h"
 
+#define TTT_HD __device__ __forceinline__
+#define TTT_EXP2(x) __builtin_amdgcn_exp2f(x)
+#define TTT_RCP(x) __builtin_amdgcn_rcpf(x)
+#include "ttt_gelu.hpp"
+
 namespace ttt {
 
 // ---------------------------------------------------------------------------

@@ -91,13 +91,18 @@ __device__ __forceinline__ float sum16(float v) {
 }
 __device__ __forceinline__ float bf(__bf16 x) { return static_cast<float>(x); }
 
+// erf-form GELU through the branch-free A&S 7.1.26 evaluation (ttt_gelu.hpp); the tanh
+// form through the library tanh.
 template <int GELU_KIND>
 __device__ __forceinline__ void act_d(float x, float& v, float& d1) {
-  gelu_d(x, GELU_KIND, v, d1);
+  if (GELU_KIND == TTT_GELU_ERF)
+    ttt_gelu::gelu_d(x, v, d1);
+  else
+    gelu_d(x, GELU_KIND, v, d1);
 }
 template <int GELU_KIND>
 __device__ __forceinline__ float act(float x) {
-  return gelu(x, GELU_KIND);
+  return GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(x) : gelu(x, GELU_KIND);
 }
 
 template <int GELU_KIND>
