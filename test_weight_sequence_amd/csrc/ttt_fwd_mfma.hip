@@ -187,7 +187,9 @@ fwd_mfma_kernel(ScanParams p) {
     if (has_next) gload(c + 1, nk, nq, nv, ne);
     if (p.saved) {
       // chunk-start weights for the backward pass; buffer stores keep the per-lane
-      // address to one register (the tile offsets are scalar constants)
+      // address to one register (the tile offsets are scalar constants). The element is
+      // copied to a scalar float first: a bit_cast applied directly to a vector element
+      // was compiled as a read of element 0.
       float* sv = p.saved + (static_cast<size_t>(bh) * nchunks + c) * (2 * D * HID);
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc(sv, 0, 2 * D * HID * 4, 0x00020000);
@@ -199,9 +201,9 @@ fwd_mfma_kernel(ScanParams p) {
         for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, W1c[dt][ht][r]),
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(static_cast<float>(W1c[dt][ht][r])),
                                                   rsrc, v1, ((16 * dt + r) * HID + 16 * ht) * 4, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, W2c[ht][dt][r]),
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(static_cast<float>(W2c[ht][dt][r])),
                                                   rsrc, v2, ((16 * ht + r) * D + 16 * dt) * 4, 0);
           }
     }

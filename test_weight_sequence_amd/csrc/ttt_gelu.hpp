@@ -12,7 +12,7 @@
 #pragma once
 
 #ifndef TTT_HD
-#define TTT_HD
+#define TTT_HD inline
 #endif
 #ifndef TTT_EXP2
 #define TTT_EXP2(x) exp2f(x)
@@ -38,7 +38,7 @@ struct PhiPhi {
   float e;    // exp(-x^2 / 2)
 };
 
-TTT_HD inline PhiPhi phi_pair(float x) {
+TTT_HD PhiPhi phi_pair(float x) {
   const float ax = x < 0.f ? -x : x;
   const float t = TTT_RCP(ax * kP + 1.0f);
   const float poly = t * (kA1 + t * (kA2 + t * (kA3 + t * (kA4 + t * kA5))));
@@ -51,17 +51,17 @@ TTT_HD inline PhiPhi phi_pair(float x) {
 }
 
 // GELU(x) = x Phi(x)
-TTT_HD inline float gelu(float x) { return x * phi_pair(x).cdf; }
+TTT_HD float gelu(float x) { return x * phi_pair(x).cdf; }
 
 // value and first derivative: GELU' = Phi + x phi
-TTT_HD inline void gelu_d(float x, float& v, float& d1) {
+TTT_HD void gelu_d(float x, float& v, float& d1) {
   const PhiPhi p = phi_pair(x);
   v = x * p.cdf;
   d1 = p.cdf + x * (p.e * kInvSqrt2Pi);
 }
 
 // value, first and second derivative: GELU'' = phi (2 - x^2)
-TTT_HD inline void gelu_d2(float x, float& v, float& d1, float& d2) {
+TTT_HD void gelu_d2(float x, float& v, float& d1, float& d2) {
   const PhiPhi p = phi_pair(x);
   const float pdf = p.e * kInvSqrt2Pi;
   v = x * p.cdf;

@@ -79,7 +79,7 @@ struct DecodeParams {
   unsigned* status;
 };
 
-inline size_t n_weights(int kind, int d, int hid) {
+__host__ __device__ inline size_t n_weights(int kind, int d, int hid) {
   return kind == TTT_MLP ? static_cast<size_t>(2) * d * hid : static_cast<size_t>(d) * d;
 }
 
@@ -88,9 +88,15 @@ hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t s);
 size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
 bool fwd_mfma_supported(const ScanParams& p);
 hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t s);
+// Per-head backward workspace (floats): the carried dW, then kBwdArrays [chunk x hidden]
+// intermediates (MLP only).
+constexpr int kBwdArrays = 12;
+__host__ __device__ inline size_t bwd_work_floats_per_head(int kind, int d, int hid, int chunk) {
+  const size_t nW = kind == TTT_MLP ? static_cast<size_t>(2) * d * hid : static_cast<size_t>(d) * d;
+  return nW + (kind == TTT_MLP ? static_cast<size_t>(kBwdArrays) * chunk * hid : 0);
+}
 hipError_t launch_bwd_generic(const BwdParams& p, hipStream_t s);
 size_t bwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
-size_t bwd_work_floats_per_head(int kind, int d, int hid, int chunk);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_reset_status(unsigned* status, hipStream_t s);
