@@ -94,6 +94,27 @@ def test_cfg4_d128_reduced_T():
     _check_heads(res, inp, [(0, 0), (0, 1)], w, TOL["bf16"])
 
 
+def test_cfg4_full_length_two_heads_prefix():
+    """Config-4 heads at full length (T=131072, d=128, hidden=512, AR(1) drift): two heads
+    run through the whole scan; outputs of the first 1024 tokens (which depend only on the
+    prefix) are checked against the oracle, and the end state must stay finite."""
+    w = WORKLOADS[4]
+    note("cfg4 full T two heads")
+    inp = make_inputs(w, head_idx=[5, 17])
+    cfg = ops_config(w, H=2)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    for x in res["W_T"]:
+        assert torch.isfinite(x).all()
+    Tp = 1024
+    pre = {k: (v[:, :, :Tp] if k in ("Q", "K", "V", "eta") else v) for k, v in inp.items()}
+    Z, _, L = oracle_heads(pre, [(0, 0), (0, 1)], w.kind, w.chunk)
+    gz = res["Z"][0, :, :Tp].cpu()
+    assert rel_l2(gz, Z) <= TOL["bf16"], rel_l2(gz, Z)
+    assert rel_l2(res["loss"][0, :, :Tp].cpu(), L) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("kernel", ["generic", "tuned"])
 def test_cfg5_fwd_full_size_sampled_heads(kernel):
     w = WORKLOADS[5]
