@@ -1,9 +1,9 @@
 // Tuned forward scan for the TTT-MLP head shape d = 64, hidden = 256, chunk 16, bf16
 // Q/K/V/Z, fp32 fast weights (gfx950, bf16 MFMA with fp32 accumulation).
 //
-// One persistent workgroup of 4 waves per (batch, head); wave w owns hidden units
-// [64w, 64w + 64). The fp32 fast weights never leave registers: each wave keeps its
-// slice of W1 (d x h) and W2 (h x d) as 16x16 MFMA accumulator tiles that the
+// One persistent workgroup of NW waves per (batch, head); wave w owns hidden units
+// [w*HS, (w+1)*HS), HS = 256 / NW. The fp32 fast weights never leave registers: each wave
+// keeps its slice of W1 (d x h) and W2 (h x d) as 16x16 MFMA accumulator tiles that the
 // chunk-end update accumulates into.
 //
 // Register-layout rule used throughout: an MFMA accumulator tile C[m][n] puts m on
@@ -32,14 +32,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 64;
 constexpr int HID = 256;
 constexpr int BC = 16;             // chunk
-constexpr int NWAVE = 4;
-constexpr int HS = HID / NWAVE;    // hidden units per wave
-constexpr int NHT = HS / 16;       // h tiles per wave
 constexpr int NDT = D / 16;        // d tiles
 constexpr int RS = D + 8;          // padded row stride (bf16 elements) of [token][d] arrays
 constexpr int TS = BC + 8;         // padded row stride of [d][token] arrays
@@ -52,11 +50,12 @@ struct Stage {
   float eta[BC];
 };
 
+template <int NW>
 struct Smem {
   Stage st[2];
-  float red[2][NWAVE][NDT][4][64];  // [0]: Z^K partials, [1]: Z^Q partials
-  __bf16 E2[BC * RS];               // En2, [token][d]
-  __bf16 E2t[D * TS];               // En2, [d][token]
+  float red[2][NW][NDT][4][64];  // [0]: Z^K partials, [1]: Z^Q partials
+  __bf16 E2[BC * RS];            // En2, [token][d]
+  __bf16 E2t[D * TS];            // En2, [d][token]
 };
 
 __device__ __forceinline__ f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
@@ -82,11 +81,19 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ bf16x4 lds4(const __bf16* p) {
   return *reinterpret_cast<const bf16x4*>(p);
 }
+// Sum over aligned groups of 16 lanes with DPP moves (no LDS round trip). After the two
+// quad permutations every lane of a quad holds the quad sum, so mirroring within 8 lanes
+// and then within 16 lanes pairs each lane with the other half; every lane of the group
+// ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
   return v;
 }
 __device__ __forceinline__ float bf(__bf16 x) { return static_cast<float>(x); }
@@ -105,10 +112,35 @@ __device__ __forceinline__ float act(float x) {
   return GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(x) : gelu(x, GELU_KIND);
 }
 
-template <int GELU_KIND>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Staged elements per thread and their load type.
+template <int EPT>
+struct StageVec;
+template <>
+struct StageVec<4> {
+  using T = uint2;
+  using B = bf16x4;
+};
+template <>
+struct StageVec<2> {
+  using T = unsigned;
+  using B = bf16x2;
+};
+
+template <int GELU_KIND, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 fwd_mfma_kernel(ScanParams p) {
-  __shared__ Smem sm;
+  constexpr int NT = 64 * NW;
+  constexpr int HS = HID / NW;     // hidden units per wave
+  constexpr int NHT = HS / 16;     // h tiles per wave
+  constexpr int NKH = NHT / 2;     // 32-wide k-steps over this wave's h slice
+  constexpr int EPT = BC * D / NT; // staged elements per thread and tensor
+  // LayerNorm: waves 0..3, 4 tokens per wave, 16 lanes per token, 4 d values per lane
+  constexpr int DPL = D / 16;
+  static_assert(NHT % 2 == 0 && EPT * NT == BC * D, "wave split");
+  using SV = StageVec<EPT>;
+  using LdT = typename SV::T;
+
+  __shared__ Smem<NW> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -117,7 +149,7 @@ fwd_mfma_kernel(ScanParams p) {
   const int T = p.T, nchunks = T / BC;
   const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
 
-  // ---- fast weights: fp32 accumulator tiles + bf16 operand copies ----
+  // ---- fast weights: fp32 accumulator tiles ----
   f4 W1c[NDT][NHT], W2c[NHT][NDT];
   {
     const size_t wh = per_seq ? static_cast<size_t>(bh) : static_cast<size_t>(hidx);
@@ -139,11 +171,15 @@ fwd_mfma_kernel(ScanParams p) {
   bf16x4 I4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) I4[j] = (__bf16)((4 * g + j) == c16 ? 1.0f : 0.0f);
-  float gam[NDT], bet[NDT];
+
+  // LayerNorm lane mapping (waves 0..3): token ln_t = 4w + lane/16, d = 16 i + lane%16
+  const bool ln_wave = w < 4;
+  const int ln_t = 4 * w + g;
+  float gam[DPL], bet[DPL];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    gam[dt] = p.gamma[hidx * D + 16 * dt + c16];
-    bet[dt] = p.beta[hidx * D + 16 * dt + c16];
+  for (int i = 0; i < DPL; ++i) {
+    gam[i] = p.gamma[hidx * D + 16 * i + c16];
+    bet[i] = p.beta[hidx * D + 16 * i + c16];
   }
 
   const __bf16* Qg = static_cast<const __bf16*>(p.Q) + static_cast<size_t>(bh) * T * D;
@@ -152,26 +188,26 @@ fwd_mfma_kernel(ScanParams p) {
   __bf16* Zg = static_cast<__bf16*>(p.Z) + static_cast<size_t>(bh) * T * D;
   const float* etag = p.eta + static_cast<size_t>(bh) * T;
 
-  // staging: thread -> (token st_t, 4 consecutive d from st_d)
-  const int st_t = tid >> 4, st_d = (tid & 15) * 4;
-  auto stage_write = [&](Stage& S, uint2 kk, uint2 qq, uint2 vv, float e) {
-    *reinterpret_cast<uint2*>(&S.K[st_t * RS + st_d]) = kk;
-    *reinterpret_cast<uint2*>(&S.Q[st_t * RS + st_d]) = qq;
-    *reinterpret_cast<uint2*>(&S.V[st_t * RS + st_d]) = vv;
-    const bf16x4 kv = __builtin_bit_cast(bf16x4, kk);
+  // staging: thread -> (token st_t, EPT consecutive d from st_d)
+  const int st_t = tid / (D / EPT), st_d = (tid % (D / EPT)) * EPT;
+  auto stage_write = [&](Stage& S, LdT kk, LdT qq, LdT vv, float e) {
+    *reinterpret_cast<LdT*>(&S.K[st_t * RS + st_d]) = kk;
+    *reinterpret_cast<LdT*>(&S.Q[st_t * RS + st_d]) = qq;
+    *reinterpret_cast<LdT*>(&S.V[st_t * RS + st_d]) = vv;
+    const typename SV::B kv = __builtin_bit_cast(typename SV::B, kk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S.Kt[(st_d + j) * TS + st_t] = kv[j];
+    for (int j = 0; j < EPT; ++j) S.Kt[(st_d + j) * TS + st_t] = kv[j];
     if (tid < BC) S.eta[tid] = e * p.eta_scale;
   };
-  auto gload = [&](int chunk, uint2& kk, uint2& qq, uint2& vv, float& e) {
+  auto gload = [&](int chunk, LdT& kk, LdT& qq, LdT& vv, float& e) {
     const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
-    kk = *reinterpret_cast<const uint2*>(Kg + off);
-    qq = *reinterpret_cast<const uint2*>(Qg + off);
-    vv = *reinterpret_cast<const uint2*>(Vg + off);
+    kk = *reinterpret_cast<const LdT*>(Kg + off);
+    qq = *reinterpret_cast<const LdT*>(Qg + off);
+    vv = *reinterpret_cast<const LdT*>(Vg + off);
     e = tid < BC ? etag[chunk * BC + tid] : 0.f;
   };
   {
-    uint2 kk, qq, vv;
+    LdT kk, qq, vv;
     float e;
     gload(0, kk, qq, vv, e);
     stage_write(sm.st[0], kk, qq, vv, e);
@@ -181,7 +217,7 @@ fwd_mfma_kernel(ScanParams p) {
   for (int c = 0; c < nchunks; ++c) {
     Stage& S = sm.st[c & 1];
     const int t0 = c * BC;
-    uint2 nk = {0, 0}, nq = {0, 0}, nv = {0, 0};
+    LdT nk{}, nq{}, nv{};
     float ne = 0.f;
     const bool has_next = c + 1 < nchunks;
     if (has_next) gload(c + 1, nk, nq, nv, ne);
@@ -215,7 +251,6 @@ fwd_mfma_kernel(ScanParams p) {
       aK[ks] = cat(lds4(&S.K[c16 * RS + 32 * ks + 4 * g]), lds4(&S.K[c16 * RS + 32 * ks + 16 + 4 * g]));
       aQ[ks] = cat(lds4(&S.Q[c16 * RS + 32 * ks + 4 * g]), lds4(&S.Q[c16 * RS + 32 * ks + 16 + 4 * g]));
     }
-
     // bf16 operand copies of the chunk-start weights
     bf16x4 W1b[NDT][NHT], W2b[NHT][NDT];
 #pragma unroll
@@ -227,23 +262,18 @@ fwd_mfma_kernel(ScanParams p) {
       }
 
     // ---- K side: H^K = K W1 (token x h, R layout) ----
-    f4 hk[NHT];
+    bf16x4 akR[NHT], akT[NHT];
+    f4 gk[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma32(aK[ks], cat(W1b[2 * ks][ht], W1b[2 * ks + 1][ht]), acc);
-      hk[ht] = acc;
-    }
-    bf16x4 akR[NHT], akT[NHT];
-    f4 gk[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
       f4 a, gd;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v, d1;
-        act_d<GELU_KIND>(hk[ht][r], v, d1);
+        act_d<GELU_KIND>(acc[r], v, d1);
         a[r] = v;
         gd[r] = d1;
       }
@@ -257,7 +287,7 @@ fwd_mfma_kernel(ScanParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < NKH; ++ks)
         acc = mfma32(cat(akT[2 * ks], akT[2 * ks + 1]), cat(W2b[2 * ks][dt], W2b[2 * ks + 1][dt]), acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.red[0][w][dt][r][lane] = acc[r];
@@ -276,41 +306,45 @@ fwd_mfma_kernel(ScanParams p) {
     for (int ks = 0; ks < 2; ++ks) s1t = mfma32(aK[ks], aQ[ks], s1t);
     __syncthreads();
 
-    // ---- LayerNorm forward/backward of Z^K: tokens 4w .. 4w+3, 16 lanes each ----
-    {
-      const int t = 4 * w + g;
-      float z[NDT];
+    // ---- LayerNorm forward/backward of Z^K: 4 tokens per wave, 16 lanes each ----
+    if (ln_wave) {
+      const int t = ln_t;
+      float z[DPL];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int i = 0; i < DPL; ++i) {
+        const int dt = i;
         float s = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) s += sm.red[0][ww][dt][g][16 * w + c16];
-        z[dt] = s;
+        for (int ww = 0; ww < NW; ++ww) s += sm.red[0][ww][dt][t & 3][16 * (t >> 2) + c16];
+        z[i] = s;
       }
-      const float mu = sum16(z[0] + z[1] + z[2] + z[3]) * (1.0f / D);
+      float zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) zs += z[i];
+      const float mu = sum16(zs) * (1.0f / D);
       float var = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) var += (z[dt] - mu) * (z[dt] - mu);
+      for (int i = 0; i < DPL; ++i) var += (z[i] - mu) * (z[i] - mu);
       var = sum16(var) * (1.0f / D);
       const float rs = 1.0f / sqrtf(var + p.eps);
-      float xh[NDT], gg[NDT], l2 = 0.f, sg = 0.f, sgx = 0.f;
+      float xh[DPL], gg[DPL], l2 = 0.f, sg = 0.f, sgx = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 16 * dt + c16;
-        xh[dt] = (z[dt] - mu) * rs;
-        const float r = bf(S.K[t * RS + d]) + gam[dt] * xh[dt] + bet[dt] - bf(S.V[t * RS + d]);
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        xh[i] = (z[i] - mu) * rs;
+        const float r = bf(S.K[t * RS + d]) + gam[i] * xh[i] + bet[i] - bf(S.V[t * RS + d]);
         l2 += r * r;
-        gg[dt] = 2.f * r * gam[dt];
-        sg += gg[dt];
-        sgx += gg[dt] * xh[dt];
+        gg[i] = 2.f * r * gam[i];
+        sg += gg[i];
+        sgx += gg[i] * xh[i];
       }
       const float loss = sum16(l2);
       const float mg = sum16(sg) * (1.0f / D), mgx = sum16(sgx) * (1.0f / D);
       const float ne2 = -S.eta[t] * rs;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 16 * dt + c16;
-        const __bf16 e = (__bf16)(ne2 * (gg[dt] - mg - xh[dt] * mgx));
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
         sm.E2[t * RS + d] = e;
         sm.E2t[d * TS + t] = e;
       }
@@ -366,7 +400,7 @@ fwd_mfma_kernel(ScanParams p) {
     // ---- Z^Q partial = A^Q W2 + tril(A^Q A^K^T) En2 over this wave's h slice ----
     f4 s2t = {0.f, 0.f, 0.f, 0.f};  // C[s][t] = A^K_s . A^Q_t (this slice)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < NKH; ++ks)
       s2t = mfma32(cat(akT[2 * ks], akT[2 * ks + 1]), cat(aqT[2 * ks], aqT[2 * ks + 1]), s2t);
     f4 s2m;
 #pragma unroll
@@ -376,7 +410,7 @@ fwd_mfma_kernel(ScanParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < NKH; ++ks)
         acc = mfma32(cat(aqT[2 * ks], aqT[2 * ks + 1]), cat(W2b[2 * ks][dt], W2b[2 * ks + 1][dt]), acc);
       acc = mfma16(s2a, bE[dt], acc);
 #pragma unroll
@@ -395,28 +429,32 @@ fwd_mfma_kernel(ScanParams p) {
     if (has_next) stage_write(sm.st[(c + 1) & 1], nk, nq, nv, ne);
     __syncthreads();
 
-    // ---- output: z = Q + LN(Z^Q), tokens 4w .. 4w+3 ----
-    {
-      const int t = 4 * w + g;
-      float z[NDT];
+    // ---- output: z = Q + LN(Z^Q) ----
+    if (ln_wave) {
+      const int t = ln_t;
+      float z[DPL];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int i = 0; i < DPL; ++i) {
+        const int dt = i;
         float s = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) s += sm.red[1][ww][dt][g][16 * w + c16];
-        z[dt] = s;
+        for (int ww = 0; ww < NW; ++ww) s += sm.red[1][ww][dt][t & 3][16 * (t >> 2) + c16];
+        z[i] = s;
       }
-      const float mu = sum16(z[0] + z[1] + z[2] + z[3]) * (1.0f / D);
+      float zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) zs += z[i];
+      const float mu = sum16(zs) * (1.0f / D);
       float var = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) var += (z[dt] - mu) * (z[dt] - mu);
+      for (int i = 0; i < DPL; ++i) var += (z[i] - mu) * (z[i] - mu);
       var = sum16(var) * (1.0f / D);
       const float rs = 1.0f / sqrtf(var + p.eps);
       float chk = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 16 * dt + c16;
-        const float o = bf(S.Q[t * RS + d]) + gam[dt] * (z[dt] - mu) * rs + bet[dt];
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        const float o = bf(S.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
         chk += o;
         Zg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)o;
       }
@@ -442,16 +480,24 @@ fwd_mfma_kernel(ScanParams p) {
 
 }  // namespace
 
+// Waves per workgroup of the launched variant (4: one wave per SIMD, 64 hidden units per
+// wave; 8: two waves per SIMD, 32 hidden units per wave). TTT_MFMA_WAVES overrides it at
+// build time.
+#ifndef TTT_MFMA_WAVES
+#define TTT_MFMA_WAVES 8
+#endif
+
 bool fwd_mfma_supported(const ScanParams& p) {
   return p.kind == TTT_MLP && p.d == D && p.hid == HID && p.chunk == BC && p.io == TTT_BF16;
 }
 
 hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t stream) {
-  const dim3 grid(p.B * p.H), block(256);
+  constexpr int NW = TTT_MFMA_WAVES;
+  const dim3 grid(p.B * p.H), block(64 * NW);
   if (p.gelu == TTT_GELU_TANH)
-    hipLaunchKernelGGL(fwd_mfma_kernel<TTT_GELU_TANH>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<TTT_GELU_TANH, NW>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(fwd_mfma_kernel<TTT_GELU_ERF>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<TTT_GELU_ERF, NW>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
