@@ -52,7 +52,7 @@ struct Stage {
 
 template <int NW>
 struct Smem {
-  Stage st[2];
+  Stage st[3];                   // chunk c lives in st[c % 3]
   float red[2][NW][NDT][4][64];  // [0]: Z^K partials, [1]: Z^Q partials
   __bf16 E2[BC * RS];            // En2, [token][d]
   __bf16 E2t[D * TS];            // En2, [d][token]
@@ -136,6 +136,7 @@ fwd_mfma_kernel(ScanParams p) {
   constexpr int EPT = BC * D / NT; // staged elements per thread and tensor
   // LayerNorm: waves 0..3, 4 tokens per wave, 16 lanes per token, 4 d values per lane
   constexpr int DPL = D / 16;
+  static_assert(NW == 8, "LayerNorm of Z^K runs on waves 0..3 while waves 4..7 emit the previous chunk");
   static_assert(NHT % 2 == 0 && EPT * NT == BC * D, "wave split");
   using SV = StageVec<EPT>;
   using LdT = typename SV::T;
@@ -172,7 +173,7 @@ fwd_mfma_kernel(ScanParams p) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) I4[j] = (__bf16)((4 * g + j) == c16 ? 1.0f : 0.0f);
 
-  // LayerNorm lane mapping (waves 0..3): token ln_t = 4w + lane/16, d = 16 i + lane%16
+  // LayerNorm lane mapping (waves 0..3 for Z^K): token ln_t = 4w + lane/16, d = 16 i + lane%16
   const bool ln_wave = w < 4;
   const int ln_t = 4 * w + g;
   float gam[DPL], bet[DPL];
@@ -206,6 +207,39 @@ fwd_mfma_kernel(ScanParams p) {
     vv = *reinterpret_cast<const LdT*>(Vg + off);
     e = tid < BC ? etag[chunk * BC + tid] : 0.f;
   };
+  // output z = Q + LN(Z^Q) of chunk cc, from the Z^Q partials in red[1] (waves 4..7,
+  // token 4 (w - 4) + lane/16, 16 lanes per token)
+  auto ln_out = [&](int cc) {
+    const Stage& So = sm.st[cc % 3];
+    const int t = 4 * (w - 4) + g;
+    float z[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) s += sm.red[1][ww][i][t & 3][16 * (t >> 2) + c16];
+      z[i] = s;
+    }
+    float zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) zs += z[i];
+    const float mu = sum16(zs) * (1.0f / D);
+    float var = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) var += (z[i] - mu) * (z[i] - mu);
+    var = sum16(var) * (1.0f / D);
+    const float rs = 1.0f / sqrtf(var + p.eps);
+    float chk = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = 16 * i + c16;
+      const float o = bf(So.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
+      chk += o;
+      Zg[static_cast<size_t>(cc * BC + t) * D + d] = (__bf16)o;
+    }
+    chk = sum16(chk);
+    if (c16 == 0) flag_nonfinite(p.status, chk);
+  };
   {
     LdT kk, qq, vv;
     float e;
@@ -215,7 +249,7 @@ fwd_mfma_kernel(ScanParams p) {
   __syncthreads();
 
   for (int c = 0; c < nchunks; ++c) {
-    Stage& S = sm.st[c & 1];
+    Stage& S = sm.st[c % 3];
     const int t0 = c * BC;
     LdT nk{}, nq{}, nv{};
     float ne = 0.f;
@@ -352,7 +386,11 @@ fwd_mfma_kernel(ScanParams p) {
         if (p.loss) p.loss[static_cast<size_t>(bh) * T + t0 + t] = loss;
         flag_nonfinite(p.status, loss);
       }
+    } else if (c > 0) {
+      ln_out(c - 1);  // the previous chunk's output, off the chunk-to-chunk critical path
     }
+    // stage the next chunk (its buffer last held chunk c - 2, whose readers are done)
+    if (has_next) stage_write(sm.st[(c + 1) % 3], nk, nq, nv, ne);
     __syncthreads();
 
     // ---- E1n = (En2 W2^T) (.) G ----
@@ -426,42 +464,10 @@ fwd_mfma_kernel(ScanParams p) {
         W2c[ht][dt] = mfma16(akR[ht], bE[dt], W2c[ht][dt]);
       }
     }
-    if (has_next) stage_write(sm.st[(c + 1) & 1], nk, nq, nv, ne);
-    __syncthreads();
-
-    // ---- output: z = Q + LN(Z^Q) ----
-    if (ln_wave) {
-      const int t = ln_t;
-      float z[DPL];
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const int dt = i;
-        float s = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) s += sm.red[1][ww][dt][t & 3][16 * (t >> 2) + c16];
-        z[i] = s;
-      }
-      float zs = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) zs += z[i];
-      const float mu = sum16(zs) * (1.0f / D);
-      float var = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) var += (z[i] - mu) * (z[i] - mu);
-      var = sum16(var) * (1.0f / D);
-      const float rs = 1.0f / sqrtf(var + p.eps);
-      float chk = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const int d = 16 * i + c16;
-        const float o = bf(S.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
-        chk += o;
-        Zg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)o;
-      }
-      chk = sum16(chk);
-      if (c16 == 0) flag_nonfinite(p.status, chk);
-    }
   }
+  // output of the last chunk
+  __syncthreads();
+  if (!ln_wave) ln_out(nchunks - 1);
 
   if (p.wt_1) {
     float* o1 = p.wt_1 + static_cast<size_t>(bh) * D * HID;
@@ -480,12 +486,8 @@ fwd_mfma_kernel(ScanParams p) {
 
 }  // namespace
 
-// Waves per workgroup of the launched variant (4: one wave per SIMD, 64 hidden units per
-// wave; 8: two waves per SIMD, 32 hidden units per wave). TTT_MFMA_WAVES overrides it at
-// build time.
-#ifndef TTT_MFMA_WAVES
+// Waves per workgroup: two per SIMD, 32 hidden units per wave.
 #define TTT_MFMA_WAVES 8
-#endif
 
 bool fwd_mfma_supported(const ScanParams& p) {
   return p.kind == TTT_MLP && p.d == D && p.hid == HID && p.chunk == BC && p.io == TTT_BF16;
