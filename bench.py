@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-T", type=int, default=4096)
     ap.add_argument("--force-generic", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the scan, time a plain device-to-device copy of MIB MiB "
+                         "(the known-size reference for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the scan's heads would be "
@@ -93,6 +96,22 @@ def main():
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS, make_inputs
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.randn(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "ms_per_copy": dt * 1e3, "GB_per_s": 8 * n / dt / 1e9}), flush=True)
+        return
 
     w = WORKLOADS[WORKLOAD_ID]
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,

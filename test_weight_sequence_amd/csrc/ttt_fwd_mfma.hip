@@ -41,6 +41,9 @@ constexpr int BC = 16;             // chunk
 constexpr int NDT = D / 16;        // d tiles
 constexpr int RS = D + 8;          // padded row stride (bf16 elements) of [token][d] arrays
 constexpr int TS = BC + 8;         // padded row stride of [d][token] arrays
+// Row stride (floats) of the cross-wave partial-sum rows. LayerNorm lanes read four rows at
+// once (16 lanes each); 80 = 64 + 16 puts the four rows on different banks.
+constexpr int PS = 80;
 
 struct Stage {
   __bf16 K[BC * RS];
@@ -53,7 +56,7 @@ struct Stage {
 template <int NW>
 struct Smem {
   Stage st[3];                   // chunk c lives in st[c % 3]
-  float red[2][NW][NDT][4][64];  // [0]: Z^K partials, [1]: Z^Q partials
+  float red[2][NW][NDT][4][PS];  // [0]: Z^K partials, [1]: Z^Q partials (64 used per row)
   __bf16 E2[BC * RS];            // En2, [token][d]
   __bf16 E2t[D * TS];            // En2, [d][token]
 };
