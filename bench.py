@@ -37,11 +37,19 @@ def bytes_per_token_head(d: int, io_bytes: int, nW: int, T: int) -> float:
     return 4 * d * io_bytes + 4 + 2 * nW * 4 / T
 
 
+KERNEL_SOURCES = {
+    "ttt_fwd_mfma_pair_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp"),
+    "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp"),
+    "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
+}
+
+
 def _source_hash(kernel: str) -> str:
-    src = os.path.join(ROOT, "test_weight_sequence_amd", "csrc",
-                       "ttt_fwd_mfma.hip" if kernel == "ttt_fwd_mfma_d64" else "ttt_fwd_generic.hip")
-    with open(src, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "test_weight_sequence_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str, n_launch_units: int):
@@ -57,20 +65,22 @@ def _traffic(kernel: str, n_launch_units: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_heads: int, T: int) -> dict:
+def cpu_baseline(w, n_seq: int, T: int) -> dict:
+    """The fp64 oracle on the first n_seq sequences (all H heads each), first T tokens."""
     import torch
     from oracle import OracleConfig, scan
     from test_weight_sequence_amd.synth import flatten_heads, make_inputs
     torch.set_num_threads(max(1, torch.get_num_threads()))
     cores = torch.get_num_threads()
-    hi = list(range(n_heads))
-    inp = flatten_heads(make_inputs(w, batch_idx=[0], head_idx=hi, T=T))
+    inp = flatten_heads(make_inputs(w, batch_idx=list(range(n_seq)), head_idx=list(range(w.H)), T=T))
+    n_heads = n_seq * w.H
     cfg = OracleConfig(kind=w.kind, chunk=w.chunk)
     t0 = time.perf_counter()
     scan(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"], inp["beta"], cfg)
     dt = time.perf_counter() - t0
     return {"value": n_heads * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle on {n_heads} heads x T={T} of the same workload "
+            "sample": f"fp64 oracle on sequences 0..{n_seq - 1} (all {w.H} heads, {n_heads} "
+                      f"(batch, head) pairs) x first T={T} tokens of the same workload "
                       f"({dt:.1f} s wall, torch intra-op threads={cores})"}
 
 
@@ -80,9 +90,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32)
-    ap.add_argument("--cpu-T", type=int, default=4096)
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--force-generic", action="store_true")
+    ap.add_argument("--one-wg", action="store_true",
+                    help="tuned kernel with one workgroup per head (no producer/consumer pair)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the scan, time a plain device-to-device copy of MIB MiB "
                          "(the known-size reference for scaling the HBM byte counters)")
@@ -115,7 +127,7 @@ def main():
 
     w = WORKLOADS[WORKLOAD_ID]
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
-                     io=w.io, force_generic=args.force_generic)
+                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
     kernel = ops.fwd_kernel_name(cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -168,7 +180,7 @@ def main():
     value = units / (ms_step * 1e-3)
     flop = units * flops_per_token_head(w.d, w.hidden, w.chunk)
     achieved = flop / (k_avg * 1e-3) / 1e12
-    mfma = kernel == "ttt_fwd_mfma_d64"
+    mfma = kernel != "ttt_fwd_generic"
     peak = PEAK_BF16_TFLOPS
     io_bytes = 2 if w.io == "bf16" else 4
     traffic = _traffic(kernel, units)
@@ -196,7 +208,7 @@ def main():
                          w.d, io_bytes, 2 * w.d * w.hidden, w.T)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads, args.cpu_T)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_T)
     print(json.dumps(out), flush=True)
 
 

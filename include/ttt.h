@@ -36,7 +36,10 @@
  *    runs on the host before anything is enqueued, so a non-OK return means nothing
  *    ran. A failed launch returns TTT_ERR_HIP. A non-finite loss or output detected
  *    inside a kernel is OR-ed into a status word in the workspace (sticky until
- *    ttt_reset_status); ttt_read_status reports it as TTT_ERR_NONFINITE.
+ *    ttt_reset_status); ttt_read_status reports it as TTT_ERR_NONFINITE. The paired
+ *    forward kernel (two workgroups per head that hand data to each other) bounds
+ *    every wait; an expired wait sets TTT_ERR_TIMEOUT in the same word (the outputs
+ *    of that call are then undefined).
  *  - No C++ exception crosses this interface. Calls that share a workspace must be
  *    ordered on one stream.
  */
@@ -62,7 +65,8 @@ typedef enum {
   TTT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than ttt_workspace_size     */
   TTT_ERR_HIP = 7,         /* a HIP runtime call failed                             */
   TTT_ERR_NONFINITE = 8,   /* a kernel saw a NaN/Inf loss or output                 */
-  TTT_ERR_ARG = 9          /* any other bad argument (unknown op, pos_in_chunk ...) */
+  TTT_ERR_ARG = 9,         /* any other bad argument (unknown op, pos_in_chunk ...) */
+  TTT_ERR_TIMEOUT = 10     /* a bounded wait between cooperating workgroups expired */
 } ttt_status;
 
 enum { TTT_LINEAR = 0, TTT_MLP = 1 };
@@ -71,7 +75,9 @@ enum { TTT_GELU_ERF = 0, TTT_GELU_TANH = 1 };
 /* ttt_config.flags */
 enum {
   TTT_W0_PER_SEQ = 1 << 0,    /* W0 (and dW0) are [B, H, ...] instead of [H, ...]         */
-  TTT_FORCE_GENERIC = 1 << 1  /* use the portable fp32 kernel even where a tuned one exists */
+  TTT_FORCE_GENERIC = 1 << 1, /* use the portable fp32 kernel even where a tuned one exists */
+  TTT_ONE_WG_PER_HEAD = 1 << 2 /* tuned forward: one workgroup per (batch, head) instead of a
+                                  producer/consumer pair of workgroups                      */
 };
 /* op codes for ttt_workspace_size */
 enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2 };
@@ -84,7 +90,7 @@ typedef struct {
   int32_t chunk;     /* mini-batch size b, 1 <= b <= 16; T % b == 0 for scans          */
   int32_t io_dtype;  /* TTT_F32 or TTT_BF16 for Q, K, V, Z, dQ, dK, dV, dZ             */
   int32_t gelu;      /* TTT_GELU_ERF (exact) or TTT_GELU_TANH                          */
-  int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC                             */
+  int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD       */
   float ln_eps;      /* LayerNorm epsilon inside the square root (e.g. 1e-6)           */
   float eta_scale;   /* multiplies every eta_t (1 = plain sum; 1/b = averaged sum)     */
 } ttt_config;
@@ -149,14 +155,18 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
                            int32_t pos_in_chunk, void* z, void* workspace, size_t ws_bytes,
                            void* stream);
 
-/* Synchronises `stream`, then reads the workspace status word: TTT_OK, or
- * TTT_ERR_NONFINITE if any kernel since the last reset saw a NaN/Inf. */
+/* Synchronises `stream`, then reads the workspace status word: TTT_OK,
+ * TTT_ERR_TIMEOUT if a paired forward launch since the last reset had a wait expire,
+ * else TTT_ERR_NONFINITE if any kernel since the last reset saw a NaN/Inf. */
 ttt_status ttt_read_status(const void* workspace, void* stream);
 
 /* Enqueues a zero-fill of the workspace status word on `stream`. */
 ttt_status ttt_reset_status(void* workspace, void* stream);
 
-/* Name of the kernel variant ttt_scan_fwd would launch for cfg ("" if invalid). */
+/* Name of the kernel variant ttt_scan_fwd would launch for cfg ("" if invalid). Host
+ * only: "ttt_fwd_mfma_pair_d64" is chosen for the tuned shape when B*H <= 128 and
+ * TTT_ONE_WG_PER_HEAD is not set; if the device then cannot hold all 2*ceil(B*H/8)*8
+ * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. */
 const char* ttt_fwd_kernel_name(const ttt_config* cfg);
 
 const char* ttt_status_str(ttt_status s);

@@ -22,7 +22,7 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   if (c->kind != TTT_LINEAR && c->kind != TTT_MLP) return TTT_ERR_UNSUPPORTED;
   if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
   if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH) return TTT_ERR_UNSUPPORTED;
-  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC)) return TTT_ERR_ARG;
+  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD)) return TTT_ERR_ARG;
   if (c->B < 1 || c->H < 1 || c->d < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
   if (need_T && c->T < 1) return TTT_ERR_SHAPE;
   if (c->d < 16 || c->d > 128 || c->d % 16 != 0) return TTT_ERR_UNSUPPORTED;
@@ -66,7 +66,13 @@ bool use_mfma(const ttt_config* c) {
   return fwd_mfma_supported(p);
 }
 
+bool use_pair(const ttt_config* c) {
+  return use_mfma(c) && !(c->flags & TTT_ONE_WG_PER_HEAD) &&
+         static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
+}
+
 size_t fwd_ws_bytes(const ttt_config* c) {
+  if (use_pair(c)) return kStatusBytes + fwd_pair_workspace_bytes(c->B * c->H);
   if (use_mfma(c)) return kStatusBytes;
   return kStatusBytes + static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
 }
@@ -98,6 +104,7 @@ const char* ttt_status_str(ttt_status s) {
     case TTT_ERR_HIP: return "HIP runtime error";
     case TTT_ERR_NONFINITE: return "non-finite value seen by a kernel";
     case TTT_ERR_ARG: return "bad argument";
+    case TTT_ERR_TIMEOUT: return "a bounded wait between cooperating workgroups expired";
   }
   return "unknown status";
 }
@@ -128,6 +135,7 @@ ttt_status ttt_saved_size(const ttt_config* cfg, size_t* bytes) {
 
 const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK) return "";
+  if (use_pair(cfg)) return "ttt_fwd_mfma_pair_d64";
   return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
 }
 
@@ -168,6 +176,7 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.status = static_cast<unsigned*>(workspace);
   p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
   return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
 }
 
@@ -292,6 +301,7 @@ ttt_status ttt_read_status(const void* workspace, void* stream) {
   unsigned word = 0;
   if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
     return TTT_ERR_HIP;
+  if (word & kStatusTimeout) return TTT_ERR_TIMEOUT;
   return (word & kStatusNonFinite) ? TTT_ERR_NONFINITE : TTT_OK;
 }
 

@@ -25,33 +25,12 @@
 // (dual form of the per-token rule on the page "Test-Time Training(TTT)과 LLM 메모리",
 // section "TTT layer", Eq. 2/4/5; mini-batch rule of the E2E paper review, section 2.3,
 // Eq. 5.)
-#include "ttt_device.hpp"
+#include "ttt_mfma_common.hpp"
 
 namespace ttt {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-constexpr int D = 64;
-constexpr int HID = 256;
-constexpr int BC = 16;             // chunk
-constexpr int NDT = D / 16;        // d tiles
-constexpr int RS = D + 8;          // padded row stride (bf16 elements) of [token][d] arrays
-constexpr int TS = BC + 8;         // padded row stride of [d][token] arrays
-// Row stride (floats) of the cross-wave partial-sum rows. LayerNorm lanes read four rows at
-// once (16 lanes each); 80 = 64 + 16 puts the four rows on different banks.
-constexpr int PS = 80;
-
-struct Stage {
-  __bf16 K[BC * RS];
-  __bf16 Q[BC * RS];
-  __bf16 V[BC * RS];
-  __bf16 Kt[D * TS];
-  float eta[BC];
-};
+using namespace mfma;
 
 template <int NW>
 struct Smem {
@@ -59,74 +38,6 @@ struct Smem {
   float red[2][NW][NDT][4][PS];  // [0]: Z^K partials, [1]: Z^Q partials (64 used per row)
   __bf16 E2[BC * RS];            // En2, [token][d]
   __bf16 E2t[D * TS];            // En2, [d][token]
-};
-
-__device__ __forceinline__ f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// K = 16 product (k = 4*(lane/16) + j, j < 4) issued as a 16x16x32 MFMA whose upper four
-// k-slots are zero in both operands. The result is identical; the kernel uses only the
-// 16x16x32 encoding (the legacy 16x16x16 bf16 encoding read a source register that the
-// compiler had already reallocated to a following VALU write).
-__device__ __forceinline__ f4 mfma16(bf16x4 a, bf16x4 b, f4 c) {
-  const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                 __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                 c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x4 cvt4(f4 v) {
-  bf16x4 r = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-  return r;
-}
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ bf16x4 lds4(const __bf16* p) {
-  return *reinterpret_cast<const bf16x4*>(p);
-}
-// Sum over aligned groups of 16 lanes with DPP moves (no LDS round trip). After the two
-// quad permutations every lane of a quad holds the quad sum, so mirroring within 8 lanes
-// and then within 16 lanes pairs each lane with the other half; every lane of the group
-// ends with the same bits.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
-}
-__device__ __forceinline__ float bf(__bf16 x) { return static_cast<float>(x); }
-
-// erf-form GELU through the branch-free A&S 7.1.26 evaluation (ttt_gelu.hpp); the tanh
-// form through the library tanh.
-template <int GELU_KIND>
-__device__ __forceinline__ void act_d(float x, float& v, float& d1) {
-  if (GELU_KIND == TTT_GELU_ERF)
-    ttt_gelu::gelu_d(x, v, d1);
-  else
-    gelu_d(x, GELU_KIND, v, d1);
-}
-template <int GELU_KIND>
-__device__ __forceinline__ float act(float x) {
-  return GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(x) : gelu(x, GELU_KIND);
-}
-
-// Staged elements per thread and their load type.
-template <int EPT>
-struct StageVec;
-template <>
-struct StageVec<4> {
-  using T = uint2;
-  using B = bf16x4;
-};
-template <>
-struct StageVec<2> {
-  using T = unsigned;
-  using B = bf16x2;
 };
 
 template <int GELU_KIND, int NW>
@@ -172,9 +83,7 @@ fwd_mfma_kernel(ScanParams p) {
         }
   }
   // identity operand for exact transposes (B[k][n] = [k == n], k = 4g + j, n = lane%16)
-  bf16x4 I4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) I4[j] = (__bf16)((4 * g + j) == c16 ? 1.0f : 0.0f);
+  const bf16x4 I4 = make_ident(g, c16).i4;
 
   // LayerNorm lane mapping (waves 0..3 for Z^K): token ln_t = 4w + lane/16, d = 16 i + lane%16
   const bool ln_wave = w < 4;

@@ -1,0 +1,785 @@
+// Forward scan for the TTT-MLP head shape d = 64, hidden = 256, chunk 16, bf16 I/O, fp32
+// fast weights, on TWO workgroups (two compute units) per (batch, head):
+//   producer: the chain that carries the weights from chunk to chunk -- H^K = K W1,
+//             A^K = GELU, G = GELU', Z^K = A^K W2, the LayerNorm forward/backward of Z^K
+//             (En2 = -eta * delta2), E1n = (En2 W2^T) (.) G, then W1 += K^T E1n and
+//             W2 += A^K^T En2. It hands E1n, A^K and En2 of every chunk to its partner.
+//   consumer: replays the same weight update from the same bf16 operands (so its fp32
+//             weights stay bitwise equal to the producer's) and computes the query side of
+//             the dual form: H^Q = Q W1 + tril(Q K^T) E1n, A^Q = GELU(H^Q),
+//             Z^Q = A^Q W2 + tril(A^Q A^K^T) En2, z = Q + LN(Z^Q).
+// Nothing flows from the consumer to the producer except "slot consumed" counters, so the
+// query side is off the chunk-to-chunk critical path. (Dual form of the per-token rule on
+// the page "Test-Time Training(TTT)과 LLM 메모리", section "TTT layer", Eq. 2/4/5;
+// mini-batch rule of the E2E paper review, section 2.3, Eq. 5.)
+//
+// The producer's chain is shortened by a look-ahead: with W1(c+1) = W1(c) + K(c)^T E1n(c),
+//   H^K(c+1) = K(c+1) W1(c) + (K(c+1) K(c)^T) E1n(c),
+// and K(c+1) W1(c) is computed while chunk c is in flight. Between E1n(c) and H^K(c+1) there
+// is then one K = 16 product; the fp32 weight update of chunk c is applied at the start of
+// chunk c + 1, next to the GELU work, where it is off the chain. (The same identity is the
+// dual form's own: the look-ahead term is the next chunk's first dual-form correction.)
+//
+// Hand-off: a ring of RING chunk slots per head in the workspace, and per-wave counters
+// (ready[w] = chunks published by producer wave w, consumed[w] = chunks consumer wave w is
+// done reading). A producer wave waits for its slot stores to complete (s_waitcnt vmcnt)
+// before it raises its counter, and a consumer wave issues its slot loads only after it has
+// seen the counter. Workgroups b and b + 8 of each group of 16 form a pair; workgroups are
+// dealt to the 8 XCDs round-robin, so both normally sit on one XCD. Each side reads its XCD
+// id at start and the two compare them through device-coherent atomics: on one XCD the
+// hand-off meets in the shared L2 (plain stores through the write-through L1, device-scope
+// loads that skip the L1); otherwise every hand-off access is an agent-scope atomic.
+//
+// Every wait is bounded. On expiry the status word gets kStatusTimeout, later waits return
+// at once, and the kernel runs to completion with meaningless outputs. The launch is
+// cooperative, so the two workgroups of a pair are always co-resident.
+#include "ttt_mfma_common.hpp"
+
+namespace ttt {
+namespace {
+
+using namespace mfma;
+
+constexpr int NW = 8;                  // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int HS = HID / NW;           // hidden units per wave (32)
+constexpr int NHT = HS / 16;           // h tiles per wave (2)
+constexpr int RING = 6;                // chunk slots per head
+constexpr int ZS = 40;                 // row stride (bf16) of the zero-padded [d][4 x 8] arrays (16-byte rows)
+// slot layout (bytes): E1n and A^K of wave w as one 16-byte (two-tile) operand per lane,
+// then En2 as four 8-byte (k = token, n = d) operands per lane
+constexpr int SLOT_E1 = 0;
+constexpr int SLOT_AK = NW * 64 * 16;
+constexpr int SLOT_E2 = 2 * NW * 64 * 16;
+constexpr int SLOT_BYTES = SLOT_E2 + 64 * 32;
+constexpr int FLAG_WORDS = 32;         // per head: ready[0..7], consumed[16..23], XCD ids
+constexpr int FLAG_XCC = 24;           // producer's and consumer's XCD id + 1 (words 24, 25)
+constexpr int kSpinLimit = 1 << 20;
+static_assert(NHT == 2, "layout assumes 8 waves of 32 hidden units");
+
+struct Pair {
+  unsigned* flags;  // [head][FLAG_WORDS]
+  char* ring;       // [head][RING][SLOT_BYTES]
+  int nheads;
+};
+
+// [d][group of 4 tokens][8] with the group's 4 values in one half and zeros in the other:
+// lo = (data, zero), hi = (zero, data). A 16-byte read gives a K = 16 operand padded to the
+// 16x16x32 MFMA's K = 32, data in the lower or upper four k-slots.
+struct ZPad2 {
+  alignas(16) __bf16 lo[D * ZS];
+  alignas(16) __bf16 hi[D * ZS];
+};
+__device__ __forceinline__ bf16x8 zp_lo(const ZPad2& z, int d, int g) {
+  return *reinterpret_cast<const bf16x8*>(&z.lo[d * ZS + 8 * g]);
+}
+__device__ __forceinline__ bf16x8 zp_hi(const ZPad2& z, int d, int g) {
+  return *reinterpret_cast<const bf16x8*>(&z.hi[d * ZS + 8 * g]);
+}
+__device__ __forceinline__ bf16x4 zp_data(const ZPad2& z, int d, int g) {
+  return *reinterpret_cast<const bf16x4*>(&z.hi[d * ZS + 8 * g + 4]);
+}
+__device__ __forceinline__ void zp_put(ZPad2& z, int d, int t, __bf16 v) {
+  z.lo[d * ZS + 8 * (t >> 2) + (t & 3)] = v;
+  z.hi[d * ZS + 8 * (t >> 2) + 4 + (t & 3)] = v;
+}
+__device__ __forceinline__ void zp_clear(ZPad2& z, int i) {  // i < D * 4: zero halves of one group
+  const int d = i >> 2, gg = i & 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    z.lo[d * ZS + 8 * gg + 4 + j] = (__bf16)0.f;
+    z.hi[d * ZS + 8 * gg + j] = (__bf16)0.f;
+  }
+}
+
+struct PStage {
+  alignas(16) __bf16 K[BC * RS];
+  alignas(16) __bf16 X[BC * RS];  // V (producer) or Q (consumer)
+  alignas(16) float eta[BC];
+};
+struct ProdSmem {
+  PStage st[4];   // chunk j in slot j & 3
+  ZPad2 Ktz[4];
+  float red[NW][NDT][4][PS];
+  alignas(16) __bf16 E2[BC * RS];  // En2 [token][d]
+  ZPad2 E2z;           // En2 zero-padded [d][token]
+  alignas(16) __bf16 zeros[8];
+};
+struct ConsSmem {
+  PStage st[3];   // chunk j in slot j % 3
+  ZPad2 Ktz[3];
+  float red[2][NW][NDT][4][PS];
+  alignas(16) __bf16 zeros[8];
+};
+union SmemP {
+  ProdSmem p;
+  ConsSmem c;
+};
+
+// Cache policy of hand-off loads on one XCD: device scope (sc1), which skips the CU's L1
+// (a plain or sc0 load may return a line the L1 still holds from an earlier read).
+constexpr int kLoadL2 = 16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
+typedef u64 u64x2 __attribute__((ext_vector_type(2)));
+
+// Hand-off memory of one head: its counter words and its ring of chunk slots.
+template <bool LOCAL>
+struct HandOff {
+  unsigned* flags;
+  char* ring;
+  __amdgpu_buffer_rsrc_t fr, rr;
+  __device__ __forceinline__ HandOff(unsigned* f, char* r) : flags(f), ring(r) {
+    fr = __builtin_amdgcn_make_buffer_rsrc(f, 0, FLAG_WORDS * 4, kBufFlags);
+    rr = __builtin_amdgcn_make_buffer_rsrc(r, 0, RING * SLOT_BYTES, kBufFlags);
+  }
+  __device__ __forceinline__ unsigned ld(int i) const {
+    if constexpr (LOCAL)
+      return __builtin_amdgcn_raw_buffer_load_b32(fr, 0, 4 * i, kLoadL2);
+    else
+      return __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void st(int i, unsigned v) const {
+    if constexpr (LOCAL)
+      __builtin_amdgcn_raw_buffer_store_b32(v, fr, 0, 4 * i, 0);
+    else
+      __hip_atomic_store(flags + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ bf16x8 ld16(int off) const {
+    if constexpr (LOCAL) {
+      return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, kLoadL2));
+    } else {
+      const u64* q = reinterpret_cast<const u64*>(ring + off);
+      const u64x2 v = {__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __device__ __forceinline__ void st16(int off, bf16x8 v) const {
+    if constexpr (LOCAL) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rr, off, 0, 0);
+    } else {
+      const u64x2 x = __builtin_bit_cast(u64x2, v);
+      u64* q = reinterpret_cast<u64*>(ring + off);
+      __hip_atomic_store(q, x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, x[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+};
+
+// Wait until counter word i >= target, at most kSpinLimit polls; gives up at once once any
+// wave of the launch has timed out.
+template <bool LOCAL>
+__device__ __forceinline__ void spin_geq(const HandOff<LOCAL>& h, int i, unsigned target, unsigned* status) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (h.ld(i) >= target) return;
+    if ((it & 63) == 0 && (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout))
+      return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  atomicOr(status, kStatusTimeout);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// One chunk's hand-off data as held by a consumer lane.
+struct Slot {
+  bf16x8 e1, ak;
+  bf16x8 e2[2];  // En2 tiles (d tiles 0,1) and (2,3), each 4 values with k = token
+};
+template <bool LOCAL>
+__device__ __forceinline__ void slot_load(const HandOff<LOCAL>& h, Slot& s, int chunk, int w, int lane) {
+  const int base = (chunk % RING) * SLOT_BYTES;
+  s.e1 = h.ld16(base + SLOT_E1 + (w * 64 + lane) * 16);
+  s.ak = h.ld16(base + SLOT_AK + (w * 64 + lane) * 16);
+  s.e2[0] = h.ld16(base + SLOT_E2 + lane * 32);
+  s.e2[1] = h.ld16(base + SLOT_E2 + lane * 32 + 16);
+}
+__device__ __forceinline__ bf16x4 slot_e2(const Slot& s, int dt) { return dt & 1 ? hi4(s.e2[dt >> 1]) : lo4(s.e2[dt >> 1]); }
+// A value that depends on every register of the slot: the compiler must wait for all its
+// loads before computing it.
+__device__ __forceinline__ unsigned slot_dep(const Slot& s) {
+  const u64x2 a = __builtin_bit_cast(u64x2, s.e1), b = __builtin_bit_cast(u64x2, s.ak);
+  const u64x2 c = __builtin_bit_cast(u64x2, s.e2[0]), d = __builtin_bit_cast(u64x2, s.e2[1]);
+  const u64 x = a[0] ^ a[1] ^ b[0] ^ b[1] ^ c[0] ^ c[1] ^ d[0] ^ d[1];
+  return static_cast<unsigned>(x) ^ static_cast<unsigned>(x >> 32);
+}
+
+// What the producer carries from chunk c - 1 into chunk c.
+struct Carry {
+  f4 P[NHT];       // K(c) W1(c-1) for this wave's h tiles
+  bf16x4 sA;       // K(c) K(c-1)^T as an A operand (m = token of c, k = token of c-1)
+  bf16x8 e1, ak;   // E1n(c-1), A^K(c-1): k = token (two h tiles)
+};
+
+// The 16 MFMAs of a chunk-end update: W1 += K^T E1n, W2 += A^K^T En2 (K = 16 over the
+// chunk's tokens, operands padded by the zero halves of the [d][token] arrays).
+__device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const ZPad2& Kt,
+                                             const ZPad2& E2t, bf16x8 e1, bf16x8 ak, int g, int c16) {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int d = 16 * dt + c16;
+    W1c[dt][0] = mfma32(zp_lo(Kt, d, g), e1, W1c[dt][0]);
+    W1c[dt][1] = mfma32(zp_hi(Kt, d, g), e1, W1c[dt][1]);
+    W2c[0][dt] = mfma32(ak, zp_lo(E2t, d, g), W2c[0][dt]);
+    W2c[1][dt] = mfma32(ak, zp_hi(E2t, d, g), W2c[1][dt]);
+  }
+}
+
+// Operands of a staged [token][d] chunk: rows (token = lane%16), permuted d order.
+__device__ __forceinline__ void rows(const __bf16* X, int g, int c16, bf16x8 (&a)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    a[ks] = cat(lds4(&X[c16 * RS + 32 * ks + 4 * g]), lds4(&X[c16 * RS + 32 * ks + 16 + 4 * g]));
+}
+// bf16 operand copies of the fp32 weight tiles.
+__device__ __forceinline__ void cvt_w(const f4 (&W1c)[NDT][NHT], const f4 (&W2c)[NHT][NDT], bf16x4 (&W1b)[NDT][NHT],
+                                      bf16x8 (&W2b8)[NDT]) {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) W1b[dt][ht] = cvt4(W1c[dt][ht]);
+    W2b8[dt] = cat(cvt4(W2c[0][dt]), cvt4(W2c[1][dt]));
+  }
+}
+// X W1 for this wave's h tiles (X as row operands).
+__device__ __forceinline__ void xw1(const bf16x8 (&a)[2], const bf16x4 (&W1b)[NDT][NHT], f4 (&out)[NHT]) {
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    f4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) acc = mfma32(a[ks], cat(W1b[2 * ks][ht], W1b[2 * ks + 1][ht]), acc);
+    out[ht] = acc;
+  }
+}
+
+// Per-workgroup view of one (batch, head).
+struct Ctx {
+  int tid, lane, w, g, c16, head, hidx, hs, T, nchunks;
+  unsigned* flags;  // counter words of this head
+  char* ring;       // ring of this head
+  const __bf16* Kg;
+  const __bf16* Xg;  // V (producer) or Q (consumer)
+  __bf16* Zg;
+  const float* etag;
+};
+// Chunk-start weights of the head, LayerNorm affine parameters and identity operands.
+struct HeadState {
+  f4 W1c[NDT][NHT], W2c[NHT][NDT];
+  float gam[NDT], bet[NDT];
+  Ident id;
+};
+__device__ __forceinline__ void head_init(const ScanParams& p, const Ctx& x, HeadState& h) {
+  const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
+  const size_t wh = per_seq ? static_cast<size_t>(x.head) : static_cast<size_t>(x.hidx);
+  wtiles_load(p.w0_1 + wh * D * HID, p.w0_2 + wh * HID * D, x.g, x.c16, x.hs, h.W1c, h.W2c);
+  h.id = make_ident(x.g, x.c16);
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) {
+    h.gam[i] = p.gamma[x.hidx * D + 16 * i + x.c16];
+    h.bet[i] = p.beta[x.hidx * D + 16 * i + x.c16];
+  }
+}
+
+template <int GELU_KIND, bool LOCAL>
+__device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x, ProdSmem& S) {
+  const int tid = x.tid, lane = x.lane, w = x.w, g = x.g, c16 = x.c16, head = x.head, hs = x.hs;
+  const int T = x.T, nchunks = x.nchunks;
+  const HandOff<LOCAL> ho(x.flags, x.ring);
+  const __bf16* Kg = x.Kg;
+  const __bf16* Xg = x.Xg;
+  const float* etag = x.etag;
+  HeadState hst;
+  head_init(p, x, hst);
+  auto& W1c = hst.W1c;
+  auto& W2c = hst.W2c;
+  const float* gam = hst.gam;
+  const float* bet = hst.bet;
+  const Ident& id = hst.id;
+  for (int i = tid; i < D * 4; i += NT) {
+    zp_clear(S.E2z, i);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) zp_clear(S.Ktz[s4], i);
+  }
+  if (tid < 8) S.zeros[tid] = (__bf16)0.f;
+  // staging by waves 4..7: thread -> (token, 4 consecutive d). Every wave issues exactly
+  // three loads (K, V, eta) per chunk (waves 0..3 load the same addresses as waves 4..7 and
+  // drop the data), so the count of memory operations after the slot stores is fixed.
+  const int lt = tid & 255;
+  const int st_t = lt >> 4, st_d = (lt & 15) * 4;
+  struct Ld {
+    uint2 k, x;
+    float e;
+  };
+  auto gload = [&](int chunk) {
+    Ld r;
+    const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
+    r.k = *reinterpret_cast<const uint2*>(Kg + off);
+    r.x = *reinterpret_cast<const uint2*>(Xg + off);
+    r.e = etag[chunk * BC + (lt & 15)];
+    return r;
+  };
+  auto stage_write = [&](int chunk, const Ld& r) {
+    PStage& st = S.st[chunk & 3];
+    *reinterpret_cast<uint2*>(&st.K[st_t * RS + st_d]) = r.k;
+    *reinterpret_cast<uint2*>(&st.X[st_t * RS + st_d]) = r.x;
+    const bf16x4 kv = __builtin_bit_cast(bf16x4, r.k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zp_put(S.Ktz[chunk & 3], st_d + j, st_t, kv[j]);
+    if (lt < BC) st.eta[lt] = r.e * p.eta_scale;
+  };
+  if (w >= 4) {
+    stage_write(0, gload(0));
+    if (nchunks > 1) stage_write(1, gload(1));
+  }
+  __syncthreads();
+  const bf16x4 zz = lds4(S.zeros);
+
+  // chunk 0 enters with P = K(0) W0, and zero look-ahead terms
+  Carry ca{}, cb{};
+  {
+    bf16x4 W1b[NDT][NHT];
+    bf16x8 W2b8[NDT];
+    cvt_w(W1c, W2c, W1b, W2b8);
+    bf16x8 aK[2];
+    rows(S.st[0].K, g, c16, aK);
+    xw1(aK, W1b, ca.P);
+  }
+
+  auto step = [&](const int c, const Carry& in, Carry& out) {
+    const PStage& st = S.st[c & 3];
+    const int t0 = c * BC;
+    const Ld ld = gload(min(c + 2, nchunks - 1));
+    // H^K(c) = K(c) W1(c-1) + (K(c) K(c-1)^T) E1n(c-1)
+    f4 hk[NHT];
+    hk[0] = mfma32(cat(in.sA, zz), in.e1, in.P[0]);
+    hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
+    // the update of chunk c - 1 (W(c) = W(c-1) + ...), next to the GELU work
+    if (c > 0) chunk_update(W1c, W2c, S.Ktz[(c - 1) & 3], S.E2z, in.e1, in.ak, g, c16);
+    // A^K (R layout: m = h, k = token), G
+    bf16x4 akR[NHT];
+    f4 gk[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f4 a, gd;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v, d1;
+        act_d<GELU_KIND>(hk[ht][r], v, d1);
+        a[r] = v;
+        gd[r] = d1;
+      }
+      gk[ht] = gd;
+      akR[ht] = cvt4(a);
+    }
+    out.ak = cat(akR[0], akR[1]);
+    bf16x4 W1b[NDT][NHT];
+    bf16x8 W2b8[NDT];
+    cvt_w(W1c, W2c, W1b, W2b8);
+    // look-ahead for chunk c + 1: K(c+1) W1(c) and K(c+1) K(c)^T
+    if (c + 1 < nchunks) {
+      bf16x8 aK[2], aK1[2];
+      rows(st.K, g, c16, aK);
+      rows(S.st[(c + 1) & 3].K, g, c16, aK1);
+      xw1(aK1, W1b, out.P);
+      f4 sT = mfma32(aK[0], aK1[0], zero4());  // C[t][t'] = K(c)_t . K(c+1)_t'
+      sT = mfma32(aK[1], aK1[1], sT);
+      out.sA = cvt4(sT);
+    }
+    // Z^K partial over this wave's h slice
+    const bf16x8 akT8 = cat(cvt4(mfma32(out.ak, id.ilo, zero4())), cvt4(mfma32(out.ak, id.ihi, zero4())));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f4 acc = mfma32(akT8, W2b8[dt], zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.red[w][dt][r][lane] = acc[r];
+    }
+    // W2(c)^T tiles for E1n: waves 0..3 now, waves 4..7 during the LayerNorm
+    bf16x4 W2Tb[NDT][NHT];
+    auto w2t = [&]() {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        W2Tb[dt][0] = cvt4(mfma32(W2b8[dt], id.ilo, zero4()));
+        W2Tb[dt][1] = cvt4(mfma32(W2b8[dt], id.ihi, zero4()));
+      }
+    };
+    if (w < 4) w2t();
+    // publish chunk c - 1: its slot stores were the last vector-memory operations before
+    // this chunk's three input loads
+    if (c > 0) {
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+      if (lane == 0) ho.st(w, static_cast<unsigned>(c));
+      compiler_fence();
+    }
+    // consumed counters for this chunk's slot (own consumer wave; wave 0 also writes the
+    // En2 part that every consumer wave reads), reduced after the barriers
+    unsigned cv[NW];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) cv[ww] = ho.ld(16 + ww);
+    if (p.saved) {
+      float* sv = p.saved + (static_cast<size_t>(head) * nchunks + c) * (2 * D * HID);
+      wtiles_store(sv, sv + D * HID, g, c16, hs, W1c, W2c);
+    }
+    __syncthreads();
+
+    if (w < 4) {
+      // LayerNorm forward/backward of Z^K: token 4w + lane/16, 16 lanes each
+      const int t = 4 * w + g;
+      float z[NDT];
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += S.red[ww][i][t & 3][16 * (t >> 2) + c16];
+        z[i] = s;
+      }
+      const LnStats ls = ln_stats(z, p.eps);
+      float xh[NDT], gg[NDT], l2 = 0.f, sg = 0.f, sgx = 0.f;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int d = 16 * i + c16;
+        xh[i] = (z[i] - ls.mu) * ls.rs;
+        const float r = bf(st.K[t * RS + d]) + gam[i] * xh[i] + bet[i] - bf(st.X[t * RS + d]);
+        l2 += r * r;
+        gg[i] = 2.f * r * gam[i];
+        sg += gg[i];
+        sgx += gg[i] * xh[i];
+      }
+      const float loss = sum16(l2);
+      const float mg = sum16(sg) * (1.0f / D), mgx = sum16(sgx) * (1.0f / D);
+      const float ne2 = -st.eta[t] * ls.rs;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int d = 16 * i + c16;
+        const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
+        S.E2[t * RS + d] = e;
+        zp_put(S.E2z, d, t, e);
+      }
+      if (c16 == 0) {
+        if (p.loss) p.loss[static_cast<size_t>(head) * T + t0 + t] = loss;
+        flag_nonfinite(p.status, loss);
+      }
+    } else {
+      w2t();
+      if (c + 2 < nchunks) stage_write(c + 2, ld);
+    }
+    __syncthreads();
+
+    // E1n(c) = (En2 W2^T) (.) G
+    bf16x8 aE[2];
+    rows(S.E2, g, c16, aE);
+    bf16x4 e1[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc = mfma32(aE[ks], cat(W2Tb[2 * ks][ht], W2Tb[2 * ks + 1][ht]), acc);
+      e1[ht] = cvt4(acc * gk[ht]);
+    }
+    out.e1 = cat(e1[0], e1[1]);
+
+    // hand chunk c to the consumer: slot c % RING must have been read (chunk c - RING)
+    const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
+    unsigned cons = ~0u;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) cons = (w == 0 || ww == w) ? min(cons, cv[ww]) : cons;
+    if (cons < need) {
+      spin_geq(ho, 16 + w, need, p.status);
+      if (w == 0)
+        for (int ww = 1; ww < NW; ++ww) spin_geq(ho, 16 + ww, need, p.status);
+    }
+    compiler_fence();
+    const int base = (c % RING) * SLOT_BYTES;
+    ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
+    ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
+    if (w == 0) {
+      ho.st16(base + SLOT_E2 + lane * 32, cat(zp_data(S.E2z, c16, g), zp_data(S.E2z, 16 + c16, g)));
+      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(zp_data(S.E2z, 32 + c16, g), zp_data(S.E2z, 48 + c16, g)));
+    }
+    compiler_fence();
+  };
+
+  // two chunks per trip, so the carried registers alternate without copies
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(c, ca, cb);
+    step(c + 1, cb, ca);
+  }
+  if (c < nchunks) step(c, ca, cb);
+  const Carry& last = (nchunks & 1) ? cb : ca;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0) ho.st(w, static_cast<unsigned>(nchunks));
+  // the last chunk's update (its En2 is still in E2z)
+  chunk_update(W1c, W2c, S.Ktz[(nchunks - 1) & 3], S.E2z, last.e1, last.ak, g, c16);
+  if (p.wt_1)
+    wtiles_store(p.wt_1 + static_cast<size_t>(head) * D * HID, p.wt_2 + static_cast<size_t>(head) * HID * D,
+                 g, c16, hs, W1c, W2c);
+  return;
+}
+
+template <int GELU_KIND, bool LOCAL>
+__device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x, ConsSmem& S) {
+  const int tid = x.tid, lane = x.lane, w = x.w, g = x.g, c16 = x.c16;
+  const int nchunks = x.nchunks;
+  const HandOff<LOCAL> ho(x.flags, x.ring);
+  const __bf16* Kg = x.Kg;
+  const __bf16* Xg = x.Xg;
+  __bf16* Zg = x.Zg;
+  HeadState hst;
+  head_init(p, x, hst);
+  auto& W1c = hst.W1c;
+  auto& W2c = hst.W2c;
+  const float* gam = hst.gam;
+  const float* bet = hst.bet;
+  const Ident& id = hst.id;
+  for (int i = tid; i < D * 4; i += NT) {
+#pragma unroll
+    for (int s3 = 0; s3 < 3; ++s3) zp_clear(S.Ktz[s3], i);
+  }
+  if (tid < 8) S.zeros[tid] = (__bf16)0.f;
+  // staging by all waves: thread -> (token, 2 consecutive d)
+  const int st_t = tid >> 5, st_d = (tid & 31) * 2;
+  struct Ld {
+    unsigned k, x;
+  };
+  auto gload = [&](int chunk) {
+    Ld r;
+    const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
+    r.k = *reinterpret_cast<const unsigned*>(Kg + off);
+    r.x = *reinterpret_cast<const unsigned*>(Xg + off);
+    return r;
+  };
+  auto stage_write = [&](int slot, const Ld& r) {
+    PStage& st = S.st[slot];
+    *reinterpret_cast<unsigned*>(&st.K[st_t * RS + st_d]) = r.k;
+    *reinterpret_cast<unsigned*>(&st.X[st_t * RS + st_d]) = r.x;
+    const bf16x2 kv = __builtin_bit_cast(bf16x2, r.k);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) zp_put(S.Ktz[slot], st_d + j, st_t, kv[j]);
+  };
+  stage_write(0, gload(0));
+  __syncthreads();
+  const bf16x4 zz = lds4(S.zeros);
+
+  auto ln_out = [&](int cc) {
+    const PStage& So = S.st[cc % 3];
+    const int t = 4 * w + g;
+    float z[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) s += S.red[cc & 1][ww][i][t & 3][16 * (t >> 2) + c16];
+      z[i] = s;
+    }
+    const LnStats ls = ln_stats(z, p.eps);
+    float chk = 0.f;
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const int d = 16 * i + c16;
+      const float o = bf(So.X[t * RS + d]) + gam[i] * (z[i] - ls.mu) * ls.rs + bet[i];
+      chk += o;
+      Zg[static_cast<size_t>(cc * BC + t) * D + d] = (__bf16)o;
+    }
+    chk = sum16(chk);
+    if (c16 == 0) flag_nonfinite(p.status, chk);
+  };
+
+  auto step = [&](const int c, const Slot& cur, Slot& nxt) {
+    const int sl = c % 3;
+    const PStage& st = S.st[sl];
+    const bool has_next = c + 1 < nchunks;
+    // counters for chunk c + 1, checked late in this chunk
+    const unsigned rdy_own = ho.ld(w), rdy_0 = ho.ld(0);
+    Ld ld{};
+    if (has_next) ld = gload(c + 1);
+    bf16x8 aK[2], aQ[2];
+    rows(st.K, g, c16, aK);
+    rows(st.X, g, c16, aQ);
+    bf16x4 W1b[NDT][NHT];
+    bf16x8 W2b8[NDT];
+    cvt_w(W1c, W2c, W1b, W2b8);
+    f4 hq[NHT];
+    xw1(aQ, W1b, hq);
+    f4 s1t = zero4();  // C[s][t] = K_s . Q_t
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) s1t = mfma32(aK[ks], aQ[ks], s1t);
+
+    // H^Q = Q W1 + tril(Q K^T) E1n ; A^Q = GELU(H^Q)
+    f4 s1m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s1m[r] = (4 * g + r) <= c16 ? s1t[r] : 0.f;
+    const bf16x4 s1a = cvt4(s1m);
+    bf16x4 aqR[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const f4 h = mfma32(ht == 0 ? cat(s1a, zz) : cat(zz, s1a), cur.e1, hq[ht]);
+      f4 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = act<GELU_KIND>(h[r]);
+      aqR[ht] = cvt4(a);
+    }
+    const bf16x8 aqR8 = cat(aqR[0], aqR[1]);
+    const bf16x8 aqT8 = cat(cvt4(mfma32(aqR8, id.ilo, zero4())), cvt4(mfma32(aqR8, id.ihi, zero4())));
+    const bf16x8 akT8 = cat(cvt4(mfma32(cur.ak, id.ilo, zero4())), cvt4(mfma32(cur.ak, id.ihi, zero4())));
+    // Z^Q partial = A^Q W2 + tril(A^Q A^K^T) En2 over this wave's h slice
+    const f4 s2t = mfma32(akT8, aqT8, zero4());  // C[s][t] = A^K_s . A^Q_t (this slice)
+    f4 s2m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s2m[r] = (4 * g + r) <= c16 ? s2t[r] : 0.f;
+    const bf16x8 s2a8 = cat(cvt4(s2m), zz);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f4 acc = mfma32(aqT8, W2b8[dt], zero4());
+      acc = mfma32(s2a8, cat(slot_e2(cur, dt), zz), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.red[c & 1][w][dt][r][lane] = acc[r];
+    }
+    // the producer's chunk-end update, from the same operands
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = 16 * dt + c16;
+      W1c[dt][0] = mfma32(zp_lo(S.Ktz[sl], d, g), cur.e1, W1c[dt][0]);
+      W1c[dt][1] = mfma32(zp_hi(S.Ktz[sl], d, g), cur.e1, W1c[dt][1]);
+      W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);
+      W2c[1][dt] = mfma32(cur.ak, cat(zz, slot_e2(cur, dt)), W2c[1][dt]);
+    }
+    // release slot c (its loads have returned: the dependency forces the wait), then
+    // prefetch chunk c + 1
+    {
+      const unsigned dep = slot_dep(cur);
+      asm volatile("" ::"v"(dep) : "memory");
+      if (lane == 0) ho.st(16 + w, static_cast<unsigned>(c + 1));
+      compiler_fence();
+    }
+    if (has_next) {
+      const unsigned need = static_cast<unsigned>(c + 2);
+      if (min(rdy_own, rdy_0) < need) {
+        spin_geq(ho, w, need, p.status);
+        if (w != 0) spin_geq(ho, 0, need, p.status);
+      }
+      compiler_fence();
+      slot_load(ho, nxt, c + 1, w, lane);
+      stage_write((c + 1) % 3, ld);
+    }
+    __syncthreads();
+    if (w < 4) ln_out(c);
+  };
+
+  spin_geq(ho, w, 1u, p.status);
+  if (w != 0) spin_geq(ho, 0, 1u, p.status);
+  compiler_fence();
+  Slot sa, sb;
+  slot_load(ho, sa, 0, w, lane);
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(c, sa, sb);
+    step(c + 1, sb, sa);
+  }
+  if (c < nchunks) step(c, sa, sb);
+}
+
+template <int GELU_KIND>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_mfma_pair_kernel(ScanParams p, Pair q) {
+  __shared__ SmemP sm;
+  Ctx x;
+  x.tid = threadIdx.x;
+  x.lane = x.tid & 63;
+  x.w = x.tid >> 6;
+  x.g = x.lane >> 4;
+  x.c16 = x.lane & 15;
+  const int b = blockIdx.x;
+  x.head = (b >> 4) * 8 + (b & 7);
+  const bool producer = ((b >> 3) & 1) == 0;
+  if (x.head >= q.nheads) return;  // both members of a padding pair leave
+  x.hidx = x.head % p.H;
+  x.hs = x.w * HS;
+  x.T = p.T;
+  x.nchunks = p.T / BC;
+  x.flags = q.flags + static_cast<size_t>(x.head) * FLAG_WORDS;
+  x.ring = q.ring + static_cast<size_t>(x.head) * RING * SLOT_BYTES;
+  const size_t io_off = static_cast<size_t>(x.head) * p.T * D;
+  x.Kg = static_cast<const __bf16*>(p.K) + io_off;
+  x.Xg = static_cast<const __bf16*>(producer ? p.V : p.Q) + io_off;
+  x.Zg = static_cast<__bf16*>(p.Z) + io_off;
+  x.etag = p.eta + static_cast<size_t>(x.head) * p.T;
+  // placement: each side publishes its XCD id + 1 (device-coherent) and reads the partner's
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  const int mine = producer ? FLAG_XCC : FLAG_XCC + 1, theirs = producer ? FLAG_XCC + 1 : FLAG_XCC;
+  if (x.tid == 0) __hip_atomic_store(x.flags + mine, xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned other = 0;
+  for (int it = 0; it < kSpinLimit; ++it) {
+    other = __hip_atomic_load(x.flags + theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (other != 0) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (other == 0 && x.tid == 0) atomicOr(p.status, kStatusTimeout);
+  const bool local = other == xcc + 1;
+  if (producer) {
+    if (local)
+      producer_body<GELU_KIND, true>(p, x, sm.p);
+    else
+      producer_body<GELU_KIND, false>(p, x, sm.p);
+  } else {
+    if (local)
+      consumer_body<GELU_KIND, true>(p, x, sm.c);
+    else
+      consumer_body<GELU_KIND, false>(p, x, sm.c);
+  }
+}
+
+__global__ void pair_reset_kernel(unsigned* flags, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0u;
+}
+
+size_t flag_bytes(int nheads) {
+  return (static_cast<size_t>(nheads) * FLAG_WORDS * sizeof(unsigned) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+size_t fwd_pair_workspace_bytes(int nheads) {
+  return flag_bytes(nheads) + static_cast<size_t>(nheads) * RING * SLOT_BYTES;
+}
+
+int fwd_pair_blocks(int nheads) { return (nheads + 7) / 8 * 16; }
+
+// Whether the current device can hold every workgroup of the paired launch at once
+// (cooperative launch support, and resident workgroups per CU times the CU count). The
+// device answers are cached per device ordinal.
+bool fwd_pair_fits(int nheads) {
+  constexpr int kMaxDev = 64;
+  static int cap[kMaxDev];  // 0 = unknown, else 1 + resident workgroups on the device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+  if (cap[dev] == 0) {
+    int coop = 0, ncu = 0, per_cu = 0;
+    const bool ok =
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF>), NT, 0) == hipSuccess;
+    cap[dev] = 1 + ((ok && coop) ? ncu * per_cu : 0);
+  }
+  return fwd_pair_blocks(nheads) <= cap[dev] - 1;
+}
+
+hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t stream) {
+  const int nheads = p.B * p.H;
+  Pair q;
+  q.flags = reinterpret_cast<unsigned*>(p.wbuf);
+  q.ring = reinterpret_cast<char*>(p.wbuf) + flag_bytes(nheads);
+  q.nheads = nheads;
+  const int nflags = nheads * FLAG_WORDS;
+  hipLaunchKernelGGL(pair_reset_kernel, dim3((nflags + 255) / 256), dim3(256), 0, stream, q.flags, nflags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ScanParams pc = p;
+  void* args[] = {&pc, &q};
+  const void* fn = p.gelu == TTT_GELU_TANH ? reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_TANH>)
+                                           : reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF>);
+  return hipLaunchCooperativeKernel(fn, dim3(fwd_pair_blocks(nheads)), dim3(NT), args, 0, stream);
+}
+
+}  // namespace ttt

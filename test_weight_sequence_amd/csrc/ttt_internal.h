@@ -11,6 +11,7 @@
 namespace ttt {
 
 constexpr unsigned kStatusNonFinite = 1u;
+constexpr unsigned kStatusTimeout = 2u;    // a bounded wait between workgroups expired
 constexpr size_t kStatusBytes = 256;  // status word region at the start of a workspace
 constexpr int kMaxChunk = 16;
 constexpr int kThreads = 256;         // threads per workgroup of the portable kernels
@@ -88,6 +89,14 @@ hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t s);
 size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
 bool fwd_mfma_supported(const ScanParams& p);
 hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t s);
+// Two-workgroup (producer/consumer) variant of the tuned forward: its workspace region
+// (after the status word), its grid size, whether the current device can co-schedule that
+// grid, and its launcher (wbuf points at the region).
+constexpr int kPairMaxHeads = 128;
+size_t fwd_pair_workspace_bytes(int nheads);
+int fwd_pair_blocks(int nheads);
+bool fwd_pair_fits(int nheads);
+hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t s);
 // Per-head backward workspace (floats): the carried dW, then kBwdArrays [chunk x hidden]
 // intermediates (MLP only).
 constexpr int kBwdArrays = 12;

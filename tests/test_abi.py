@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 def test_abi_version_and_status_strings():
     L = ops.lib()
     assert L.ttt_abi_version() == 1
-    for code in range(10):
+    for code in range(11):
         assert L.ttt_status_str(code).decode() != "unknown status"
     assert L.ttt_status_str(99).decode() == "unknown status"
 

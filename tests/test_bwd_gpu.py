@@ -135,17 +135,17 @@ def test_bwd_cfg5_full_size_runs_and_is_finite():
         assert torch.isfinite(a).all() and torch.equal(a, b)
 
 
-@pytest.mark.parametrize("force_generic", [True, False])
-def test_saved_chunk_start_weights(force_generic):
+@pytest.mark.parametrize("variant", ["generic", "pair", "one_wg"])
+def test_saved_chunk_start_weights(variant):
     """The forward's saved buffer holds W0 at chunk 0 exactly and the carried weights at
     every later chunk start (W at chunk c equals W_T of a scan over the first c chunks)."""
     w = WORKLOADS[5]
     T = 64
     inp = make_inputs(w, batch_idx=[0, 1], head_idx=[3, 9], T=T)
     cfg = ops.Config(kind="mlp", B=2, H=2, T=T, d=w.d, hidden=w.hidden, chunk=w.chunk, io="bf16",
-                     force_generic=force_generic)
+                     force_generic=variant == "generic", one_wg_per_head=variant == "one_wg")
     d = to_dev(inp)
-    note(f"saved weights generic={force_generic}")
+    note(f"saved weights {variant} -> {ops.fwd_kernel_name(cfg)}")
     res = ops.scan_fwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["W0"], d["gamma"], d["beta"],
                        want_saved=True)
     nW1 = w.d * w.hidden

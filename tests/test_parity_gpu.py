@@ -32,12 +32,18 @@ def _check_heads(res, inp, pairs, w, tol, cfg_kw=None, B_axis=True):
     return rel_l2(gz, Z)
 
 
-def _kernels_for(w):
-    names = ["generic"]
-    cfg = ops_config(w)
-    if ops.fwd_kernel_name(cfg) != "ttt_fwd_generic":
-        names.append("tuned")
-    return names
+# forward variants: the portable kernel, the tuned kernel with a producer/consumer pair of
+# workgroups per head (the default where it applies), and the tuned kernel with one
+# workgroup per head
+KERNEL_FLAGS = {"generic": dict(force_generic=True), "pair": {}, "one_wg": dict(one_wg_per_head=True)}
+KERNEL_NAMES = {"generic": "ttt_fwd_generic", "pair": "ttt_fwd_mfma_pair_d64",
+                "one_wg": "ttt_fwd_mfma_d64"}
+
+
+def _variant_config(w, kernel, **kw):
+    cfg = ops_config(w, **kw, **KERNEL_FLAGS[kernel])
+    assert ops.fwd_kernel_name(cfg) == KERNEL_NAMES[kernel], ops.fwd_kernel_name(cfg)
+    return cfg
 
 
 def test_cfg1_mlp_fp32_full():
@@ -57,13 +63,11 @@ def test_cfg2_linear_fp32_full():
     _check_heads(res, inp, pairs, w, TOL["f32"])
 
 
-@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+@pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
 def test_cfg3_full_size_sampled_heads(kernel):
     """Full config-3 launch (B=8, H=12, T=8192); the oracle checks three heads at full T."""
     w = WORKLOADS[3]
-    cfg = ops_config(w, force_generic=(kernel == "generic"))
-    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
-        pytest.skip("no tuned kernel for this configuration")
+    cfg = _variant_config(w, kernel)
     note(f"cfg3 full {kernel} -> {ops.fwd_kernel_name(cfg)}")
     inp = make_inputs(w)
     res = _run(cfg, to_dev(inp), want_loss=True)
@@ -71,12 +75,10 @@ def test_cfg3_full_size_sampled_heads(kernel):
     _check_heads(res, inp, [(0, 0), (3, 7), (7, 11)], w, TOL["bf16"])
 
 
-@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+@pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
 def test_cfg3_all_heads_short(kernel):
     w = WORKLOADS[3]
-    cfg = ops_config(w, T=256, force_generic=(kernel == "generic"))
-    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
-        pytest.skip("no tuned kernel for this configuration")
+    cfg = _variant_config(w, kernel, T=256)
     note(f"cfg3 T=256 all heads {kernel}")
     inp = make_inputs(w, T=256)
     res = _run(cfg, to_dev(inp), want_loss=True)
@@ -115,16 +117,57 @@ def test_cfg4_full_length_two_heads_prefix():
     assert rel_l2(res["loss"][0, :, :Tp].cpu(), L) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("kernel", ["generic", "tuned"])
+@pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
 def test_cfg5_fwd_full_size_sampled_heads(kernel):
     w = WORKLOADS[5]
-    cfg = ops_config(w, force_generic=(kernel == "generic"))
-    if kernel == "tuned" and ops.fwd_kernel_name(cfg) == "ttt_fwd_generic":
-        pytest.skip("no tuned kernel for this configuration")
+    cfg = _variant_config(w, kernel)
     note(f"cfg5 fwd full {kernel}")
     inp = make_inputs(w)
     res = _run(cfg, to_dev(inp))
     _check_heads(res, inp, [(1, 2), (3, 15)], w, TOL["bf16"])
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 5, 128), (2, 3, 16), (3, 1, 48)])
+def test_pair_partial_groups_all_heads(B, H, T):
+    """Head counts that leave part of the last group of 8 pairs empty, single-chunk and
+    few-chunk scans (fewer chunks than ring slots): every head against the oracle."""
+    w = WORKLOADS[3]
+    cfg = _variant_config(w, "pair", B=B, H=H, T=T)
+    note(f"pair partial groups B={B} H={H} T={T}")
+    inp = make_inputs(w, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    _check_heads(res, inp, [(b, h) for b in range(B) for h in range(H)], w, TOL["bf16"])
+
+
+def test_pair_not_used_above_128_heads():
+    """More than 128 (batch, head) pairs: the host picks one workgroup per head."""
+    w = WORKLOADS[3]
+    cfg = ops_config(w, B=9, H=16, T=64)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_d64"
+    note("144 heads T=64")
+    inp = make_inputs(w, batch_idx=list(range(9)), head_idx=list(range(16)), T=64)
+    res = _run(cfg, to_dev(inp))
+    _check_heads(res, inp, [(0, 0), (4, 9), (8, 15)], w, TOL["bf16"])
+
+
+def test_pair_tanh_per_seq():
+    """The paired kernel with tanh GELU and per-sequence W0, all heads."""
+    B, H, T = 2, 3, 160
+    inp = _rand_case("mlp", B, H, T, 64, 16, "bf16", seed=11, per_seq=True)
+    cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io="bf16",
+                     gelu="tanh", w0_per_seq=True, eta_scale=0.5)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_pair_d64"
+    note("pair tanh per-seq")
+    res = _run(cfg, to_dev(inp))
+    flat, ocfg = _oracle_all(inp, "mlp", 16, per_seq=True, gelu="tanh", eta_scale=0.5)
+    from oracle import scan as oracle_scan
+    Z, WT, _ = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
+                           flat["gamma"], flat["beta"], ocfg)
+    assert rel_l2(res["Z"].reshape(B * H, T, 64), Z) <= TOL["bf16"]
+    for g, o in zip(res["W_T"], WT):
+        assert rel_l2(g.reshape(o.shape), o) <= TOL["bf16"]
 
 
 def _rand_case(kind, B, H, T, d, chunk, io, seed, per_seq=False):
