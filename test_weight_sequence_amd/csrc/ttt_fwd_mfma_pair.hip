@@ -295,10 +295,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   const float* gam = hst.gam;
   const float* bet = hst.bet;
   const Ident& id = hst.id;
-  for (int i = tid; i < D * 4; i += NT) {
-    zp_clear(S.E2z, i);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) zp_clear(S.Ktz[s4], i);
+  // all padded [d][token] arrays start at zero: their zero halves stay zero, and the
+  // update applied at chunk 0 (from the zero carry of "chunk -1") reads finite values
+  {
+    uint4* z4 = reinterpret_cast<uint4*>(&S.Ktz[0]);
+    for (int i = tid; i < 4 * static_cast<int>(sizeof(ZPad2)) / 16; i += NT) z4[i] = uint4{0u, 0u, 0u, 0u};
+    uint4* e4 = reinterpret_cast<uint4*>(&S.E2z);
+    for (int i = tid; i < static_cast<int>(sizeof(ZPad2)) / 16; i += NT) e4[i] = uint4{0u, 0u, 0u, 0u};
   }
   if (tid < 8) S.zeros[tid] = (__bf16)0.f;
   // staging by waves 4..7: thread -> (token, 4 consecutive d). Every wave issues exactly
@@ -354,7 +357,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     hk[0] = mfma32(cat(in.sA, zz), in.e1, in.P[0]);
     hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
     // the update of chunk c - 1 (W(c) = W(c-1) + ...), next to the GELU work
-    if (c > 0) chunk_update(W1c, W2c, S.Ktz[(c - 1) & 3], S.E2z, in.e1, in.ak, g, c16);
+    // (at chunk 0 the carry is zero and the operands are zero-filled: an exact no-op)
+    chunk_update(W1c, W2c, S.Ktz[(c - 1) & 3], S.E2z, in.e1, in.ak, g, c16);
     // A^K (R layout: m = h, k = token), G
     bf16x4 akR[NHT];
     f4 gk[NHT];
@@ -375,8 +379,9 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     bf16x4 W1b[NDT][NHT];
     bf16x8 W2b8[NDT];
     cvt_w(W1c, W2c, W1b, W2b8);
-    // look-ahead for chunk c + 1: K(c+1) W1(c) and K(c+1) K(c)^T
-    if (c + 1 < nchunks) {
+    // look-ahead for chunk c + 1: K(c+1) W1(c) and K(c+1) K(c)^T (after the last chunk the
+    // slot holds other data and the result is not used)
+    {
       bf16x8 aK[2], aK1[2];
       rows(st.K, g, c16, aK);
       rows(S.st[(c + 1) & 3].K, g, c16, aK1);

@@ -137,7 +137,7 @@ __device__ __forceinline__ LnStats ln_stats(const float z[4], float eps) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) var += (z[i] - mu) * (z[i] - mu);
   var = sum16(var) * (1.0f / D);
-  return LnStats{mu, 1.0f / sqrtf(var + eps)};
+  return LnStats{mu, __builtin_amdgcn_rsqf(var + eps)};  // v_rsq_f32, 1 ulp
 }
 
 // One wave's fp32 weight tiles: W1[:, hs:hs+32] as [d tile][h tile] and W2[hs:hs+32, :] as
