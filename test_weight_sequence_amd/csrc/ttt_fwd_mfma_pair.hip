@@ -20,9 +20,9 @@
 // chunk c + 1, next to the GELU work, where it is off the chain. (The same identity is the
 // dual form's own: the look-ahead term is the next chunk's first dual-form correction.)
 //
-// Hand-off: a ring of RING chunk slots per head in the workspace, per-wave counters
-// ready[w] (chunks published by producer wave w) and one counter of chunks the consumer
-// workgroup is done reading. A producer wave waits for its slot stores to complete (s_waitcnt vmcnt)
+// Hand-off: a ring of RING chunk slots per head in the workspace, and per-wave counters
+// (ready[w] = chunks published by producer wave w, consumed[w] = chunks consumer wave w is
+// done reading). A producer wave waits for its slot stores to complete (s_waitcnt vmcnt)
 // before it raises its counter, and a consumer wave issues its slot loads only after it has
 // seen the counter. Workgroups b and b + 8 of each group of 16 form a pair; workgroups are
 // dealt to the 8 XCDs round-robin, so both normally sit on one XCD. Each side reads its XCD
@@ -52,7 +52,7 @@ constexpr int SLOT_E1 = 0;
 constexpr int SLOT_AK = NW * 64 * 16;
 constexpr int SLOT_E2 = 2 * NW * 64 * 16;
 constexpr int SLOT_BYTES = SLOT_E2 + 64 * 32;
-constexpr int FLAG_WORDS = 32;         // per head: ready[0..7], consumed[16], XCD ids
+constexpr int FLAG_WORDS = 32;         // per head: ready[0..7], consumed[16..23], XCD ids
 constexpr int FLAG_XCC = 24;           // producer's and consumer's XCD id + 1 (words 24, 25)
 constexpr int kSpinLimit = 1 << 20;
 static_assert(NHT == 2, "layout assumes 8 waves of 32 hidden units");
@@ -100,17 +100,15 @@ struct PStage {
 struct ProdSmem {
   PStage st[4];   // chunk j in slot j & 3
   ZPad2 Ktz[4];
-  f4 red[NW][4][64];  // Z^K partial of wave w: [r][lane] -> the 4 d tiles of C[4(lane/16)+r][lane%16]
+  float red[NW][NDT][4][PS];
   alignas(16) __bf16 E2[BC * RS];  // En2 [token][d]
   ZPad2 E2z;           // En2 zero-padded [d][token]
   alignas(16) __bf16 zeros[8];
-  bf16x8 ilo[64], ihi[64];  // per-lane identity operands (kept here, not in registers)
-  f4 gb[16][2];             // LayerNorm gamma, beta: [d % 16][gamma|beta][d / 16]
 };
 struct ConsSmem {
   PStage st[3];   // chunk j in slot j % 3
   ZPad2 Ktz[3];
-  f4 red[2][NW][4][64];  // Z^Q partials, double-buffered, layout as in ProdSmem::red
+  float red[2][NW][NDT][4][PS];
   alignas(16) __bf16 zeros[8];
 };
 union SmemP {
@@ -206,11 +204,26 @@ __device__ __forceinline__ unsigned slot_dep(const Slot& s) {
   return static_cast<unsigned>(x) ^ static_cast<unsigned>(x >> 32);
 }
 
-// What the producer carries into chunk c: A^K(c) (k = token, two h tiles) and G(c).
+// What the producer carries from chunk c - 1 into chunk c.
 struct Carry {
-  bf16x8 ak;
-  f4 gk[NHT];
+  f4 P[NHT];       // K(c) W1(c-1) for this wave's h tiles
+  bf16x4 sA;       // K(c) K(c-1)^T as an A operand (m = token of c, k = token of c-1)
+  bf16x8 e1, ak;   // E1n(c-1), A^K(c-1): k = token (two h tiles)
 };
+
+// The 16 MFMAs of a chunk-end update: W1 += K^T E1n, W2 += A^K^T En2 (K = 16 over the
+// chunk's tokens, operands padded by the zero halves of the [d][token] arrays).
+__device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const ZPad2& Kt,
+                                             const ZPad2& E2t, bf16x8 e1, bf16x8 ak, int g, int c16) {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int d = 16 * dt + c16;
+    W1c[dt][0] = mfma32(zp_lo(Kt, d, g), e1, W1c[dt][0]);
+    W1c[dt][1] = mfma32(zp_hi(Kt, d, g), e1, W1c[dt][1]);
+    W2c[0][dt] = mfma32(ak, zp_lo(E2t, d, g), W2c[0][dt]);
+    W2c[1][dt] = mfma32(ak, zp_hi(E2t, d, g), W2c[1][dt]);
+  }
+}
 
 // Operands of a staged [token][d] chunk: rows (token = lane%16), permuted d order.
 __device__ __forceinline__ void rows(const __bf16* X, int g, int c16, bf16x8 (&a)[2]) {
@@ -279,21 +292,18 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   head_init(p, x, hst);
   auto& W1c = hst.W1c;
   auto& W2c = hst.W2c;
+  const float* gam = hst.gam;
+  const float* bet = hst.bet;
+  const Ident& id = hst.id;
+  // all padded [d][token] arrays start at zero: their zero halves stay zero, and the
+  // update applied at chunk 0 (from the zero carry of "chunk -1") reads finite values
+  {
+    uint4* z4 = reinterpret_cast<uint4*>(&S.Ktz[0]);
+    for (int i = tid; i < 4 * static_cast<int>(sizeof(ZPad2)) / 16; i += NT) z4[i] = uint4{0u, 0u, 0u, 0u};
+    uint4* e4 = reinterpret_cast<uint4*>(&S.E2z);
+    for (int i = tid; i < static_cast<int>(sizeof(ZPad2)) / 16; i += NT) e4[i] = uint4{0u, 0u, 0u, 0u};
+  }
   if (tid < 8) S.zeros[tid] = (__bf16)0.f;
-  if (tid < 64) {
-    const Ident id = make_ident(g, c16);
-    S.ilo[tid] = id.ilo;
-    S.ihi[tid] = id.ihi;
-  }
-  if (tid < D) {
-    S.gb[tid & 15][0][tid >> 4] = p.gamma[x.hidx * D + tid];
-    S.gb[tid & 15][1][tid >> 4] = p.beta[x.hidx * D + tid];
-  }
-  for (int i = tid; i < D * 4; i += NT) {
-    zp_clear(S.E2z, i);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) zp_clear(S.Ktz[s4], i);
-  }
   // staging by waves 4..7: thread -> (token, 4 consecutive d). Every wave issues exactly
   // three loads (K, V, eta) per chunk (waves 0..3 load the same addresses as waves 4..7 and
   // drop the data), so the count of memory operations after the slot stores is fixed.
@@ -325,10 +335,33 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     if (nchunks > 1) stage_write(1, gload(1));
   }
   __syncthreads();
+  const bf16x4 zz = lds4(S.zeros);
 
-  // A^K (R layout: m = h, k = token) and G = GELU' from H^K
-  auto activate = [&](const f4 (&hk)[NHT], Carry& out) {
+  // chunk 0 enters with P = K(0) W0, and zero look-ahead terms
+  Carry ca{}, cb{};
+  {
+    bf16x4 W1b[NDT][NHT];
+    bf16x8 W2b8[NDT];
+    cvt_w(W1c, W2c, W1b, W2b8);
+    bf16x8 aK[2];
+    rows(S.st[0].K, g, c16, aK);
+    xw1(aK, W1b, ca.P);
+  }
+
+  auto step = [&](const int c, const Carry& in, Carry& out) {
+    const PStage& st = S.st[c & 3];
+    const int t0 = c * BC;
+    const Ld ld = gload(min(c + 2, nchunks - 1));
+    // H^K(c) = K(c) W1(c-1) + (K(c) K(c-1)^T) E1n(c-1)
+    f4 hk[NHT];
+    hk[0] = mfma32(cat(in.sA, zz), in.e1, in.P[0]);
+    hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
+    // the update of chunk c - 1 (W(c) = W(c-1) + ...), next to the GELU work
+    // (at chunk 0 the carry is zero and the operands are zero-filled: an exact no-op)
+    chunk_update(W1c, W2c, S.Ktz[(c - 1) & 3], S.E2z, in.e1, in.ak, g, c16);
+    // A^K (R layout: m = h, k = token), G
     bf16x4 akR[NHT];
+    f4 gk[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       f4 a, gd;
@@ -339,65 +372,39 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         a[r] = v;
         gd[r] = d1;
       }
-      out.gk[ht] = gd;
+      gk[ht] = gd;
       akR[ht] = cvt4(a);
     }
     out.ak = cat(akR[0], akR[1]);
-  };
-  // chunk 0: H^K = K(0) W0
-  Carry ca, cb;
-  {
-    bf16x4 W1b[NDT][NHT];
-    bf16x8 W2b8[NDT];
-    cvt_w(W1c, W2c, W1b, W2b8);
-    bf16x8 aK[2];
-    rows(S.st[0].K, g, c16, aK);
-    f4 hk[NHT];
-    xw1(aK, W1b, hk);
-    activate(hk, ca);
-  }
-
-  // One chunk. Enters with A^K(c), G(c) (in) and W(c); leaves with A^K(c+1), G(c+1) (out)
-  // and W(c+1): the tail computes H^K(c+1) = K(c+1) W1(c) + (K(c+1) K(c)^T) E1n(c) and runs
-  // the GELU of chunk c+1 next to the MFMAs of chunk c's weight update.
-  auto step = [&](const int c, const Carry& in, Carry& out) {
-    const PStage& st = S.st[c & 3];
-    const int t0 = c * BC;
-    const Ld ld = gload(min(c + 2, nchunks - 1));
     bf16x4 W1b[NDT][NHT];
     bf16x8 W2b8[NDT];
     cvt_w(W1c, W2c, W1b, W2b8);
     // look-ahead for chunk c + 1: K(c+1) W1(c) and K(c+1) K(c)^T (after the last chunk the
     // slot holds other data and the result is not used)
-    f4 P[NHT];
-    bf16x4 sA;
     {
       bf16x8 aK[2], aK1[2];
       rows(st.K, g, c16, aK);
       rows(S.st[(c + 1) & 3].K, g, c16, aK1);
-      xw1(aK1, W1b, P);
+      xw1(aK1, W1b, out.P);
       f4 sT = mfma32(aK[0], aK1[0], zero4());  // C[t][t'] = K(c)_t . K(c+1)_t'
       sT = mfma32(aK[1], aK1[1], sT);
-      sA = cvt4(sT);
+      out.sA = cvt4(sT);
     }
     // Z^K partial over this wave's h slice
-    const bf16x8 ilo = S.ilo[lane], ihi = S.ihi[lane];
-    const bf16x8 akT8 = cat(cvt4(mfma32(in.ak, ilo, zero4())), cvt4(mfma32(in.ak, ihi, zero4())));
-    {
-      f4 acc[NDT];
+    const bf16x8 akT8 = cat(cvt4(mfma32(out.ak, id.ilo, zero4())), cvt4(mfma32(out.ak, id.ihi, zero4())));
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma32(akT8, W2b8[dt], zero4());
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f4 acc = mfma32(akT8, W2b8[dt], zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S.red[w][r][lane] = f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      for (int r = 0; r < 4; ++r) S.red[w][dt][r][lane] = acc[r];
     }
     // W2(c)^T tiles for E1n: waves 0..3 now, waves 4..7 during the LayerNorm
     bf16x4 W2Tb[NDT][NHT];
     auto w2t = [&]() {
-      const bf16x8 jlo = S.ilo[lane], jhi = S.ihi[lane];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        W2Tb[dt][0] = cvt4(mfma32(W2b8[dt], jlo, zero4()));
-        W2Tb[dt][1] = cvt4(mfma32(W2b8[dt], jhi, zero4()));
+        W2Tb[dt][0] = cvt4(mfma32(W2b8[dt], id.ilo, zero4()));
+        W2Tb[dt][1] = cvt4(mfma32(W2b8[dt], id.ihi, zero4()));
       }
     };
     if (w < 4) w2t();
@@ -408,8 +415,11 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       if (lane == 0) ho.st(w, static_cast<unsigned>(c));
       compiler_fence();
     }
-    // chunks the consumer is done reading (checked after the barriers)
-    const unsigned cons = ho.ld(16);
+    // consumed counters for this chunk's slot (own consumer wave; wave 0 also writes the
+    // En2 part that every consumer wave reads), reduced after the barriers
+    unsigned cv[NW];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) cv[ww] = ho.ld(16 + ww);
     if (p.saved) {
       float* sv = p.saved + (static_cast<size_t>(head) * nchunks + c) * (2 * D * HID);
       wtiles_store(sv, sv + D * HID, g, c16, hs, W1c, W2c);
@@ -419,21 +429,23 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     if (w < 4) {
       // LayerNorm forward/backward of Z^K: token 4w + lane/16, 16 lanes each
       const int t = 4 * w + g;
-      f4 zs = S.red[0][t & 3][16 * (t >> 2) + c16];
+      float z[NDT];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) zs += S.red[ww][t & 3][16 * (t >> 2) + c16];
-      const float z[NDT] = {zs[0], zs[1], zs[2], zs[3]};
-      const f4 gav = S.gb[c16][0], bev = S.gb[c16][1];
+      for (int i = 0; i < NDT; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += S.red[ww][i][t & 3][16 * (t >> 2) + c16];
+        z[i] = s;
+      }
       const LnStats ls = ln_stats(z, p.eps);
       float xh[NDT], gg[NDT], l2 = 0.f, sg = 0.f, sgx = 0.f;
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
         const int d = 16 * i + c16;
         xh[i] = (z[i] - ls.mu) * ls.rs;
-        const float ga = gav[i];
-        const float r = bf(st.K[t * RS + d]) + ga * xh[i] + bev[i] - bf(st.X[t * RS + d]);
+        const float r = bf(st.K[t * RS + d]) + gam[i] * xh[i] + bet[i] - bf(st.X[t * RS + d]);
         l2 += r * r;
-        gg[i] = 2.f * r * ga;
+        gg[i] = 2.f * r * gam[i];
         sg += gg[i];
         sgx += gg[i] * xh[i];
       }
@@ -457,16 +469,6 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     }
     __syncthreads();
 
-    // operands of this chunk's weight update, read early
-    bf16x8 kl[NDT], kh[NDT], el[NDT], eh[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + c16;
-      kl[dt] = zp_lo(S.Ktz[c & 3], d, g);
-      kh[dt] = zp_hi(S.Ktz[c & 3], d, g);
-      el[dt] = zp_lo(S.E2z, d, g);
-      eh[dt] = zp_hi(S.E2z, d, g);
-    }
     // E1n(c) = (En2 W2^T) (.) G
     bf16x8 aE[2];
     rows(S.E2, g, c16, aE);
@@ -476,36 +478,29 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       f4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) acc = mfma32(aE[ks], cat(W2Tb[2 * ks][ht], W2Tb[2 * ks + 1][ht]), acc);
-      e1[ht] = cvt4(acc * in.gk[ht]);
+      e1[ht] = cvt4(acc * gk[ht]);
     }
-    const bf16x8 e18 = cat(e1[0], e1[1]);
+    out.e1 = cat(e1[0], e1[1]);
 
     // hand chunk c to the consumer: slot c % RING must have been read (chunk c - RING)
     const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
-    if (cons < need) spin_geq(ho, 16, need, p.status);
+    unsigned cons = ~0u;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) cons = (w == 0 || ww == w) ? min(cons, cv[ww]) : cons;
+    if (cons < need) {
+      spin_geq(ho, 16 + w, need, p.status);
+      if (w == 0)
+        for (int ww = 1; ww < NW; ++ww) spin_geq(ho, 16 + ww, need, p.status);
+    }
     compiler_fence();
     const int base = (c % RING) * SLOT_BYTES;
-    ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, e18);
-    ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, in.ak);
+    ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
+    ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
     if (w == 0) {
-      ho.st16(base + SLOT_E2 + lane * 32, cat(hi4(eh[0]), hi4(eh[1])));
-      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(hi4(eh[2]), hi4(eh[3])));
+      ho.st16(base + SLOT_E2 + lane * 32, cat(zp_data(S.E2z, c16, g), zp_data(S.E2z, 16 + c16, g)));
+      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(zp_data(S.E2z, 32 + c16, g), zp_data(S.E2z, 48 + c16, g)));
     }
     compiler_fence();
-
-    // H^K(c+1), then the update of chunk c next to the GELU of chunk c+1
-    const bf16x4 zz = lds4(S.zeros);
-    f4 hk[NHT];
-    hk[0] = mfma32(cat(sA, zz), e18, P[0]);
-    hk[1] = mfma32(cat(zz, sA), e18, P[1]);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      W1c[dt][0] = mfma32(kl[dt], e18, W1c[dt][0]);
-      W1c[dt][1] = mfma32(kh[dt], e18, W1c[dt][1]);
-      W2c[0][dt] = mfma32(in.ak, el[dt], W2c[0][dt]);
-      W2c[1][dt] = mfma32(in.ak, eh[dt], W2c[1][dt]);
-    }
-    activate(hk, out);
   };
 
   // two chunks per trip, so the carried registers alternate without copies
@@ -515,11 +510,15 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     step(c + 1, cb, ca);
   }
   if (c < nchunks) step(c, ca, cb);
+  const Carry& last = (nchunks & 1) ? cb : ca;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (lane == 0) ho.st(w, static_cast<unsigned>(nchunks));
+  // the last chunk's update (its En2 is still in E2z)
+  chunk_update(W1c, W2c, S.Ktz[(nchunks - 1) & 3], S.E2z, last.e1, last.ak, g, c16);
   if (p.wt_1)
     wtiles_store(p.wt_1 + static_cast<size_t>(head) * D * HID, p.wt_2 + static_cast<size_t>(head) * HID * D,
                  g, c16, hs, W1c, W2c);
+  return;
 }
 
 template <int GELU_KIND, bool LOCAL>
@@ -569,10 +568,14 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
   auto ln_out = [&](int cc) {
     const PStage& So = S.st[cc % 3];
     const int t = 4 * w + g;
-    f4 zs = S.red[cc & 1][0][t & 3][16 * (t >> 2) + c16];
+    float z[NDT];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) zs += S.red[cc & 1][ww][t & 3][16 * (t >> 2) + c16];
-    const float z[NDT] = {zs[0], zs[1], zs[2], zs[3]};
+    for (int i = 0; i < NDT; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) s += S.red[cc & 1][ww][i][t & 3][16 * (t >> 2) + c16];
+      z[i] = s;
+    }
     const LnStats ls = ln_stats(z, p.eps);
     float chk = 0.f;
 #pragma unroll
@@ -629,15 +632,12 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
 #pragma unroll
     for (int r = 0; r < 4; ++r) s2m[r] = (4 * g + r) <= c16 ? s2t[r] : 0.f;
     const bf16x8 s2a8 = cat(cvt4(s2m), zz);
-    {
-      f4 acc[NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        acc[dt] = mfma32(aqT8, W2b8[dt], zero4());
-        acc[dt] = mfma32(s2a8, cat(slot_e2(cur, dt), zz), acc[dt]);
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      f4 acc = mfma32(aqT8, W2b8[dt], zero4());
+      acc = mfma32(s2a8, cat(slot_e2(cur, dt), zz), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S.red[c & 1][w][r][lane] = f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      for (int r = 0; r < 4; ++r) S.red[c & 1][w][dt][r][lane] = acc[r];
     }
     // the producer's chunk-end update, from the same operands
 #pragma unroll
@@ -648,11 +648,12 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);
       W2c[1][dt] = mfma32(cur.ak, cat(zz, slot_e2(cur, dt)), W2c[1][dt]);
     }
-    // this wave is done with slot c (its loads have returned: the dependency forces the
-    // wait); wave 0 releases the slot after the barrier. Then prefetch chunk c + 1.
+    // release slot c (its loads have returned: the dependency forces the wait), then
+    // prefetch chunk c + 1
     {
       const unsigned dep = slot_dep(cur);
       asm volatile("" ::"v"(dep) : "memory");
+      if (lane == 0) ho.st(16 + w, static_cast<unsigned>(c + 1));
       compiler_fence();
     }
     if (has_next) {
@@ -666,7 +667,6 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       stage_write((c + 1) % 3, ld);
     }
     __syncthreads();
-    if (w == 0 && lane == 0) ho.st(16, static_cast<unsigned>(c + 1));
     if (w < 4) ln_out(c);
   };
 
