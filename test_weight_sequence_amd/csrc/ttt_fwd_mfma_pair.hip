@@ -215,13 +215,21 @@ struct Carry {
 // chunk's tokens, operands padded by the zero halves of the [d][token] arrays).
 __device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const ZPad2& Kt,
                                              const ZPad2& E2t, bf16x8 e1, bf16x8 ak, int g, int c16) {
+  bf16x8 kl[NDT], kh[NDT], el[NDT], eh[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     const int d = 16 * dt + c16;
-    W1c[dt][0] = mfma32(zp_lo(Kt, d, g), e1, W1c[dt][0]);
-    W1c[dt][1] = mfma32(zp_hi(Kt, d, g), e1, W1c[dt][1]);
-    W2c[0][dt] = mfma32(ak, zp_lo(E2t, d, g), W2c[0][dt]);
-    W2c[1][dt] = mfma32(ak, zp_hi(E2t, d, g), W2c[1][dt]);
+    kl[dt] = zp_lo(Kt, d, g);
+    kh[dt] = zp_hi(Kt, d, g);
+    el[dt] = zp_lo(E2t, d, g);
+    eh[dt] = zp_hi(E2t, d, g);
+  }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    W1c[dt][0] = mfma32(kl[dt], e1, W1c[dt][0]);
+    W1c[dt][1] = mfma32(kh[dt], e1, W1c[dt][1]);
+    W2c[0][dt] = mfma32(ak, el[dt], W2c[0][dt]);
+    W2c[1][dt] = mfma32(ak, eh[dt], W2c[1][dt]);
   }
 }
 
@@ -376,6 +384,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       akR[ht] = cvt4(a);
     }
     out.ak = cat(akR[0], akR[1]);
+    // scheduling hint: issue the 16 update MFMAs one at a time between runs of 8 VALU
+    // instructions of the GELU above, so the matrix unit works while the VALU does
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
     bf16x4 W1b[NDT][NHT];
     bf16x8 W2b8[NDT];
     cvt_w(W1c, W2c, W1b, W2b8);
@@ -407,7 +422,19 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         W2Tb[dt][1] = cvt4(mfma32(W2b8[dt], id.ihi, zero4()));
       }
     };
-    if (w < 4) w2t();
+    // LayerNorm inputs that do not depend on Z^K, prepared by the LayerNorm waves ahead of
+    // the barrier: K + beta - V and -eta for token 4w + lane/16
+    float kvb[NDT] = {0.f, 0.f, 0.f, 0.f}, neta = 0.f;
+    if (w < 4) {
+      w2t();
+      const int t = 4 * w + g;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int d = 16 * i + c16;
+        kvb[i] = bf(st.K[t * RS + d]) + bet[i] - bf(st.X[t * RS + d]);
+      }
+      neta = -st.eta[t];
+    }
     // publish chunk c - 1: its slot stores were the last vector-memory operations before
     // this chunk's three input loads
     if (c > 0) {
@@ -443,7 +470,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       for (int i = 0; i < NDT; ++i) {
         const int d = 16 * i + c16;
         xh[i] = (z[i] - ls.mu) * ls.rs;
-        const float r = bf(st.K[t * RS + d]) + gam[i] * xh[i] + bet[i] - bf(st.X[t * RS + d]);
+        const float r = kvb[i] + gam[i] * xh[i];
         l2 += r * r;
         gg[i] = 2.f * r * gam[i];
         sg += gg[i];
@@ -451,7 +478,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       }
       const float loss = sum16(l2);
       const float mg = sum16(sg) * (1.0f / D), mgx = sum16(sgx) * (1.0f / D);
-      const float ne2 = -st.eta[t] * ls.rs;
+      const float ne2 = neta * ls.rs;
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
         const int d = 16 * i + c16;
