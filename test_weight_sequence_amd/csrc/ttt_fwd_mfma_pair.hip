@@ -20,9 +20,10 @@
 // chunk c + 1, next to the GELU work, where it is off the chain. (The same identity is the
 // dual form's own: the look-ahead term is the next chunk's first dual-form correction.)
 //
-// Hand-off: a ring of RING chunk slots per head in the workspace, and per-wave counters
-// (ready[w] = chunks published by producer wave w, consumed[w] = chunks consumer wave w is
-// done reading). A producer wave waits for its slot stores to complete (s_waitcnt vmcnt)
+// Hand-off: a ring of RING chunk slots per head in the workspace, per-wave counters
+// ready[w] (chunks published by producer wave w) and one counter of chunks the consumer
+// workgroup is done reading (raised by its wave 0 after the barrier that follows the slot
+// loads of every wave). A producer wave waits for its slot stores to complete (s_waitcnt vmcnt)
 // before it raises its counter, and a consumer wave issues its slot loads only after it has
 // seen the counter. Workgroups b and b + 8 of each group of 16 form a pair; workgroups are
 // dealt to the 8 XCDs round-robin, so both normally sit on one XCD. Each side reads its XCD
@@ -52,7 +53,7 @@ constexpr int SLOT_E1 = 0;
 constexpr int SLOT_AK = NW * 64 * 16;
 constexpr int SLOT_E2 = 2 * NW * 64 * 16;
 constexpr int SLOT_BYTES = SLOT_E2 + 64 * 32;
-constexpr int FLAG_WORDS = 32;         // per head: ready[0..7], consumed[16..23], XCD ids
+constexpr int FLAG_WORDS = 32;         // per head: ready[0..7], consumed[16], XCD ids
 constexpr int FLAG_XCC = 24;           // producer's and consumer's XCD id + 1 (words 24, 25)
 constexpr int kSpinLimit = 1 << 20;
 static_assert(NHT == 2, "layout assumes 8 waves of 32 hidden units");
@@ -442,11 +443,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       if (lane == 0) ho.st(w, static_cast<unsigned>(c));
       compiler_fence();
     }
-    // consumed counters for this chunk's slot (own consumer wave; wave 0 also writes the
-    // En2 part that every consumer wave reads), reduced after the barriers
-    unsigned cv[NW];
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) cv[ww] = ho.ld(16 + ww);
+    // chunks the consumer is done reading (checked after the barriers)
+    const unsigned cons = ho.ld(16);
     if (p.saved) {
       float* sv = p.saved + (static_cast<size_t>(head) * nchunks + c) * (2 * D * HID);
       wtiles_store(sv, sv + D * HID, g, c16, hs, W1c, W2c);
@@ -511,14 +509,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
 
     // hand chunk c to the consumer: slot c % RING must have been read (chunk c - RING)
     const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
-    unsigned cons = ~0u;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) cons = (w == 0 || ww == w) ? min(cons, cv[ww]) : cons;
-    if (cons < need) {
-      spin_geq(ho, 16 + w, need, p.status);
-      if (w == 0)
-        for (int ww = 1; ww < NW; ++ww) spin_geq(ho, 16 + ww, need, p.status);
-    }
+    if (cons < need) spin_geq(ho, 16, need, p.status);
     compiler_fence();
     const int base = (c % RING) * SLOT_BYTES;
     ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
@@ -675,12 +666,11 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);
       W2c[1][dt] = mfma32(cur.ak, cat(zz, slot_e2(cur, dt)), W2c[1][dt]);
     }
-    // release slot c (its loads have returned: the dependency forces the wait), then
-    // prefetch chunk c + 1
+    // this wave is done with slot c (its loads have returned: the dependency forces the
+    // wait); wave 0 releases the slot after the barrier below. Then prefetch chunk c + 1.
     {
       const unsigned dep = slot_dep(cur);
       asm volatile("" ::"v"(dep) : "memory");
-      if (lane == 0) ho.st(16 + w, static_cast<unsigned>(c + 1));
       compiler_fence();
     }
     if (has_next) {
@@ -694,6 +684,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       stage_write((c + 1) % 3, ld);
     }
     __syncthreads();
+    if (w == 0 && lane == 0) ho.st(16, static_cast<unsigned>(c + 1));
     if (w < 4) ln_out(c);
   };
 
