@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-T", type=int, default=8192)
     ap.add_argument("--force-generic", action="store_true")
     ap.add_argument("--one-wg", action="store_true",
