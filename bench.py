@@ -24,7 +24,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3
-WORKLOAD_ID = 3
 
 
 def flops_per_token_head(d: int, h: int, b: int) -> int:
@@ -65,30 +64,260 @@ def _traffic(kernel: str, n_launch_units: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_seq: int, T: int) -> dict:
-    """The fp64 oracle on the first n_seq sequences (all H heads each), first T tokens."""
+def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool = False) -> dict:
+    """The fp64 oracle on the first n_seq sequences (the first n_heads heads of each, default
+    all), first T tokens; with grads, the oracle's outer-loop gradients (autograd through
+    its primal scan) instead of the forward."""
     import torch
-    from oracle import OracleConfig, scan
+    from oracle import OracleConfig, scan, scan_outer_grads
     from test_weight_sequence_amd.synth import flatten_heads, make_inputs
     torch.set_num_threads(max(1, torch.get_num_threads()))
     cores = torch.get_num_threads()
-    inp = flatten_heads(make_inputs(w, batch_idx=list(range(n_seq)), head_idx=list(range(w.H)), T=T))
-    n_heads = n_seq * w.H
+    nh = w.H if n_heads is None else n_heads
+    inp = flatten_heads(make_inputs(w, batch_idx=list(range(n_seq)), head_idx=list(range(nh)),
+                                    T=T, with_dz=grads))
+    pairs = n_seq * nh
     cfg = OracleConfig(kind=w.kind, chunk=w.chunk)
     t0 = time.perf_counter()
-    scan(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"], inp["beta"], cfg)
+    if grads:
+        scan_outer_grads(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"],
+                         inp["beta"], cfg, inp["dZ"].double())
+    else:
+        scan(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"], inp["beta"], cfg)
     dt = time.perf_counter() - t0
-    return {"value": n_heads * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 oracle on sequences 0..{n_seq - 1} (all {w.H} heads, {n_heads} "
-                      f"(batch, head) pairs) x first T={T} tokens of the same workload "
+    what = "outer-loop gradients (autograd through the primal scan)" if grads else "forward scan"
+    return {"value": pairs * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle {what} on sequences 0..{n_seq - 1} x heads 0..{nh - 1} "
+                      f"({pairs} (batch, head) pairs) x first T={T} tokens of the same workload "
                       f"({dt:.1f} s wall, torch intra-op threads={cores})"}
+
+
+def _time_calls(call, steps: int, warmup: int, calls_per_step: int = 1):
+    """Run `warmup` untimed steps, then `steps` timed steps of `calls_per_step` library calls
+    each. Every call is bracketed by hipEvents on the launch stream (torch's current stream,
+    which is the stream handed to the library). Returns (wall ms per step, per-call ms list)."""
+    import torch
+    from test_weight_sequence_amd import ops
+    for i in range(warmup * calls_per_step):
+        rc = call(i % calls_per_step)
+        if rc != 0:
+            raise ops.TTTError(rc, "warm-up call")
+    torch.cuda.synchronize()
+    n = steps * calls_per_step
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        starts[i].record()
+        call(i % calls_per_step)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+DATA = "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) W0, eta=0.1*sigmoid(N(0,1)))"
+
+
+def _base_record(args, metric, value, ms_step, w, kernel, dtype, extra_cfg=None):
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "hidden": w.hidden,
+           "chunk": w.chunk, "io": w.io, "state": "fp32", "kernel": kernel}
+    cfg.update(extra_cfg or {})
+    return {"metric": metric, "value": value, "unit": "token*heads/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": DATA + (" (AR(1) drift 0.999 along tokens)" if w.drift > 0 else ""),
+            "config": cfg}
+
+
+def _device_inputs(w, dev, with_dz=False):
+    from test_weight_sequence_amd.synth import make_inputs
+    inp = make_inputs(w, with_dz=with_dz)
+    return {k: (tuple(x.to(dev) for x in v) if isinstance(v, tuple) else v.to(dev))
+            for k, v in inp.items()}
+
+
+def bench_scan_fwd(args, wid: int) -> dict:
+    """One step = one ttt_scan_fwd over the whole batch."""
+    import ctypes
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS
+    w = WORKLOADS[wid]
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
+                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
+    kernel = ops.fwd_kernel_name(cfg)
+    dev = torch.device("cuda:0")
+    d = _device_inputs(w, dev)
+    ws = ops.new_workspace(cfg, ops.TTT_OP_FWD, dev)
+    Z = torch.empty(w.B, w.H, w.T, w.d, dtype=cfg.io_dtype, device=dev)
+    WT = tuple(torch.empty(s, device=dev) for s in cfg.weight_shapes((w.B, w.H)))
+    # arguments are marshalled once, outside the timed region
+    cfg_struct = cfg.c()
+    cfg_c = ctypes.byref(cfg_struct)
+    P = ctypes.c_void_p
+    ptrs = [P(d[k].data_ptr()) for k in ("Q", "K", "V", "eta", "gamma", "beta")]
+    ptrs.append(ctypes.byref(ops.CWeights(d["W0"][0].data_ptr(), d["W0"][1].data_ptr())))
+    ptrs.append(P(Z.data_ptr()))
+    wt_arg = ctypes.byref(ops.CWeights(WT[0].data_ptr(), WT[1].data_ptr()))
+    ws_ptr = P(ws.data_ptr())
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    fwd = ops.lib().ttt_scan_fwd
+    ms_step, kms = _time_calls(
+        lambda i: fwd(cfg_c, *ptrs, wt_arg, None, None, ws_ptr, ws.numel(), stream),
+        args.steps, args.warmup)
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    k_avg = statistics.fmean(kms)
+    units = w.B * w.H * w.T
+    flop = units * flops_per_token_head(w.d, w.hidden, w.chunk)
+    achieved = flop / (k_avg * 1e-3) / 1e12
+    mfma = kernel != "ttt_fwd_generic"
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
+    io_bytes = 2 if w.io == "bf16" else 4
+    metric = ("TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)"
+              if wid == 3 else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}")
+    out = _base_record(args, metric, units / (ms_step * 1e-3), ms_step, w, kernel,
+                       "bf16" if mfma else "f32")
+    out["roofline"] = {
+        "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
+        "unit": "TFLOP/s", "frac": achieved / peak,
+        "traffic": _traffic(kernel, units) if wid == 3 else None,
+        "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
+        "algorithmic_bytes_per_launch": units * bytes_per_token_head(
+            w.d, io_bytes, 2 * w.d * w.hidden, w.T)}
+    if not args.no_cpu_baseline:
+        if wid == 3:
+            out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_T)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, 1, 2048)
+    return out
+
+
+def bwd_flops_per_token_head(d: int, h: int, b: int) -> int:
+    # The chunk's forward recomputed from its saved start weights (the five forward products:
+    # K W1, A^K W2, E2 W2^T, Q W1, A^Q W2, and the four dual terms), then two adjoint
+    # products for each of the seven d*h products (the five above and the two weight
+    # updates) and for each of the four dual terms.
+    return 5 * 2 * d * h + 4 * b * (d + h) + 2 * (7 * 2 * d * h + 4 * b * (d + h))
+
+
+def bench_scan_bwd(args) -> dict:
+    """One step = one ttt_scan_bwd over the whole batch (saved chunk-start weights from one
+    forward before the timed region)."""
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS
+    w = WORKLOADS[5]
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
+                     io=w.io)
+    kernel = ops.bwd_kernel_name(cfg)
+    dev = torch.device("cuda:0")
+    d = _device_inputs(w, dev, with_dz=True)
+    fwd = ops.scan_fwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["W0"], d["gamma"], d["beta"],
+                       want_saved=True)
+    ws = ops.new_workspace(cfg, ops.TTT_OP_BWD, dev)
+    res = {}
+
+    def call(i):
+        res.update(ops.scan_bwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["gamma"], d["beta"],
+                                fwd["saved"], d["dZ"], workspace=ws))
+        return 0
+
+    ms_step, kms = _time_calls(call, args.steps, args.warmup)
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    k_avg = statistics.fmean(kms)
+    units = w.B * w.H * w.T
+    flop = units * bwd_flops_per_token_head(w.d, w.hidden, w.chunk)
+    achieved = flop / (k_avg * 1e-3) / 1e12
+    mfma = kernel != "ttt_bwd_generic"
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
+    out = _base_record(args, f"TTT-MLP outer-loop backward token*heads/s at d={w.d}, T={w.T}",
+                       units / (ms_step * 1e-3), ms_step, w, kernel, "bf16" if mfma else "f32")
+    saved_bytes = w.B * w.H * (w.T // w.chunk) * 2 * w.d * w.hidden * 4
+    out["roofline"] = {
+        "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
+        "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+        "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
+        # Q, K, V, dZ in and dQ, dK, dV out (bf16), eta in and deta out, the saved weights
+        "algorithmic_bytes_per_launch": units * (7 * w.d * 2 + 8) + saved_bytes}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, 1, 1024, n_heads=4, grads=True)
+    return out
+
+
+def bench_decode(args) -> dict:
+    """One step = one full chunk of decode calls (16 tokens for every (batch, head) of the
+    config-3 shape), so every step includes one commit."""
+    import ctypes
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS
+    w = WORKLOADS[3]
+    b = w.chunk
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=b, d=w.d, hidden=w.hidden, chunk=b, io=w.io)
+    dev = torch.device("cuda:0")
+    d = _device_inputs(w.with_(T=b), dev)
+    Ws = tuple(x.unsqueeze(0).expand(w.B, *x.shape).contiguous() for x in d["W0"])
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    qkv = [d[k].permute(2, 0, 1, 3).contiguous() for k in ("Q", "K", "V")]  # [b, B, H, d]
+    eta = d["eta"].permute(2, 0, 1).contiguous()
+    z = torch.empty(w.B, w.H, w.d, dtype=cfg.io_dtype, device=dev)
+    ws = ops.new_workspace(cfg, ops.TTT_OP_DECODE, dev)
+    cfg_struct = cfg.c()
+    cfg_c = ctypes.byref(cfg_struct)
+    P = ctypes.c_void_p
+    wsw = ctypes.byref(ops.CWeights(Ws[0].data_ptr(), Ws[1].data_ptr()))
+    wacc = ctypes.byref(ops.CWeights(acc[0].data_ptr(), acc[1].data_ptr()))
+    gam, bet = P(d["gamma"].data_ptr()), P(d["beta"].data_ptr())
+    per_tok = [[P(qkv[0][t].data_ptr()), P(qkv[1][t].data_ptr()), P(qkv[2][t].data_ptr()),
+                P(eta[t].data_ptr())] for t in range(b)]
+    zp, ws_ptr = P(z.data_ptr()), P(ws.data_ptr())
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    dec = ops.lib().ttt_decode_step
+
+    def call(t):
+        q, k, v, e = per_tok[t]
+        return dec(cfg_c, q, k, v, e, gam, bet, wsw, wacc, t, zp, ws_ptr, ws.numel(), stream)
+
+    ms_step, kms = _time_calls(call, args.steps, args.warmup, calls_per_step=b)
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    heads = w.B * w.H
+    nW = 2 * w.d * w.hidden * 4
+    # per head: every call reads W_start and acc; b - 1 calls write acc, the commit writes
+    # W_start and clears acc
+    bytes_step = heads * nW * (2 * b + (b - 1) + 2)
+    k_sum_step = sum(kms) / args.steps
+    achieved = bytes_step / (k_sum_step * 1e-3) / 1e9
+    out = _base_record(args, f"TTT-MLP decode token*heads/s at d={w.d} ({heads} heads, one token "
+                             "per head per call)", heads * b / (ms_step * 1e-3), ms_step,
+                       w.with_(T=b), "ttt_decode", "f32")
+    out["roofline"] = {
+        "bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
+        "frac": achieved / 8000.0, "traffic": None,
+        "kernel_ms": statistics.fmean(kms), "kernel_ms_min": min(kms),
+        "algorithmic_bytes_per_launch": bytes_step / b}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, w.B, 4096)
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 2 for the d=128 workload)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 5; 1 for the d=128 workload)")
+    ap.add_argument("--workload", default="scan_fwd",
+                    choices=["scan_fwd", "scan_fwd_d128", "scan_bwd", "decode"],
+                    help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
+                         "scan_fwd_d128: B=1 H=24 T=131072 d=128 forward; "
+                         "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
+                         "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-T", type=int, default=8192)
@@ -99,6 +328,11 @@ def main():
                     help="instead of the scan, time a plain device-to-device copy of MIB MiB "
                          "(the known-size reference for scaling the HBM byte counters)")
     args = ap.parse_args()
+    long_run = args.workload == "scan_fwd_d128"
+    if args.steps is None:
+        args.steps = 2 if long_run else 20
+    if args.warmup is None:
+        args.warmup = 1 if long_run else 5
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the scan's heads would be "
               "sharded across GPUs with no communication, which is not built here.",
@@ -106,8 +340,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from test_weight_sequence_amd import ops
-    from test_weight_sequence_amd.synth import WORKLOADS, make_inputs
+    torch.cuda.set_device(torch.device("cuda:0"))
 
     if args.copy_probe:
         n = args.copy_probe * (1 << 20) // 4
@@ -125,90 +358,14 @@ def main():
                           "ms_per_copy": dt * 1e3, "GB_per_s": 8 * n / dt / 1e9}), flush=True)
         return
 
-    w = WORKLOADS[WORKLOAD_ID]
-    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
-                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
-    kernel = ops.fwd_kernel_name(cfg)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    inp = make_inputs(w)
-    d = {k: (tuple(x.to(dev) for x in v) if isinstance(v, tuple) else v.to(dev))
-         for k, v in inp.items()}
-    del inp
-    ws = ops.new_workspace(cfg, ops.TTT_OP_FWD, dev)
-    Z = torch.empty(w.B, w.H, w.T, w.d, dtype=cfg.io_dtype, device=dev)
-    WT = tuple(torch.empty(s, device=dev) for s in cfg.weight_shapes((w.B, w.H)))
-
-    # One step = one ttt_scan_fwd call; arguments are marshalled once, outside the
-    # timed region.
-    import ctypes
-    cfg_struct = cfg.c()
-    cfg_c = ctypes.byref(cfg_struct)
-    P = ctypes.c_void_p
-    ptrs = [P(d[k].data_ptr()) for k in ("Q", "K", "V", "eta", "gamma", "beta")]
-    ptrs.append(ctypes.byref(ops.CWeights(d["W0"][0].data_ptr(), d["W0"][1].data_ptr())))
-    ptrs.append(P(Z.data_ptr()))
-    wt_arg = ctypes.byref(ops.CWeights(WT[0].data_ptr(), WT[1].data_ptr()))
-    ws_ptr = P(ws.data_ptr())
-    stream = P(torch.cuda.current_stream().cuda_stream)
-    fwd = ops.lib().ttt_scan_fwd
-
-    def step():
-        return fwd(cfg_c, *ptrs, wt_arg, None, None, ws_ptr, ws.numel(), stream)
-
-    for _ in range(args.warmup):
-        rc = step()
-        if rc != 0:
-            raise ops.TTTError(rc, "ttt_scan_fwd")
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record()
-        step()
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if ops.read_status(ws) != 0:
-        raise RuntimeError("kernel reported non-finite values")
-    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_step = wall * 1e3 / args.steps
-    k_avg = statistics.fmean(kms)
-    units = w.B * w.H * w.T
-    value = units / (ms_step * 1e-3)
-    flop = units * flops_per_token_head(w.d, w.hidden, w.chunk)
-    achieved = flop / (k_avg * 1e-3) / 1e12
-    mfma = kernel != "ttt_fwd_generic"
-    peak = PEAK_BF16_TFLOPS
-    io_bytes = 2 if w.io == "bf16" else 4
-    traffic = _traffic(kernel, units)
-    out = {
-        "metric": "TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)",
-        "value": value,
-        "unit": "token*heads/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if mfma else "f32",
-        "data": "synthetic (seeded N(0,1/d) Q/K/V, N(0,0.02^2) W0, eta=0.1*sigmoid(N(0,1)))",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
-                   "hidden": w.hidden, "chunk": w.chunk, "io": w.io, "state": "fp32",
-                   "kernel": kernel},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel_ms": k_avg, "kernel_ms_min": min(kms),
-                     "flop_per_launch": flop,
-                     "algorithmic_bytes_per_launch": units * bytes_per_token_head(
-                         w.d, io_bytes, 2 * w.d * w.hidden, w.T)},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_T)
+    if args.workload == "scan_fwd":
+        out = bench_scan_fwd(args, 3)
+    elif args.workload == "scan_fwd_d128":
+        out = bench_scan_fwd(args, 4)
+    elif args.workload == "scan_bwd":
+        out = bench_scan_bwd(args)
+    else:
+        out = bench_decode(args)
     print(json.dumps(out), flush=True)
 
 

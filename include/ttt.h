@@ -169,6 +169,9 @@ ttt_status ttt_reset_status(void* workspace, void* stream);
  * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. */
 const char* ttt_fwd_kernel_name(const ttt_config* cfg);
 
+/* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */
+const char* ttt_bwd_kernel_name(const ttt_config* cfg);
+
 const char* ttt_status_str(ttt_status s);
 int32_t ttt_abi_version(void);
 

@@ -77,6 +77,17 @@ size_t fwd_ws_bytes(const ttt_config* c) {
   return kStatusBytes + static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
 }
 
+bool use_bwd_mfma(const ttt_config* c) {
+  if (c->flags & TTT_FORCE_GENERIC) return false;
+  BwdParams p{};
+  p.kind = c->kind;
+  p.d = c->d;
+  p.hid = hidden_of(c);
+  p.chunk = c->chunk;
+  p.io = c->io_dtype;
+  return bwd_mfma_supported(p);
+}
+
 size_t bwd_ws_bytes(const ttt_config* c) {
   const size_t heads = static_cast<size_t>(c->B) * c->H;
   return kStatusBytes +
@@ -137,6 +148,11 @@ const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK) return "";
   if (use_pair(cfg)) return "ttt_fwd_mfma_pair_d64";
   return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
+}
+
+const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
+  if (check_common(cfg, true) != TTT_OK) return "";
+  return use_bwd_mfma(cfg) ? "ttt_bwd_mfma_d64" : "ttt_bwd_generic";
 }
 
 ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
@@ -202,7 +218,8 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
   if (!workspace) return TTT_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TTT_ERR_ALIGN;
   if (ws_bytes < bwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
-  if (bwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk) > kMaxLds)
+  const bool tuned = use_bwd_mfma(cfg);
+  if (!tuned && bwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk) > kMaxLds)
     return TTT_ERR_UNSUPPORTED;
 
   BwdParams p{};
@@ -241,7 +258,7 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.work = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
   p.dgb = p.work + heads * bwd_work_floats_per_head(cfg->kind, cfg->d, p.hid, cfg->chunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_bwd_generic(p, s);
+  hipError_t e = tuned ? launch_bwd_mfma(p, s) : launch_bwd_generic(p, s);
   if (e != hipSuccess) return TTT_ERR_HIP;
   return map_hip(launch_bwd_finalize(p, s));
 }

@@ -105,6 +105,10 @@ __host__ __device__ inline size_t bwd_work_floats_per_head(int kind, int d, int 
   return nW + (kind == TTT_MLP ? static_cast<size_t>(kBwdArrays) * chunk * hid : 0);
 }
 hipError_t launch_bwd_generic(const BwdParams& p, hipStream_t s);
+// Tuned backward (d = 64, hidden = 256, chunk 16, bf16 I/O); writes the same per-head dW
+// and dgamma/dbeta partials as the portable kernel, for the same finalize kernel.
+bool bwd_mfma_supported(const BwdParams& p);
+hipError_t launch_bwd_mfma(const BwdParams& p, hipStream_t s);
 size_t bwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

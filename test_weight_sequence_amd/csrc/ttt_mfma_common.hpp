@@ -140,20 +140,22 @@ __device__ __forceinline__ LnStats ln_stats(const float z[4], float eps) {
   return LnStats{mu, __builtin_amdgcn_rsqf(var + eps)};  // v_rsq_f32, 1 ulp
 }
 
-// One wave's fp32 weight tiles: W1[:, hs:hs+32] as [d tile][h tile] and W2[hs:hs+32, :] as
-// [h tile][d tile] accumulator tiles, moved to and from row-major [d][HID] / [HID][d]
-// arrays with buffer instructions. Every element address is one per-lane register plus a
-// compile-time tile offset, so no per-element 64-bit addresses stay live.
+// One wave's fp32 weight tiles: W1[:, hs:hs+16*NH] as [d tile][h tile] and
+// W2[hs:hs+16*NH, :] as [h tile][d tile] accumulator tiles, moved to and from row-major
+// [d][HID] / [HID][d] arrays with buffer instructions. Every element address is one
+// per-lane register plus a compile-time tile offset, so no per-element 64-bit addresses
+// stay live.
 constexpr unsigned kBufFlags = 0x00020000u;
+template <int NH = 2>
 __device__ __forceinline__ void wtiles_load(const float* w1, const float* w2, int g, int c16, int hs,
-                                            f4 (&W1c)[NDT][2], f4 (&W2c)[2][NDT]) {
+                                            f4 (&W1c)[NDT][NH], f4 (&W2c)[NH][NDT]) {
   const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w1), 0, D * HID * 4, kBufFlags);
   const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w2), 0, D * HID * 4, kBufFlags);
   const int v1 = (4 * g * HID + hs + c16) * 4, v2 = ((hs + 4 * g) * D + c16) * 4;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < NH; ++ht)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         W1c[dt][ht][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, v1, ((16 * dt + r) * HID + 16 * ht) * 4, 0));
@@ -162,15 +164,16 @@ __device__ __forceinline__ void wtiles_load(const float* w1, const float* w2, in
 }
 // The element is copied to a scalar float first: a bit_cast applied directly to a vector
 // element was compiled as a read of element 0.
+template <int NH = 2>
 __device__ __forceinline__ void wtiles_store(float* w1, float* w2, int g, int c16, int hs,
-                                             const f4 (&W1c)[NDT][2], const f4 (&W2c)[2][NDT]) {
+                                             const f4 (&W1c)[NDT][NH], const f4 (&W2c)[NH][NDT]) {
   const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(w1, 0, D * HID * 4, kBufFlags);
   const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(w2, 0, D * HID * 4, kBufFlags);
   const int v1 = (4 * g * HID + hs + c16) * 4, v2 = ((hs + 4 * g) * D + c16) * 4;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int ht = 0; ht < NH; ++ht)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = W1c[dt][ht][r], b = W2c[ht][dt][r];
