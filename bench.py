@@ -294,7 +294,7 @@ def bench_decode(args) -> dict:
     achieved = bytes_step / (k_sum_step * 1e-3) / 1e9
     out = _base_record(args, f"TTT-MLP decode token*heads/s at d={w.d} ({heads} heads, one token "
                              "per head per call)", heads * b / (ms_step * 1e-3), ms_step,
-                       w.with_(T=b), "ttt_decode", "f32")
+                       w.with_(T=b), ops.decode_kernel_name(cfg), "f32")
     out["roofline"] = {
         "bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
         "frac": achieved / 8000.0, "traffic": None,

@@ -172,6 +172,9 @@ const char* ttt_fwd_kernel_name(const ttt_config* cfg);
 /* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */
 const char* ttt_bwd_kernel_name(const ttt_config* cfg);
 
+/* Name of the kernel variant ttt_decode_step would launch for cfg ("" if invalid). Host only. */
+const char* ttt_decode_kernel_name(const ttt_config* cfg);
+
 const char* ttt_status_str(ttt_status s);
 int32_t ttt_abi_version(void);
 

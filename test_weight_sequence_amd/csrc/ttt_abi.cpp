@@ -88,6 +88,15 @@ bool use_bwd_mfma(const ttt_config* c) {
   return bwd_mfma_supported(p);
 }
 
+bool use_decode_stream(const ttt_config* c) {
+  if (c->flags & TTT_FORCE_GENERIC) return false;
+  DecodeParams p{};
+  p.kind = c->kind;
+  p.d = c->d;
+  p.hid = hidden_of(c);
+  return decode_stream_supported(p);
+}
+
 size_t bwd_ws_bytes(const ttt_config* c) {
   const size_t heads = static_cast<size_t>(c->B) * c->H;
   return kStatusBytes +
@@ -153,6 +162,11 @@ const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
 const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK) return "";
   return use_bwd_mfma(cfg) ? "ttt_bwd_mfma_d64" : "ttt_bwd_generic";
+}
+
+const char* ttt_decode_kernel_name(const ttt_config* cfg) {
+  if (check_common(cfg, false) != TTT_OK) return "";
+  return use_decode_stream(cfg) ? "ttt_decode_stream_d64" : "ttt_decode_generic";
 }
 
 ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
@@ -308,7 +322,8 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
   p.acc_2 = mlp ? acc->w2 : nullptr;
   p.z = z;
   p.status = static_cast<unsigned*>(workspace);
-  return map_hip(launch_decode(p, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return map_hip(use_decode_stream(cfg) ? launch_decode_stream(p, s) : launch_decode(p, s));
 }
 
 ttt_status ttt_read_status(const void* workspace, void* stream) {

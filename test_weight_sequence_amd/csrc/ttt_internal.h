@@ -112,6 +112,10 @@ hipError_t launch_bwd_mfma(const BwdParams& p, hipStream_t s);
 size_t bwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// Tuned decode step (MLP, d = 64, hidden = 256): one 1024-thread workgroup per head that
+// streams W_start and acc through registers once.
+bool decode_stream_supported(const DecodeParams& p);
+hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
 hipError_t launch_reset_status(unsigned* status, hipStream_t s);
 
 }  // namespace ttt

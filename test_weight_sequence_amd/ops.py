@@ -5,7 +5,8 @@ device memory and to obtain the current HIP stream. If libttt.so is missing or
 cannot be loaded, every entry point raises: there is no fallback path.
 
 Names mirror include/ttt.h: scan_fwd, scan_bwd, decode_step, validate,
-workspace_size, saved_size, read_status, reset_status, fwd_kernel_name, bwd_kernel_name.
+workspace_size, saved_size, read_status, reset_status, fwd_kernel_name, bwd_kernel_name,
+decode_kernel_name.
 """
 from __future__ import annotations
 
@@ -30,7 +31,8 @@ STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE"
 
 EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
            "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
-           "ttt_fwd_kernel_name", "ttt_bwd_kernel_name", "ttt_status_str", "ttt_abi_version")
+           "ttt_fwd_kernel_name", "ttt_bwd_kernel_name", "ttt_decode_kernel_name", "ttt_status_str",
+           "ttt_abi_version")
 
 
 class TTTError(RuntimeError):
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_fwd_kernel_name.restype = ctypes.c_char_p
         L.ttt_bwd_kernel_name.argtypes = [cfgp]
         L.ttt_bwd_kernel_name.restype = ctypes.c_char_p
+        L.ttt_decode_kernel_name.argtypes = [cfgp]
+        L.ttt_decode_kernel_name.restype = ctypes.c_char_p
         L.ttt_status_str.argtypes = [I32]
         L.ttt_status_str.restype = ctypes.c_char_p
         for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
@@ -169,6 +173,10 @@ def fwd_kernel_name(cfg: Config) -> str:
 
 def bwd_kernel_name(cfg: Config) -> str:
     return lib().ttt_bwd_kernel_name(ctypes.byref(cfg.c())).decode()
+
+
+def decode_kernel_name(cfg: Config) -> str:
+    return lib().ttt_decode_kernel_name(ctypes.byref(cfg.c())).decode()
 
 
 def new_workspace(cfg: Config, op: int = TTT_OP_FWD, device="cuda") -> torch.Tensor:

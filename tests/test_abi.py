@@ -102,6 +102,8 @@ def test_kernel_selection_names():
     assert ops.fwd_kernel_name(cfg3(T=7)) == ""
     assert ops.bwd_kernel_name(cfg3(io="f32")) == "ttt_bwd_generic"
     assert ops.bwd_kernel_name(cfg3(T=7)) == ""
+    assert ops.decode_kernel_name(cfg3()) == "ttt_decode_stream_d64"
+    assert ops.decode_kernel_name(cfg3(force_generic=True)) == "ttt_decode_generic"
 
 
 class _FakeTensor:

@@ -294,6 +294,40 @@ def test_decode_loop_equals_scan(wid):
         assert torch.count_nonzero(a).item() == 0
 
 
+@pytest.mark.parametrize("io,gelu", [("bf16", "erf"), ("f32", "tanh")])
+def test_decode_stream_equals_oracle(io, gelu):
+    """The tuned decode kernel (MLP, d=64) and the portable one: 48 decode steps (three
+    commits) over 2 x 3 heads of the config-3 distributions, against the oracle scan of the
+    same tokens (z of every token, the committed weights)."""
+    w = WORKLOADS[3].with_(io=io)
+    T, bi, hi = 48, [0, 5], [1, 6, 11]
+    inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
+    B, H = len(bi), len(hi)
+    inp["W0"] = tuple(x.unsqueeze(0).expand(B, *x.shape).contiguous() for x in inp["W0"])
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    sub = {**inp, "W0": tuple(x[0] for x in inp["W0"])}
+    Zo, WTo, _ = oracle_heads(sub, pairs, "mlp", w.chunk, gelu=gelu)
+    d = to_dev(inp)
+    for generic in (False, True):
+        cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io=io, gelu=gelu,
+                         w0_per_seq=True, force_generic=generic)
+        assert ops.decode_kernel_name(cfg) == ("ttt_decode_generic" if generic
+                                               else "ttt_decode_stream_d64")
+        note(f"decode {ops.decode_kernel_name(cfg)} io={io} gelu={gelu}")
+        Ws = tuple(x.clone() for x in d["W0"])
+        acc = tuple(torch.zeros_like(x) for x in Ws)
+        zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
+                              _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t % 16)
+              for t in range(T)]
+        Z = torch.stack(zs, dim=2).cpu().reshape(B * H, T, 64)
+        tol = TOL[io]
+        assert rel_l2(Z, Zo) <= tol, (generic, rel_l2(Z, Zo))
+        for a, b in zip(Ws, WTo):
+            assert rel_l2(a.cpu().reshape(b.shape), b) <= TOL["f32"], generic
+        for a in acc:
+            assert torch.count_nonzero(a).item() == 0
+
+
 def test_scan_then_decode_continues_the_sequence():
     """Prefill T0 tokens with the scan, decode the rest: equals the oracle on all T."""
     w = WORKLOADS[1]
