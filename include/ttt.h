@@ -36,10 +36,11 @@
  *    runs on the host before anything is enqueued, so a non-OK return means nothing
  *    ran. A failed launch returns TTT_ERR_HIP. A non-finite loss or output detected
  *    inside a kernel is OR-ed into a status word in the workspace (sticky until
- *    ttt_reset_status); ttt_read_status reports it as TTT_ERR_NONFINITE. The paired
- *    forward kernel (two workgroups per head that hand data to each other) bounds
- *    every wait; an expired wait sets TTT_ERR_TIMEOUT in the same word (the outputs
- *    of that call are then undefined).
+ *    ttt_reset_status); ttt_read_status reports it as TTT_ERR_NONFINITE. The forward
+ *    kernels whose workgroups wait for each other (the paired d = 64 kernel, two
+ *    workgroups per head; the split d = 128 kernel, four) bound every wait; an expired
+ *    wait sets TTT_ERR_TIMEOUT in the same word (the outputs of that call are then
+ *    undefined).
  *  - No C++ exception crosses this interface. Calls that share a workspace must be
  *    ordered on one stream.
  */
@@ -156,7 +157,8 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
                            void* stream);
 
 /* Synchronises `stream`, then reads the workspace status word: TTT_OK,
- * TTT_ERR_TIMEOUT if a paired forward launch since the last reset had a wait expire,
+ * TTT_ERR_TIMEOUT if a forward launch of cooperating workgroups (the paired d = 64 or the
+ * split d = 128 kernel) since the last reset had a wait expire,
  * else TTT_ERR_NONFINITE if any kernel since the last reset saw a NaN/Inf. */
 ttt_status ttt_read_status(const void* workspace, void* stream);
 
@@ -166,7 +168,10 @@ ttt_status ttt_reset_status(void* workspace, void* stream);
 /* Name of the kernel variant ttt_scan_fwd would launch for cfg ("" if invalid). Host
  * only: "ttt_fwd_mfma_pair_d64" is chosen for the tuned shape when B*H <= 128 and
  * TTT_ONE_WG_PER_HEAD is not set; if the device then cannot hold all 2*ceil(B*H/8)*8
- * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. */
+ * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. For MLP d = 128,
+ * hidden = 512, chunk 16, bf16 I/O the name is "ttt_fwd_mfma_split_d128" (four workgroups per
+ * head); if the device cannot hold all 4*ceil(B*H/8)*8 of them at once, ttt_scan_fwd launches
+ * "ttt_fwd_generic" instead. */
 const char* ttt_fwd_kernel_name(const ttt_config* cfg);
 
 /* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */

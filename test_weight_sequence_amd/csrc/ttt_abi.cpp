@@ -3,6 +3,7 @@
 // anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -71,10 +72,19 @@ bool use_pair(const ttt_config* c) {
          static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
 }
 
+bool use_split(const ttt_config* c) {
+  if (c->flags & TTT_FORCE_GENERIC) return false;
+  ScanParams p = scan_params(c);
+  return fwd_split_supported(p);
+}
+
 size_t fwd_ws_bytes(const ttt_config* c) {
   if (use_pair(c)) return kStatusBytes + fwd_pair_workspace_bytes(c->B * c->H);
   if (use_mfma(c)) return kStatusBytes;
-  return kStatusBytes + static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
+  const size_t generic = static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
+  // the split kernel falls back to the portable one when its grid does not fit the device
+  if (use_split(c)) return kStatusBytes + std::max(generic, fwd_split_workspace_bytes(c->B * c->H));
+  return kStatusBytes + generic;
 }
 
 bool use_bwd_mfma(const ttt_config* c) {
@@ -156,6 +166,7 @@ ttt_status ttt_saved_size(const ttt_config* cfg, size_t* bytes) {
 const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK) return "";
   if (use_pair(cfg)) return "ttt_fwd_mfma_pair_d64";
+  if (use_split(cfg)) return "ttt_fwd_mfma_split_d128";
   return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
 }
 
@@ -207,6 +218,7 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
+  if (use_split(cfg) && fwd_split_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_split(p, s));
   return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
 }
 

@@ -1,0 +1,500 @@
+// Tuned forward scan for the long-context TTT-MLP head shape d = 128, hidden = 512, chunk 16,
+// bf16 Q/K/V/Z, fp32 fast weights (gfx950, bf16 MFMA with fp32 accumulation).
+//
+// A head's fp32 fast weights (W1 128 x 512 and W2 512 x 128, 512 KiB) are as large as one
+// CU's whole register file, so the head is split by hidden units over S = 4 workgroups of 4
+// waves (one wave per SIMD): workgroup s holds hidden units [128 s, 128 s + 128) and its
+// wave w the 32 units from 128 s + 32 w, as fp32 MFMA accumulator tiles that stay in
+// registers for the whole scan. Everything that is per hidden unit (H^K, A^K, E1, H^Q,
+// A^Q, the weight update) is local to a workgroup. The two sums over all hidden units that
+// every chunk needs, Z^K = A^K W2 (for the inner-loss LayerNorm) and
+// Z^Q = A^Q W2 + tril(A^Q A^K^T) E2 (for the output), are formed from the four
+// workgroups' [16 x 128] partial sums: each workgroup writes its partial to a slot in the
+// workspace, raises its counter (release, device scope), waits for the other three
+// (acquire) and adds the four partials in the same fixed order, so all four compute
+// bit-identical sums and therefore the same E2.
+//
+// Per chunk (E = eta-scaled, negated rows; all at the chunk-start weights): the dual form
+// of the per-token rule on the page "Test-Time Training(TTT)과 LLM 메모리", section
+// "TTT layer", Eq. 2/4/5, with the mini-batch rule of the E2E paper review, section 2.3,
+// Eq. 5:
+//   H^K = K W1, A^K = GELU, G = GELU';  Z^K = A^K W2 (summed over the workgroups)
+//   LN fwd/bwd of Z^K per token -> En2 = -eta * delta2;  E1n = (En2 W2^T) (.) G
+//   H^Q = Q W1 + tril(Q K^T) E1n, A^Q = GELU;  Z^Q = A^Q W2 + tril(A^Q A^K^T) En2 (summed)
+//   z = Q + LN(Z^Q);  W1 += K^T E1n, W2 += A^K^T En2
+// The four workgroups of a head are numbered so that the hardware's round-robin placement
+// puts them on one XCD, where the exchange stays in that XCD's L2.
+#include "ttt_mfma_common.hpp"
+
+namespace ttt {
+namespace {
+
+using mfma::bf16x4;
+using mfma::bf16x8;
+using mfma::f4;
+using mfma::cat;
+using mfma::cvt4;
+using mfma::lds4;
+using mfma::mfma16;
+using mfma::mfma32;
+using mfma::sum16;
+using mfma::zero4;
+
+constexpr int D = 128;
+constexpr int HID = 512;
+constexpr int BC = 16;
+constexpr int NDT = D / 16;          // d tiles
+constexpr int S = 4;                 // workgroups per head
+constexpr int NW = 4;                // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int HS = HID / (S * NW);   // hidden units per wave
+constexpr int NHT = HS / 16;         // h tiles per wave
+constexpr int NKD = D / 32;          // 32-wide k-steps over d
+constexpr int RS = D + 8;            // row stride (bf16) of [token][d] arrays
+constexpr int TS = BC + 8;           // row stride of [d][token] arrays
+constexpr int DPL = D / 16;          // d values per LayerNorm lane
+constexpr int kSpinLimit = 1 << 20;
+static_assert(NHT == 2 && NW * 4 == BC, "tile split");
+
+// Workspace per head: two exchange areas (Z^K, Z^Q) of two chunk-parity slots of S partial
+// [16 x 128] fp32 sums, then (after all heads) 32 counter words per head.
+constexpr size_t kPartFloats = static_cast<size_t>(BC) * D;
+constexpr size_t kHeadXFloats = 2 * 2 * S * kPartFloats;
+constexpr int kFlagWords = 32;  // [0, S): Z^K counters, [8, 8 + S): Z^Q counters
+
+struct Stage {
+  alignas(16) __bf16 K[BC * RS];
+  alignas(16) __bf16 Q[BC * RS];
+  alignas(16) __bf16 V[BC * RS];
+  alignas(16) __bf16 Kt[D * TS];
+  float eta[BC];
+};
+
+struct Smem {
+  Stage st[2];                        // chunk c lives in st[c & 1]
+  float red[NW][NDT][4][64];          // per-wave [token x d] partial tiles (lane-rotated rows)
+  alignas(16) __bf16 E2[BC * RS];     // En2, [token][d]
+  alignas(16) __bf16 E2t[D * TS];     // En2, [d][token]
+};
+
+__device__ __forceinline__ int prot(int r, int lane) { return (lane + 16 * r) & 63; }
+
+struct Split {
+  float* xbuf;        // exchange areas, kHeadXFloats per head
+  unsigned* flags;    // kFlagWords per head
+  int nheads;
+};
+
+// fp32 weight tiles of one wave: W1[:, hb:hb+32] as [d tile][h tile], W2[hb:hb+32, :] as
+// [h tile][d tile] (accumulator layout: row 4 (lane/16) + r, column lane % 16), moved with
+// buffer instructions: one per-lane offset register plus a scalar offset per element.
+__device__ __forceinline__ void w_load(const float* w1, const float* w2, int g, int c16, int hb,
+                                       f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT]) {
+  const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w1), 0, D * HID * 4, mfma::kBufFlags);
+  const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w2), 0, D * HID * 4, mfma::kBufFlags);
+  const int v1 = (4 * g * HID + hb + c16) * 4, v2 = ((hb + 4 * g) * D + c16) * 4;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        W1c[dt][ht][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r1, v1, ((16 * dt + r) * HID + 16 * ht) * 4, 0));
+        W2c[ht][dt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r2, v2, ((16 * ht + r) * D + 16 * dt) * 4, 0));
+      }
+}
+// (each element is copied to a scalar float before the store: a bit_cast applied directly
+// to a vector element was compiled as a read of element 0)
+__device__ __forceinline__ void w_store(float* w1, float* w2, int g, int c16, int hb,
+                                        const f4 (&W1c)[NDT][NHT], const f4 (&W2c)[NHT][NDT]) {
+  const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(w1, 0, D * HID * 4, mfma::kBufFlags);
+  const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(w2, 0, D * HID * 4, mfma::kBufFlags);
+  const int v1 = (4 * g * HID + hb + c16) * 4, v2 = ((hb + 4 * g) * D + c16) * 4;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = W1c[dt][ht][r], b = W2c[ht][dt][r];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r1, v1, ((16 * dt + r) * HID + 16 * ht) * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b), r2, v2, ((16 * ht + r) * D + 16 * dt) * 4, 0);
+      }
+}
+
+// Publish this workgroup's partial (already stored by every thread) as chunk c and wait for
+// the other workgroups' partials of chunk c. Bounded: an expired wait sets the timeout bit,
+// and once that bit is set no later wait spins, so a lost partner costs one bound in total.
+__device__ __forceinline__ void exchange(unsigned* cnt, int s, unsigned c1, unsigned* status) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(cnt + s, c1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    bool late = (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout) != 0;
+    for (int o = 0; o < S && !late; ++o) {
+      if (o == s) continue;
+      int it = 0;
+      while (__hip_atomic_load(cnt + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c1) {
+        if (++it >= kSpinLimit) {
+          late = true;
+          atomicOr(status, kStatusTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+template <int GELU_KIND>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd_split_kernel(ScanParams p, Split x) {
+  __shared__ Smem sm;
+  // block -> (head, part): the S parts of a head are 8 blocks apart (same XCD)
+  const int b = blockIdx.x;
+  const int s = (b >> 3) % S;
+  const int bh = ((b >> 3) / S) * 8 + (b & 7);
+  if (bh >= x.nheads) return;  // all parts of a missing head leave together
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int hidx = bh % p.H;
+  const int hb = s * (HID / S) + w * HS;
+  const int T = p.T, nchunks = T / BC;
+  const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
+  float* xz = x.xbuf + static_cast<size_t>(bh) * kHeadXFloats;  // [slot][S][16 x 128]
+  float* xq = xz + 2 * S * kPartFloats;
+  unsigned* cz = x.flags + static_cast<size_t>(bh) * kFlagWords;
+  unsigned* cq = cz + 8;
+
+  f4 W1c[NDT][NHT], W2c[NHT][NDT];
+  {
+    const size_t wh = per_seq ? static_cast<size_t>(bh) : static_cast<size_t>(hidx);
+    w_load(p.w0_1 + wh * D * HID, p.w0_2 + wh * HID * D, g, c16, hb, W1c, W2c);
+  }
+  const bf16x4 I4 = mfma::make_ident(g, c16).i4;
+
+  // LayerNorm lanes: token 4 w + lane/16, 16 lanes per token, d = 16 i + lane%16
+  const int ln_t = 4 * w + g;
+  float gam[DPL], bet[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    gam[i] = p.gamma[hidx * D + 16 * i + c16];
+    bet[i] = p.beta[hidx * D + 16 * i + c16];
+  }
+
+  const size_t io_off = static_cast<size_t>(bh) * T * D;
+  const __bf16* Qg = static_cast<const __bf16*>(p.Q) + io_off;
+  const __bf16* Kg = static_cast<const __bf16*>(p.K) + io_off;
+  const __bf16* Vg = static_cast<const __bf16*>(p.V) + io_off;
+  __bf16* Zg = static_cast<__bf16*>(p.Z) + io_off;
+  const float* etag = p.eta + static_cast<size_t>(bh) * T;
+
+  // staging: thread -> token st_t, 8 consecutive d from st_d
+  const int st_t = tid >> 4, st_d = (tid & 15) * 8;
+  auto gload = [&](int chunk, uint4& kk, uint4& qq, uint4& vv, float& e) {
+    const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
+    kk = *reinterpret_cast<const uint4*>(Kg + off);
+    qq = *reinterpret_cast<const uint4*>(Qg + off);
+    vv = *reinterpret_cast<const uint4*>(Vg + off);
+    e = tid < BC ? etag[chunk * BC + tid] : 0.f;
+  };
+  auto stage_write = [&](Stage& St, uint4 kk, uint4 qq, uint4 vv, float e) {
+    *reinterpret_cast<uint4*>(&St.K[st_t * RS + st_d]) = kk;
+    *reinterpret_cast<uint4*>(&St.Q[st_t * RS + st_d]) = qq;
+    *reinterpret_cast<uint4*>(&St.V[st_t * RS + st_d]) = vv;
+    const bf16x8 kv = __builtin_bit_cast(bf16x8, kk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) St.Kt[(st_d + j) * TS + st_t] = kv[j];
+    if (tid < BC) St.eta[tid] = e * p.eta_scale;
+  };
+  // this workgroup's [16 x 128] partial for the LayerNorm lanes' elements, from the waves'
+  // tiles in red (fixed wave order)
+  auto own_partial = [&](float (&o)[DPL]) {
+    const int t = ln_t;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) a += sm.red[ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
+      o[i] = a;
+    }
+  };
+  // the head's total from the S partials of a slot (fixed part order)
+  auto total = [&](const float* slot, float (&z)[DPL]) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int off = ln_t * D + 16 * i + c16;
+      float a = 0.f;
+#pragma unroll
+      for (int o = 0; o < S; ++o) a += __builtin_nontemporal_load(slot + o * kPartFloats + off);
+      z[i] = a;
+    }
+  };
+  auto ln_stats8 = [&](const float (&z)[DPL], float& mu, float& rs) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) a += z[i];
+    mu = sum16(a) * (1.0f / D);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) v += (z[i] - mu) * (z[i] - mu);
+    rs = __builtin_amdgcn_rsqf(sum16(v) * (1.0f / D) + p.eps);
+  };
+
+  {
+    uint4 kk, qq, vv;
+    float e;
+    gload(0, kk, qq, vv, e);
+    stage_write(sm.st[0], kk, qq, vv, e);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    Stage& St = sm.st[c & 1];
+    const int t0 = c * BC;
+    const unsigned c1 = static_cast<unsigned>(c) + 1u;
+    const int slot = c & 1;
+    uint4 nk{}, nq{}, nv{};
+    float ne = 0.f;
+    const bool has_next = c + 1 < nchunks;
+    if (has_next) gload(c + 1, nk, nq, nv, ne);
+    if (p.saved) {
+      float* sv = p.saved + (static_cast<size_t>(bh) * nchunks + c) * (2 * D * HID);
+      w_store(sv, sv + D * HID, g, c16, hb, W1c, W2c);
+    }
+
+    bf16x8 aK[NKD], aQ[NKD];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      aK[ks] = cat(lds4(&St.K[c16 * RS + 32 * ks + 4 * g]), lds4(&St.K[c16 * RS + 32 * ks + 16 + 4 * g]));
+      aQ[ks] = cat(lds4(&St.Q[c16 * RS + 32 * ks + 4 * g]), lds4(&St.Q[c16 * RS + 32 * ks + 16 + 4 * g]));
+    }
+    bf16x4 W1b[NDT][NHT], W2b[NHT][NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        W1b[dt][ht] = cvt4(W1c[dt][ht]);
+        W2b[ht][dt] = cvt4(W2c[ht][dt]);
+      }
+
+    // ---- K side: H^K = K W1, A^K, G; Z^K partial over this wave's hidden units ----
+    bf16x4 akR[NHT], akT[NHT];
+    f4 gk[NHT], hq[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f4 acc = zero4(), accq = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        const bf16x8 wb = cat(W1b[2 * ks][ht], W1b[2 * ks + 1][ht]);
+        acc = mfma32(aK[ks], wb, acc);
+        accq = mfma32(aQ[ks], wb, accq);
+      }
+      hq[ht] = accq;
+      f4 a, gd;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v, d1;
+        mfma::act_d<GELU_KIND>(acc[r], v, d1);
+        a[r] = v;
+        gd[r] = d1;
+      }
+      gk[ht] = gd;
+      akR[ht] = cvt4(a);
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) akT[ht] = cvt4(mfma16(akR[ht], I4, zero4()));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f4 acc = mfma32(cat(akT[0], akT[1]), cat(W2b[0][dt], W2b[1][dt]), zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
+    }
+    f4 s1t = zero4();  // C[s][t] = K_s . Q_t
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) s1t = mfma32(aK[ks], aQ[ks], s1t);
+    __syncthreads();
+
+    // ---- Z^K over all hidden units, LayerNorm forward/backward -> En2 ----
+    {
+      float own[DPL];
+      own_partial(own);
+      float* mine = xz + (slot * S + s) * kPartFloats;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) mine[ln_t * D + 16 * i + c16] = own[i];
+    }
+    exchange(cz, s, c1, p.status);
+    {
+      const int t = ln_t;
+      float z[DPL];
+      total(xz + slot * S * kPartFloats, z);
+      float mu, rs;
+      ln_stats8(z, mu, rs);
+      float xh[DPL], gg[DPL], l2 = 0.f, sg = 0.f, sgx = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        xh[i] = (z[i] - mu) * rs;
+        const float r = mfma::bf(St.K[t * RS + d]) + gam[i] * xh[i] + bet[i] - mfma::bf(St.V[t * RS + d]);
+        l2 += r * r;
+        gg[i] = 2.f * r * gam[i];
+        sg += gg[i];
+        sgx += gg[i] * xh[i];
+      }
+      const float loss = sum16(l2);
+      const float mg = sum16(sg) * (1.0f / D), mgx = sum16(sgx) * (1.0f / D);
+      const float ne2 = -St.eta[t] * rs;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
+        sm.E2[t * RS + d] = e;
+        sm.E2t[d * TS + t] = e;
+      }
+      if (c16 == 0 && s == 0) {
+        if (p.loss) p.loss[static_cast<size_t>(bh) * T + t0 + t] = loss;
+        flag_nonfinite(p.status, loss);
+      }
+    }
+    if (has_next) stage_write(sm.st[(c + 1) & 1], nk, nq, nv, ne);
+    __syncthreads();
+
+    // ---- E1n = (En2 W2^T) (.) G ; H^Q ; A^Q ; Z^Q partial ----
+    bf16x8 aE[NKD];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+      aE[ks] = cat(lds4(&sm.E2[c16 * RS + 32 * ks + 4 * g]), lds4(&sm.E2[c16 * RS + 32 * ks + 16 + 4 * g]));
+    bf16x4 e1[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks)
+        acc = mfma32(aE[ks], cat(cvt4(mfma16(W2b[ht][2 * ks], I4, zero4())),
+                                 cvt4(mfma16(W2b[ht][2 * ks + 1], I4, zero4()))), acc);
+      e1[ht] = cvt4(acc * gk[ht]);
+    }
+    f4 s1m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s1m[r] = (4 * g + r) <= c16 ? s1t[r] : 0.f;
+    const bf16x4 s1a = cvt4(s1m);
+    bf16x4 aqT[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const f4 h = mfma16(s1a, e1[ht], hq[ht]);
+      f4 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = mfma::act<GELU_KIND>(h[r]);
+      aqT[ht] = cvt4(mfma16(cvt4(a), I4, zero4()));
+    }
+    f4 s2t = mfma32(cat(akT[0], akT[1]), cat(aqT[0], aqT[1]), zero4());  // C[s][t] = A^K_s . A^Q_t
+    f4 s2m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s2m[r] = (4 * g + r) <= c16 ? s2t[r] : 0.f;
+    const bf16x4 s2a = cvt4(s2m);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x4 be = lds4(&sm.E2t[(16 * dt + c16) * TS + 4 * g]);
+      f4 acc = mfma32(cat(aqT[0], aqT[1]), cat(W2b[0][dt], W2b[1][dt]), zero4());
+      acc = mfma16(s2a, be, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
+      // chunk-end update of this wave's fp32 weights
+      const bf16x4 kt = lds4(&St.Kt[(16 * dt + c16) * TS + 4 * g]);
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        W1c[dt][ht] = mfma16(kt, e1[ht], W1c[dt][ht]);
+        W2c[ht][dt] = mfma16(akR[ht], be, W2c[ht][dt]);
+      }
+    }
+    __syncthreads();
+
+    // ---- Z^Q over all hidden units; z = Q + LN(Z^Q) (part s writes tokens 4s .. 4s + 3) ----
+    {
+      float own[DPL];
+      own_partial(own);
+      float* mine = xq + (slot * S + s) * kPartFloats;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) mine[ln_t * D + 16 * i + c16] = own[i];
+    }
+    exchange(cq, s, c1, p.status);
+    if (w == s) {
+      const int t = ln_t;
+      float z[DPL];
+      total(xq + slot * S * kPartFloats, z);
+      float mu, rs;
+      ln_stats8(z, mu, rs);
+      float chk = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        const int d = 16 * i + c16;
+        const float o = mfma::bf(St.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
+        chk += o;
+        Zg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)o;
+      }
+      chk = sum16(chk);
+      if (c16 == 0) flag_nonfinite(p.status, chk);
+    }
+  }
+
+  if (p.wt_1)
+    w_store(p.wt_1 + static_cast<size_t>(bh) * D * HID, p.wt_2 + static_cast<size_t>(bh) * HID * D,
+            g, c16, hb, W1c, W2c);
+}
+
+__global__ void split_reset_kernel(unsigned* flags, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = 0u;
+}
+
+}  // namespace
+
+bool fwd_split_supported(const ScanParams& p) {
+  return p.kind == TTT_MLP && p.d == D && p.hid == HID && p.chunk == BC && p.io == TTT_BF16;
+}
+
+size_t fwd_split_workspace_bytes(int nheads) {
+  return static_cast<size_t>(nheads) * (kHeadXFloats * sizeof(float) + kFlagWords * sizeof(unsigned));
+}
+
+int fwd_split_blocks(int nheads) { return (nheads + 7) / 8 * 8 * S; }
+
+// Whether the current device can hold every workgroup of the launch at once (the parts of a
+// head wait for each other). The answer is cached per device ordinal.
+bool fwd_split_fits(int nheads) {
+  constexpr int kMaxDev = 64;
+  static int cap[kMaxDev];  // 0 = unknown, else 1 + resident workgroups on the device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+  if (cap[dev] == 0) {
+    int coop = 0, ncu = 0, per_cu = 0;
+    const bool ok =
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_ERF>), NT, 0) == hipSuccess;
+    cap[dev] = 1 + ((ok && coop) ? ncu * per_cu : 0);
+  }
+  return fwd_split_blocks(nheads) <= cap[dev] - 1;
+}
+
+hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t stream) {
+  const int nheads = p.B * p.H;
+  Split x;
+  x.xbuf = p.wbuf;
+  x.flags = reinterpret_cast<unsigned*>(p.wbuf + static_cast<size_t>(nheads) * kHeadXFloats);
+  x.nheads = nheads;
+  const int nflags = nheads * kFlagWords;
+  hipLaunchKernelGGL(split_reset_kernel, dim3((nflags + 255) / 256), dim3(256), 0, stream, x.flags, nflags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ScanParams pc = p;
+  void* args[] = {&pc, &x};
+  const void* fn = p.gelu == TTT_GELU_TANH ? reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_TANH>)
+                                           : reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_ERF>);
+  return hipLaunchCooperativeKernel(fn, dim3(fwd_split_blocks(nheads)), dim3(NT), args, 0, stream);
+}
+
+}  // namespace ttt

@@ -97,6 +97,13 @@ size_t fwd_pair_workspace_bytes(int nheads);
 int fwd_pair_blocks(int nheads);
 bool fwd_pair_fits(int nheads);
 hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t s);
+// Forward for the d = 128, hidden = 512 head: each head split by hidden units over four
+// workgroups that exchange [chunk x d] partial sums through the workspace.
+bool fwd_split_supported(const ScanParams& p);
+size_t fwd_split_workspace_bytes(int nheads);
+int fwd_split_blocks(int nheads);
+bool fwd_split_fits(int nheads);
+hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t s);
 // Per-head backward workspace (floats): the carried dW, then kBwdArrays [chunk x hidden]
 // intermediates (MLP only).
 constexpr int kBwdArrays = 12;

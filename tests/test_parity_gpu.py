@@ -86,35 +86,93 @@ def test_cfg3_all_heads_short(kernel):
     _check_heads(res, inp, pairs, w, TOL["bf16"])
 
 
-def test_cfg4_d128_reduced_T():
-    """Config-4 head shape (d=128, hidden=512, AR(1) drifting inputs) on two heads, T=512."""
+CFG4_KERNELS = {"split": ({}, "ttt_fwd_mfma_split_d128"),
+                "generic": (dict(force_generic=True), "ttt_fwd_generic")}
+
+
+@pytest.mark.parametrize("kernel", ["split", "generic"])
+def test_cfg4_d128_reduced_T(kernel):
+    """Config-4 head shape (d=128, hidden=512, AR(1) drifting inputs) on two heads, T=512,
+    through the split kernel (four workgroups per head) and the portable one."""
     w = WORKLOADS[4]
-    note("cfg4 d=128 T=512 heads 0,23")
     inp = make_inputs(w, head_idx=[0, 23], T=512)
-    cfg = ops_config(w, T=512, H=2)
+    flags, name = CFG4_KERNELS[kernel]
+    cfg = ops_config(w, T=512, H=2, **flags)
+    assert ops.fwd_kernel_name(cfg) == name
+    note(f"cfg4 d=128 T=512 heads 0,23 {name}")
     res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
     _check_heads(res, inp, [(0, 0), (0, 1)], w, TOL["bf16"])
 
 
-def test_cfg4_full_length_two_heads_prefix():
-    """Config-4 heads at full length (T=131072, d=128, hidden=512, AR(1) drift): two heads
-    run through the whole scan; outputs of the first 1024 tokens (which depend only on the
-    prefix) are checked against the oracle, and the end state must stay finite."""
+def test_cfg4_full_size_sampled_heads_prefix():
+    """Full config-4 launch (B=1, H=24, T=131072) of the split kernel: the end state of every
+    head is finite, and for two heads z and the per-token loss of the first 4096 tokens
+    (which depend only on that prefix) match the oracle."""
     w = WORKLOADS[4]
-    note("cfg4 full T two heads")
-    inp = make_inputs(w, head_idx=[5, 17])
-    cfg = ops_config(w, H=2)
+    inp = make_inputs(w)
+    cfg = ops_config(w)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    note("cfg4 full size, split kernel")
     res = _run(cfg, to_dev(inp), want_loss=True)
     torch.cuda.synchronize()
     assert ops.read_status(res["workspace"]) == 0
     for x in res["W_T"]:
         assert torch.isfinite(x).all()
-    Tp = 1024
+    Tp = 4096
+    pairs = [(0, 5), (0, 17)]
     pre = {k: (v[:, :, :Tp] if k in ("Q", "K", "V", "eta") else v) for k, v in inp.items()}
-    Z, _, L = oracle_heads(pre, [(0, 0), (0, 1)], w.kind, w.chunk)
-    gz = res["Z"][0, :, :Tp].cpu()
+    Z, _, L = oracle_heads(pre, pairs, w.kind, w.chunk)
+    gz = torch.stack([res["Z"][b, h, :Tp] for b, h in pairs]).cpu()
+    gl = torch.stack([res["loss"][b, h, :Tp] for b, h in pairs]).cpu()
     assert rel_l2(gz, Z) <= TOL["bf16"], rel_l2(gz, Z)
-    assert rel_l2(res["loss"][0, :, :Tp].cpu(), L) <= TOL["bf16"]
+    assert rel_l2(gl, L) <= TOL["bf16"], rel_l2(gl, L)
+
+
+def test_split_partial_group_tanh_per_seq():
+    """The split kernel with per-sequence W0, tanh GELU and a head count that leaves most of
+    the last group of eight empty (B=2, H=3), all heads against the oracle."""
+    B, H, T = 2, 3, 96
+    inp = _rand_case("mlp", B, H, T, 128, 16, "bf16", seed=13, per_seq=True)
+    cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=128, hidden=512, chunk=16, io="bf16",
+                     gelu="tanh", w0_per_seq=True, eta_scale=0.5)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    note("split tanh per-seq B=2 H=3")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    flat, ocfg = _oracle_all(inp, "mlp", 16, per_seq=True, gelu="tanh", eta_scale=0.5)
+    from oracle import scan as oracle_scan
+    Z, WT, L = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
+                           flat["gamma"], flat["beta"], ocfg)
+    assert rel_l2(res["Z"].reshape(B * H, T, 128), Z) <= TOL["bf16"]
+    assert rel_l2(res["loss"].reshape(B * H, T), L) <= TOL["bf16"]
+    for g, o in zip(res["W_T"], WT):
+        assert rel_l2(g.reshape(o.shape), o) <= TOL["bf16"]
+
+
+def test_split_saved_chunk_start_weights():
+    """The split kernel's saved buffer: W0 exactly at chunk 0, and at chunk 2 the W_T of a
+    scan over the first two chunks."""
+    w = WORKLOADS[4]
+    T = 64
+    inp = make_inputs(w, head_idx=[3, 4, 9], T=T)
+    cfg = ops_config(w, T=T, H=3)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    d = to_dev(inp)
+    note("split saved weights")
+    res = _run(cfg, d, want_saved=True)
+    nW1 = w.d * w.hidden
+    sv = res["saved"].view(1, 3, T // w.chunk, 2 * nW1).cpu()
+    for h in range(3):
+        assert torch.equal(sv[0, h, 0, :nW1], inp["W0"][0][h].reshape(-1))
+        assert torch.equal(sv[0, h, 0, nW1:], inp["W0"][1][h].reshape(-1))
+    pre = _run(ops_config(w, T=32, H=3), {**d, **{k: d[k][:, :, :32].contiguous()
+                                                  for k in ("Q", "K", "V", "eta")}})
+    torch.cuda.synchronize()
+    assert torch.equal(sv[:, :, 2, :nW1], pre["W_T"][0].reshape(1, 3, -1).cpu())
+    assert torch.equal(sv[:, :, 2, nW1:], pre["W_T"][1].reshape(1, 3, -1).cpu())
 
 
 @pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
