@@ -10,9 +10,11 @@
 // every chunk needs, Z^K = A^K W2 (for the inner-loss LayerNorm) and
 // Z^Q = A^Q W2 + tril(A^Q A^K^T) E2 (for the output), are formed from the four
 // workgroups' [16 x 128] partial sums: each workgroup writes its partial to a slot in the
-// workspace, raises its counter (release, device scope), waits for the other three
-// (acquire) and adds the four partials in the same fixed order, so all four compute
-// bit-identical sums and therefore the same E2.
+// workspace, raises its counter, waits for the other three and adds the four partials in the
+// same fixed order, so all four compute bit-identical sums and therefore the same E2. Only
+// Z^K is waited for: a workgroup publishes its Z^Q partial of chunk c before its Z^K partial
+// of chunk c + 1, so once the Z^K wait of chunk c + 1 is over, the Z^Q partials of chunk c
+// are all in place, and the output of chunk c is written then.
 //
 // Per chunk (E = eta-scaled, negated rows; all at the chunk-start weights): the dual form
 // of the per-token rule on the page "Test-Time Training(TTT)과 LLM 메모리", section
@@ -23,7 +25,9 @@
 //   H^Q = Q W1 + tril(Q K^T) E1n, A^Q = GELU;  Z^Q = A^Q W2 + tril(A^Q A^K^T) En2 (summed)
 //   z = Q + LN(Z^Q);  W1 += K^T E1n, W2 += A^K^T En2
 // The four workgroups of a head are numbered so that the hardware's round-robin placement
-// puts them on one XCD, where the exchange stays in that XCD's L2.
+// puts them on one XCD. They check that at start (HW_REG_XCC_ID): on one XCD the exchange
+// goes through that XCD's L2 with plain stores and loads that skip the CU's L1; otherwise it
+// uses device-scope release/acquire fences.
 #include "ttt_mfma_common.hpp"
 
 namespace ttt {
@@ -60,7 +64,8 @@ static_assert(NHT == 2 && NW * 4 == BC, "tile split");
 // [16 x 128] fp32 sums, then (after all heads) 32 counter words per head.
 constexpr size_t kPartFloats = static_cast<size_t>(BC) * D;
 constexpr size_t kHeadXFloats = 2 * 2 * S * kPartFloats;
-constexpr int kFlagWords = 32;  // [0, S): Z^K counters, [8, 8 + S): Z^Q counters
+constexpr int kFlagWords = 32;  // [0, S): Z^K counters, [8, 8 + S): Z^Q, [16, 16 + S): XCD ids
+constexpr int kLoadL2 = 16;     // cache policy of exchange loads on one XCD: device scope (sc1)
 
 struct Stage {
   alignas(16) __bf16 K[BC * RS];
@@ -71,7 +76,7 @@ struct Stage {
 };
 
 struct Smem {
-  Stage st[2];                        // chunk c lives in st[c & 1]
+  Stage st[3];                        // chunk c lives in st[c % 3]
   float red[NW][NDT][4][64];          // per-wave [token x d] partial tiles (lane-rotated rows)
   alignas(16) __bf16 E2[BC * RS];     // En2, [token][d]
   alignas(16) __bf16 E2t[D * TS];     // En2, [d][token]
@@ -122,19 +127,46 @@ __device__ __forceinline__ void w_store(float* w1, float* w2, int g, int c16, in
       }
 }
 
-// Publish this workgroup's partial (already stored by every thread) as chunk c and wait for
-// the other workgroups' partials of chunk c. Bounded: an expired wait sets the timeout bit,
-// and once that bit is set no later wait spins, so a lost partner costs one bound in total.
-__device__ __forceinline__ void exchange(unsigned* cnt, int s, unsigned c1, unsigned* status) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// The exchange memory of one head: counter words and the Z^K / Z^Q partial slots.
+struct XMem {
+  unsigned* cnt;
+  float* xz;
+  float* xq;
+  __amdgpu_buffer_rsrc_t fr, zr, qr;
+  bool local;  // all parts on one XCD
+};
+
+__device__ __forceinline__ unsigned cnt_load(const XMem& m, int i) {
+  if (m.local) return __builtin_amdgcn_raw_buffer_load_b32(m.fr, 0, 4 * i, kLoadL2);
+  return __hip_atomic_load(m.cnt + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publish the partial that every thread has just stored as chunk c (counter word base + s
+// := c + 1): the stores are complete before the counter store.
+__device__ __forceinline__ void publish(const XMem& m, int base, int s, unsigned c1) {
+  if (m.local)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_store(cnt + s, c1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (m.local)
+      __builtin_amdgcn_raw_buffer_store_b32(c1, m.fr, 0, 4 * (base + s), 0);
+    else
+      __hip_atomic_store(m.cnt + base + s, c1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait until the other parts' counters base + o reach c1. Bounded: an expired wait sets the
+// timeout bit, and once that bit is set no later wait spins, so a lost partner costs one
+// bound in total.
+__device__ __forceinline__ void wait_all(const XMem& m, int base, int s, unsigned c1, unsigned* status) {
+  if (threadIdx.x == 0) {
     bool late = (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout) != 0;
     for (int o = 0; o < S && !late; ++o) {
       if (o == s) continue;
       int it = 0;
-      while (__hip_atomic_load(cnt + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c1) {
+      while (cnt_load(m, base + o) < c1) {
         if (++it >= kSpinLimit) {
           late = true;
           atomicOr(status, kStatusTimeout);
@@ -145,7 +177,20 @@ __device__ __forceinline__ void exchange(unsigned* cnt, int s, unsigned c1, unsi
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (!m.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// one element of a partial slot area (float offset)
+__device__ __forceinline__ float part_load(const XMem& m, bool zq, int off) {
+  if (m.local)
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zq ? m.qr : m.zr, 4 * off, 0, kLoadL2));
+  return (zq ? m.xq : m.xz)[off];
+}
+__device__ __forceinline__ void part_store(const XMem& m, bool zq, int off, float v) {
+  if (m.local)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), zq ? m.qr : m.zr, 4 * off, 0, 0);
+  else
+    (zq ? m.xq : m.xz)[off] = v;
 }
 
 template <int GELU_KIND>
@@ -163,10 +208,35 @@ fwd_split_kernel(ScanParams p, Split x) {
   const int hb = s * (HID / S) + w * HS;
   const int T = p.T, nchunks = T / BC;
   const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
-  float* xz = x.xbuf + static_cast<size_t>(bh) * kHeadXFloats;  // [slot][S][16 x 128]
-  float* xq = xz + 2 * S * kPartFloats;
-  unsigned* cz = x.flags + static_cast<size_t>(bh) * kFlagWords;
-  unsigned* cq = cz + 8;
+  __shared__ unsigned sh_local;
+  XMem m;
+  m.xz = x.xbuf + static_cast<size_t>(bh) * kHeadXFloats;  // [slot][S][16 x 128]
+  m.xq = m.xz + 2 * S * kPartFloats;
+  m.cnt = x.flags + static_cast<size_t>(bh) * kFlagWords;
+  m.fr = __builtin_amdgcn_make_buffer_rsrc(m.cnt, 0, kFlagWords * 4, mfma::kBufFlags);
+  m.zr = __builtin_amdgcn_make_buffer_rsrc(m.xz, 0, 2 * S * kPartFloats * 4, mfma::kBufFlags);
+  m.qr = __builtin_amdgcn_make_buffer_rsrc(m.xq, 0, 2 * S * kPartFloats * 4, mfma::kBufFlags);
+  {
+    // placement: every part publishes its XCD id + 1 (device scope) and reads the others'
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(m.cnt + 16 + s, xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool same = true;
+      for (int o = 0; o < S; ++o) {
+        unsigned v = 0;
+        for (int it = 0; it < kSpinLimit && v == 0; ++it) {
+          v = __hip_atomic_load(m.cnt + 16 + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (v == 0) __builtin_amdgcn_s_sleep(1);
+        }
+        if (v == 0) atomicOr(p.status, kStatusTimeout);
+        same = same && v == xcc + 1;
+      }
+      sh_local = same ? 1u : 0u;
+    }
+    __syncthreads();
+    m.local = sh_local != 0;
+  }
 
   f4 W1c[NDT][NHT], W2c[NHT][NDT];
   {
@@ -221,17 +291,6 @@ fwd_split_kernel(ScanParams p, Split x) {
       o[i] = a;
     }
   };
-  // the head's total from the S partials of a slot (fixed part order)
-  auto total = [&](const float* slot, float (&z)[DPL]) {
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const int off = ln_t * D + 16 * i + c16;
-      float a = 0.f;
-#pragma unroll
-      for (int o = 0; o < S; ++o) a += __builtin_nontemporal_load(slot + o * kPartFloats + off);
-      z[i] = a;
-    }
-  };
   auto ln_stats8 = [&](const float (&z)[DPL], float& mu, float& rs) {
     float a = 0.f;
 #pragma unroll
@@ -241,6 +300,43 @@ fwd_split_kernel(ScanParams p, Split x) {
 #pragma unroll
     for (int i = 0; i < DPL; ++i) v += (z[i] - mu) * (z[i] - mu);
     rs = __builtin_amdgcn_rsqf(sum16(v) * (1.0f / D) + p.eps);
+  };
+  // store this part's partial of chunk parity `slot` (the LayerNorm lanes' elements)
+  auto put_own = [&](bool zq, int slot) {
+    float own[DPL];
+    own_partial(own);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) part_store(m, zq, (slot * S + s) * kPartFloats + ln_t * D + 16 * i + c16, own[i]);
+  };
+  // the head's total from the S partials of a slot (fixed part order)
+  auto total = [&](bool zq, int slot, float (&z)[DPL]) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int off = slot * S * kPartFloats + ln_t * D + 16 * i + c16;
+      float a = 0.f;
+#pragma unroll
+      for (int o = 0; o < S; ++o) a += part_load(m, zq, off + o * static_cast<int>(kPartFloats));
+      z[i] = a;
+    }
+  };
+  // output z = Q + LN(Z^Q) of chunk cc for this part's tokens (wave s: tokens 4 s .. 4 s + 3)
+  auto ln_out = [&](int cc) {
+    const Stage& So = sm.st[cc % 3];
+    const int t = ln_t;
+    float z[DPL];
+    total(true, cc & 1, z);
+    float mu, rs;
+    ln_stats8(z, mu, rs);
+    float chk = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int d = 16 * i + c16;
+      const float o = mfma::bf(So.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
+      chk += o;
+      Zg[static_cast<size_t>(cc * BC + t) * D + d] = (__bf16)o;
+    }
+    chk = sum16(chk);
+    if (c16 == 0) flag_nonfinite(p.status, chk);
   };
 
   {
@@ -252,7 +348,7 @@ fwd_split_kernel(ScanParams p, Split x) {
   __syncthreads();
 
   for (int c = 0; c < nchunks; ++c) {
-    Stage& St = sm.st[c & 1];
+    Stage& St = sm.st[c % 3];
     const int t0 = c * BC;
     const unsigned c1 = static_cast<unsigned>(c) + 1u;
     const int slot = c & 1;
@@ -317,19 +413,16 @@ fwd_split_kernel(ScanParams p, Split x) {
     for (int ks = 0; ks < NKD; ++ks) s1t = mfma32(aK[ks], aQ[ks], s1t);
     __syncthreads();
 
-    // ---- Z^K over all hidden units, LayerNorm forward/backward -> En2 ----
-    {
-      float own[DPL];
-      own_partial(own);
-      float* mine = xz + (slot * S + s) * kPartFloats;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) mine[ln_t * D + 16 * i + c16] = own[i];
-    }
-    exchange(cz, s, c1, p.status);
+    // ---- Z^K over all hidden units (this wait also covers the Z^Q partials of chunk c - 1,
+    // whose output is written now), LayerNorm forward/backward -> En2 ----
+    put_own(false, slot);
+    publish(m, 0, s, c1);
+    wait_all(m, 0, s, c1, p.status);
+    if (c > 0 && w == s) ln_out(c - 1);
     {
       const int t = ln_t;
       float z[DPL];
-      total(xz + slot * S * kPartFloats, z);
+      total(false, slot, z);
       float mu, rs;
       ln_stats8(z, mu, rs);
       float xh[DPL], gg[DPL], l2 = 0.f, sg = 0.f, sgx = 0.f;
@@ -358,7 +451,7 @@ fwd_split_kernel(ScanParams p, Split x) {
         flag_nonfinite(p.status, loss);
       }
     }
-    if (has_next) stage_write(sm.st[(c + 1) & 1], nk, nq, nv, ne);
+    if (has_next) stage_write(sm.st[(c + 1) % 3], nk, nq, nv, ne);
     __syncthreads();
 
     // ---- E1n = (En2 W2^T) (.) G ; H^Q ; A^Q ; Z^Q partial ----
@@ -411,33 +504,12 @@ fwd_split_kernel(ScanParams p, Split x) {
     }
     __syncthreads();
 
-    // ---- Z^Q over all hidden units; z = Q + LN(Z^Q) (part s writes tokens 4s .. 4s + 3) ----
-    {
-      float own[DPL];
-      own_partial(own);
-      float* mine = xq + (slot * S + s) * kPartFloats;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) mine[ln_t * D + 16 * i + c16] = own[i];
-    }
-    exchange(cq, s, c1, p.status);
-    if (w == s) {
-      const int t = ln_t;
-      float z[DPL];
-      total(xq + slot * S * kPartFloats, z);
-      float mu, rs;
-      ln_stats8(z, mu, rs);
-      float chk = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const int d = 16 * i + c16;
-        const float o = mfma::bf(St.Q[t * RS + d]) + gam[i] * (z[i] - mu) * rs + bet[i];
-        chk += o;
-        Zg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)o;
-      }
-      chk = sum16(chk);
-      if (c16 == 0) flag_nonfinite(p.status, chk);
-    }
+    // ---- publish this part's Z^Q partial of chunk c (its output is written next chunk) ----
+    put_own(true, slot);
+    publish(m, 8, s, c1);
   }
+  wait_all(m, 8, s, static_cast<unsigned>(nchunks), p.status);
+  if (w == s) ln_out(nchunks - 1);
 
   if (p.wt_1)
     w_store(p.wt_1 + static_cast<size_t>(bh) * D * HID, p.wt_2 + static_cast<size_t>(bh) * HID * D,
