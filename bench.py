@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "ttt_fwd_mfma_pair_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp"),
     "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp"),
     "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
+    "ttt_decode_stream_d64": ("ttt_decode_stream.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
 }
 
 
@@ -295,9 +296,11 @@ def bench_decode(args) -> dict:
     out = _base_record(args, f"TTT-MLP decode token*heads/s at d={w.d} ({heads} heads, one token "
                              "per head per call)", heads * b / (ms_step * 1e-3), ms_step,
                        w.with_(T=b), ops.decode_kernel_name(cfg), "f32")
+    kernel = ops.decode_kernel_name(cfg)
     out["roofline"] = {
         "bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
-        "frac": achieved / 8000.0, "traffic": None,
+        "frac": achieved / 8000.0,
+        "traffic": _traffic(kernel, heads) if kernel in KERNEL_SOURCES else None,
         "kernel_ms": statistics.fmean(kms), "kernel_ms_min": min(kms),
         "algorithmic_bytes_per_launch": bytes_step / b}
     if not args.no_cpu_baseline:
