@@ -16,6 +16,11 @@ What it computes (sources, by page title and section):
   devices are mini-batch TTT with b = 16, the dual form, a learnable W0 and a
   learnable per-token eta.
 * Same page, section "재현성과 공개 구현": the stabilising form f(x) = x + LN(f_res(x)).
+* "LLM : 빠른 논문 리뷰 : End-to-End Test-Time Training for Long Context", section 2.4.2,
+  Eq. 9 (the simplified output rule, an option here): the output reuses the key-side
+  prediction g(theta_K x_t; W_{t-1}) instead of evaluating f again on theta_Q x_t with the
+  updated weights. In the mini-batch scan the gradient of token t is taken at the chunk's
+  start weights, so the plain reading is z_t = f(K_t; W_start); with b = 1 that is W_{t-1}.
 * "LLM : 빠른 논문 리뷰 : End-to-End Test-Time Training for Long Context"
   (aiflower), section 2.3, Eq. 5: in a mini-batch all gradients are taken at the
   weights the mini-batch started from, and W is carried into the next mini-batch.
@@ -62,6 +67,8 @@ class OracleConfig:
     eta_scale: multiplies every per-token eta.
     layer_norm / residual: both True for the layer as defined; switching both off
         gives the plain map f(x) = g(x) used by the attention-equivalence checks.
+    output: "query" (Eq. 5/8: z_t = f(Q_t; W_t)) or "key" (Eq. 9 of the E2E review:
+        z_t = f(K_t; W_start), the prediction the token's loss is taken on).
     """
 
     kind: str = "mlp"
@@ -71,6 +78,7 @@ class OracleConfig:
     eta_scale: float = 1.0
     layer_norm: bool = True
     residual: bool = True
+    output: str = "query"
 
 
 # ----------------------------------------------------------------------------
@@ -179,7 +187,7 @@ def scan(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig):
         grad_t = grad l_t(W_start)                     (all gradients at the chunk start)
         P     += eta_scale * eta_t * grad_t            (running sum, t included)
         W_t    = W_start - P                           (materialised)
-        z_t    = f(Q_t; W_t)
+        z_t    = f(Q_t; W_t)         (output "key": z_t = f(K_t; W_start))
       carry W_start <- W_start - P.
     Returns Z [N, T, d], the final weights (tuple) and the per-token loss [N, T]
     l_t(W_start) (the reconstruction loss at the weights the gradient is taken at).
@@ -198,8 +206,13 @@ def scan(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig):
             loss, grads = token_loss_and_grad(K[:, t], V[:, t], W_start, gamma, beta, cfg)
             step = cfg.eta_scale * eta[:, t].reshape(N, 1, 1)
             P = tuple(p + step * gw for p, gw in zip(P, grads))
-            W_t = tuple(ws - p for ws, p in zip(W_start, P))
-            Z.append(f_apply(Q[:, t], W_t, gamma, beta, cfg))
+            if cfg.output == "key":
+                Z.append(f_apply(K[:, t], W_start, gamma, beta, cfg))
+            elif cfg.output == "query":
+                W_t = tuple(ws - p for ws, p in zip(W_start, P))
+                Z.append(f_apply(Q[:, t], W_t, gamma, beta, cfg))
+            else:
+                raise ValueError(cfg.output)
             losses.append(loss)
         W = tuple(ws - p for ws, p in zip(W_start, P))
     return torch.stack(Z, dim=1), W, torch.stack(losses, dim=1)
@@ -223,7 +236,9 @@ def scan_outer_grads(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig,
     if dW_T is not None:
         for w, dw in zip(W_T, dW_T):
             L = L + (w * dw).sum()
-    grads = torch.autograd.grad(L, leaves + Wl)
+    # (with the Eq. 9 output rule Q is not read: its gradient is zero)
+    grads = torch.autograd.grad(L, leaves + Wl, allow_unused=True)
+    grads = [torch.zeros_like(x) if gr is None else gr for gr, x in zip(grads, leaves + Wl)]
     return {
         "dQ": grads[0], "dK": grads[1], "dV": grads[2], "deta": grads[3],
         "dgamma": grads[4], "dbeta": grads[5], "dW0": tuple(grads[6:]),

@@ -376,6 +376,94 @@ def test_outer_grads_finite_differences(kind):
 
 
 # ---------------------------------------------------------------------------
+# The simplified output rule (E2E paper review, section 2.4.2, Eq. 9)
+# ---------------------------------------------------------------------------
+
+def lib_scan_key_output(K, V, eta, W0, gamma, beta, kind, b, eps, eta_scale=1.0):
+    """z_t = f(K_t; W) with W the weights the token's gradient is taken at (the chunk start;
+    W_{t-1} when b = 1), gradients by autograd through the library layer, one head at a time."""
+    N, T, d = K.shape
+    Zs = []
+    for n in range(N):
+        W = [w[n].clone() for w in W0]
+        zs = []
+        for c0 in range(0, T, b):
+            Wstart = [w.clone().requires_grad_(True) for w in W]
+            P = [torch.zeros_like(w) for w in W]
+            for t in range(c0, c0 + b):
+                pred = lib_f(K[n, t], Wstart, gamma[n], beta[n], kind, eps)
+                zs.append(pred.detach())
+                gr = torch.autograd.grad(((pred - V[n, t]) ** 2).sum(), Wstart)
+                P = [p + eta_scale * eta[n, t] * gw for p, gw in zip(P, gr)]
+            W = [ws.detach() - p for ws, p in zip(Wstart, P)]
+        Zs.append(torch.stack(zs))
+    return torch.stack(Zs)
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+@pytest.mark.parametrize("b", [1, 4])
+def test_key_output_matches_library_loop(kind, b):
+    d, h, T = 4, 16, 12
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=30 + b)
+    cfg = OracleConfig(kind=kind, chunk=b, output="key", ln_eps=1e-5, eta_scale=0.5)
+    Z, _, _ = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    Zr = lib_scan_key_output(K, V, eta, W0, gamma, beta, kind, b, 1e-5, eta_scale=0.5)
+    assert rel(Z, Zr) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_key_output_is_the_loss_prediction(kind):
+    """With the Eq. 9 rule the output is the prediction the token's loss is taken on:
+    l_t = ||z_t - V_t||^2 exactly; the weights do not depend on the output rule; Q is not read."""
+    d, h, T = 8, 32, 32
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, T, d, h, kind, seed=33)
+    cfg_k = OracleConfig(kind=kind, chunk=8, output="key")
+    Z, WT, loss = scan(Q, K, V, eta, W0, gamma, beta, cfg_k)
+    assert torch.allclose(((Z - V) ** 2).sum(-1), loss, rtol=1e-13, atol=0)
+    Z2, WT2, _ = scan(torch.full_like(Q, float("nan")), K, V, eta, W0, gamma, beta, cfg_k)
+    assert torch.equal(Z, Z2)
+    _, WTq, _ = scan(Q, K, V, eta, W0, gamma, beta, OracleConfig(kind=kind, chunk=8))
+    for a, b_, c in zip(WT, WTq, WT2):
+        assert torch.equal(a, b_) and torch.equal(a, c)
+
+
+def test_key_output_outer_grads_finite_differences():
+    N, T, d, h, b = 1, 32, 4, 16, 8
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(N, T, d, h, "mlp", seed=34, w_scale=0.4)
+    g = torch.Generator().manual_seed(35)
+    dZ = torch.randn(N, T, d, generator=g, dtype=DT)
+    cfg = OracleConfig(kind="mlp", chunk=b, ln_eps=1e-5, output="key")
+    grads = scan_outer_grads(Q, K, V, eta, W0, gamma, beta, cfg, dZ)
+    assert grads["dQ"].abs().max().item() == 0.0
+
+    def L(Kx, Vx, ex, Wx):
+        Z, _, _ = scan(Q, Kx, Vx, ex, Wx, gamma, beta, cfg)
+        return (Z * dZ).sum().item()
+
+    for name in ("K", "V", "eta", "W0_0", "W0_1"):
+        for _ in range(4):
+            args = dict(K=K, V=V, eta=eta)
+            Ws = list(W0)
+            if name.startswith("W0"):
+                i = int(name[3:])
+                u = torch.randn(W0[i].shape, generator=g, dtype=DT)
+                an = (grads["dW0"][i] * u).sum().item()
+            else:
+                u = torch.randn(args[name].shape, generator=g, dtype=DT)
+                an = (grads["d" + name] * u).sum().item()
+            vals = []
+            for s_ in (1e-6, -1e-6):
+                a2, W2 = dict(args), list(Ws)
+                if name.startswith("W0"):
+                    W2[i] = W0[i] + s_ * u
+                else:
+                    a2[name] = args[name] + s_ * u
+                vals.append(L(a2["K"], a2["V"], a2["eta"], tuple(W2)))
+            fd = (vals[0] - vals[1]) / 2e-6
+            assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), (name, an, fd)
+
+
+# ---------------------------------------------------------------------------
 # The seeded input generator (shared by both sides)
 # ---------------------------------------------------------------------------
 
