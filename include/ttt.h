@@ -77,8 +77,13 @@ enum { TTT_GELU_ERF = 0, TTT_GELU_TANH = 1 };
 enum {
   TTT_W0_PER_SEQ = 1 << 0,    /* W0 (and dW0) are [B, H, ...] instead of [H, ...]         */
   TTT_FORCE_GENERIC = 1 << 1, /* use the portable fp32 kernel even where a tuned one exists */
-  TTT_ONE_WG_PER_HEAD = 1 << 2 /* tuned forward: one workgroup per (batch, head) instead of a
-                                  producer/consumer pair of workgroups                      */
+  TTT_ONE_WG_PER_HEAD = 1 << 2, /* tuned forward: one workgroup per (batch, head) instead of a
+                                   producer/consumer pair of workgroups                      */
+  TTT_OUTPUT_KEY = 1 << 3 /* output rule of Eq. 9 in the E2E paper review, section 2.4.2:
+                             z_t = f(K_t; W) with W the weights the token's gradient is taken at
+                             (the chunk start; W_{t-1} when chunk = 1), i.e. the key-side
+                             prediction reused as the output. Q does not enter it (dQ = 0). Runs on
+                             the portable kernels. */
 };
 /* op codes for ttt_workspace_size */
 enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2 };

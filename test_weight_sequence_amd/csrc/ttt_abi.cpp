@@ -23,7 +23,8 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   if (c->kind != TTT_LINEAR && c->kind != TTT_MLP) return TTT_ERR_UNSUPPORTED;
   if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
   if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH) return TTT_ERR_UNSUPPORTED;
-  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD)) return TTT_ERR_ARG;
+  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD | TTT_OUTPUT_KEY))
+    return TTT_ERR_ARG;
   if (c->B < 1 || c->H < 1 || c->d < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
   if (need_T && c->T < 1) return TTT_ERR_SHAPE;
   if (c->d < 16 || c->d > 128 || c->d % 16 != 0) return TTT_ERR_UNSUPPORTED;
@@ -61,8 +62,12 @@ ScanParams scan_params(const ttt_config* c) {
   return p;
 }
 
+// The tuned kernels implement the default output rule only; TTT_OUTPUT_KEY runs on the
+// portable ones.
+bool tuned_allowed(const ttt_config* c) { return !(c->flags & (TTT_FORCE_GENERIC | TTT_OUTPUT_KEY)); }
+
 bool use_mfma(const ttt_config* c) {
-  if (c->flags & TTT_FORCE_GENERIC) return false;
+  if (!tuned_allowed(c)) return false;
   ScanParams p = scan_params(c);
   return fwd_mfma_supported(p);
 }
@@ -73,7 +78,7 @@ bool use_pair(const ttt_config* c) {
 }
 
 bool use_split(const ttt_config* c) {
-  if (c->flags & TTT_FORCE_GENERIC) return false;
+  if (!tuned_allowed(c)) return false;
   ScanParams p = scan_params(c);
   return fwd_split_supported(p);
 }
@@ -88,7 +93,7 @@ size_t fwd_ws_bytes(const ttt_config* c) {
 }
 
 bool use_bwd_mfma(const ttt_config* c) {
-  if (c->flags & TTT_FORCE_GENERIC) return false;
+  if (!tuned_allowed(c)) return false;
   BwdParams p{};
   p.kind = c->kind;
   p.d = c->d;
@@ -99,7 +104,7 @@ bool use_bwd_mfma(const ttt_config* c) {
 }
 
 bool use_decode_stream(const ttt_config* c) {
-  if (c->flags & TTT_FORCE_GENERIC) return false;
+  if (!tuned_allowed(c)) return false;
   DecodeParams p{};
   p.kind = c->kind;
   p.d = c->d;

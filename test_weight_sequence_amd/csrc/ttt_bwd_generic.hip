@@ -17,6 +17,9 @@
 //   P2 = tril(AQ AK^T); ZQ = AQ W2 - P2 E2; z = Q + gamma xq + beta
 //   W1' = W1 - K^T E1;  W2' = W2 - AK^T E2
 // (Linear: ZK = K W, E = eta' d2, ZQ = Q W - P1 E, W' = W - K^T E.)
+// With TTT_OUTPUT_KEY (Eq. 9 of the E2E paper review, section 2.4.2) the output is
+// z = K + gamma xk + beta: dz reaches dK directly and ZK through the first-order LayerNorm
+// backward, and the query side gets a zero adjoint (dQ = 0).
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -80,6 +83,7 @@ __global__ void __launch_bounds__(NT) bwd_generic_kernel(BwdParams p) {
   const float g0 = lane < d ? gam[lane] : 0.f, g1 = lane + 64 < d ? gam[lane + 64] : 0.f;
   const float b0 = lane < d ? bet[lane] : 0.f, b1 = lane + 64 < d ? bet[lane + 64] : 0.f;
   const bool h0 = lane < d, h1 = lane + 64 < d;
+  const bool key_out = (p.flags & TTT_OUTPUT_KEY) != 0;
   float dgam0 = 0.f, dgam1 = 0.f, dbet0 = 0.f, dbet1 = 0.f;
 
   for (size_t i = tid; i < nW1; i += NT) dW1[i] = p.dwt_1 ? p.dwt_1[bh * nW1 + i] : 0.f;
@@ -290,8 +294,19 @@ __global__ void __launch_bounds__(NT) bwd_generic_kernel(BwdParams p) {
     __syncthreads();
 
     // ================= backward =================
-    // LN(Q) and the output: dQ = dO, dgamma/dbeta, dZQ
+    // LN(Q) and the output: dQ = dO, dgamma/dbeta, dZQ (zero with the key-side output)
     for (int t = wave; t < b; t += NT / 64) {
+      if (key_out) {
+        if (h0) {
+          s.DZQ[t * d + lane] = 0.f;
+          s.DQ[t * d + lane] = 0.f;
+        }
+        if (h1) {
+          s.DZQ[t * d + lane + 64] = 0.f;
+          s.DQ[t * d + lane + 64] = 0.f;
+        }
+        continue;
+      }
       const float z0 = h0 ? s.XQ[t * d + lane] : 0.f, z1 = h1 ? s.XQ[t * d + lane + 64] : 0.f;
       const float mu = row_mean(z0, z1, d);
       const float c0 = h0 ? z0 - mu : 0.f, c1 = h1 ? z1 - mu : 0.f;
@@ -496,15 +511,27 @@ __global__ void __launch_bounds__(NT) bwd_generic_kernel(BwdParams p) {
       dbet1 += dr1;
       dx0 += g0 * dr0;
       dx1 += g1 * dr1;
+      // key-side output z = K + gamma xk + beta: its adjoint dO enters through the LayerNorm
+      float o0 = 0.f, o1 = 0.f;
+      if (key_out) {
+        o0 = h0 ? s.dO[t * d + lane] : 0.f;
+        o1 = h1 ? s.dO[t * d + lane + 64] : 0.f;
+        dgam0 += o0 * x0;
+        dgam1 += o1 * x1;
+        dbet0 += o0;
+        dbet1 += o1;
+        dx0 += g0 * o0;
+        dx1 += g1 * o1;
+      }
       const float mdx = row_mean(dx0, dx1, d), mdxx = row_mean(dx0 * x0, dx1 * x1, d);
       if (h0) {
         s.DZK[t * d + lane] = rs * (dx0 - mdx - x0 * mdxx) + ds * x0 / d;
-        s.DK[t * d + lane] += dr0;
+        s.DK[t * d + lane] += dr0 + o0;
         s.DV[t * d + lane] = -dr0;
       }
       if (h1) {
         s.DZK[t * d + lane + 64] = rs * (dx1 - mdx - x1 * mdxx) + ds * x1 / d;
-        s.DK[t * d + lane + 64] += dr1;
+        s.DK[t * d + lane + 64] += dr1 + o1;
         s.DV[t * d + lane + 64] = -dr1;
       }
       if (lane == 0) p.deta[static_cast<size_t>(bh) * T + t0 + t] = deta;

@@ -4,6 +4,8 @@
 // current token, exactly as the scan does, and a step commits when the chunk is
 // full (E2E paper review, section 2.3.2: "take a gradient step only when the decoded
 // tokens fill a mini-batch"). Memory-bound: it streams W_start and acc once or twice.
+// With TTT_OUTPUT_KEY (Eq. 9 of the same review, section 2.4.2) z = f(k; W_start), the
+// key-side prediction of the LayerNorm step, and q does not enter the output.
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -29,6 +31,7 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeParams p) {
   float* P1 = p.acc_1 + bh * nW1;
   float* P2 = KIND == TTT_MLP ? p.acc_2 + bh * nW2 : nullptr;
   const bool commit = p.pos == p.chunk - 1;
+  const bool key_out = (p.flags & TTT_OUTPUT_KEY) != 0;
   const float* gam = p.gamma + static_cast<size_t>(hidx) * d;
   const float* bet = p.beta + static_cast<size_t>(hidx) * d;
 
@@ -89,6 +92,11 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeParams p) {
     if (h0) sE[lane] = sEta * (gg0 - mg - x0 * mgx) * rs;
     if (h1) sE[lane + 64] = sEta * (gg1 - mg - x1 * mgx) * rs;
     if (lane == 0) flag_nonfinite(p.status, loss);
+    if (key_out) {
+      IO* zo = static_cast<IO*>(p.z) + static_cast<size_t>(bh) * d;
+      if (h0) zo[lane] = from_f32<IO>(r0 + sv[lane]);
+      if (h1) zo[lane + 64] = from_f32<IO>(r1 + sv[lane + 64]);
+    }
   }
   __syncthreads();
 
@@ -153,7 +161,7 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeParams p) {
     }
     __syncthreads();
   }
-  if (wave == 0) {
+  if (wave == 0 && !key_out) {
     const bool h0 = lane < d, h1 = lane + 64 < d;
     const float z0 = h0 ? sZ[lane] : 0.f, z1 = h1 ? sZ[lane + 64] : 0.f;
     const float mu = wave_sum(z0 + z1) / d;

@@ -16,6 +16,9 @@
 // mini-batch rule from the E2E paper review, section 2.3, Eq. 5).
 // TTT-Linear drops the hidden layer: Z^K = K W, E = eta (.) delta, Z^Q = Q W - tril(Q K^T) E,
 // W -= K^T E.
+// With TTT_OUTPUT_KEY (the simplified output rule, E2E paper review section 2.4.2, Eq. 9)
+// the output is the key-side prediction at the chunk-start weights, z = K + LN(Z^K), and
+// the query side (H^Q, Z^Q) is skipped.
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -81,6 +84,7 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
   float* W1 = p.wbuf + static_cast<size_t>(bh) * nW;
   float* W2 = W1 + nW1;
   const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
+  const bool key_out = (p.flags & TTT_OUTPUT_KEY) != 0;
   const size_t w0_head = per_seq ? static_cast<size_t>(bh) : static_cast<size_t>(hidx);
   for (size_t i = tid; i < nW1; i += NT) W1[i] = p.w0_1[w0_head * nW1 + i];
   for (size_t i = tid; i < nW2; i += NT) W2[i] = p.w0_2[w0_head * nW2 + i];
@@ -194,9 +198,15 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
         if (p.loss) p.loss[static_cast<size_t>(bh) * p.T + t0 + t] = loss;
         flag_nonfinite(p.status, loss);
       }
+      if (key_out) {
+        // z = f(K; W_start) = K + LN(Z^K) = r + V
+        if (lane < d) Zg[static_cast<size_t>(t0 + t) * d + lane] = from_f32<IO>(r0 + s.V[t * d + lane]);
+        if (lane + 64 < d)
+          Zg[static_cast<size_t>(t0 + t) * d + lane + 64] = from_f32<IO>(r1 + s.V[t * d + lane + 64]);
+      }
     }
     // S = tril(Q K^T) (eta is carried by the E rows)
-    for (int i = tid; i < b * b; i += NT) {
+    for (int i = tid; i < b * b && !key_out; i += NT) {
       const int t = i / b, u = i % b;
       float acc = 0.f;
       if (u <= t)
@@ -226,6 +236,7 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
           if (t < b) s.G[t * h + j] *= acc[t];
       }
       __syncthreads();
+      if (!key_out) {
       // ---- H^Q = Q W1 - S E1, A^Q = GELU(H^Q) ----
       for (int j = tid; j < h; j += NT) {
         float acc[MAXB];
@@ -283,7 +294,8 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
           }
         }
       }
-    } else {
+      }  // !key_out
+    } else if (!key_out) {
       // ---- Z^Q = Q W - S E ----
       if (grp < ngrp) {
         float acc[MAXB];
@@ -311,7 +323,7 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
     __syncthreads();
 
     // ---- output: z = Q + LN(Z^Q) ----
-    for (int t = wave; t < b; t += NT / 64) {
+    for (int t = wave; t < b && !key_out; t += NT / 64) {
       const float z0 = lane < d ? s.ZQ[t * d + lane] : 0.f;
       const float z1 = lane + 64 < d ? s.ZQ[t * d + lane + 64] : 0.f;
       RowLN ln = ln_row(z0, z1, lane, d, p.eps);

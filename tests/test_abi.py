@@ -104,6 +104,11 @@ def test_kernel_selection_names():
     assert ops.bwd_kernel_name(cfg3(T=7)) == ""
     assert ops.decode_kernel_name(cfg3()) == "ttt_decode_stream_d64"
     assert ops.decode_kernel_name(cfg3(force_generic=True)) == "ttt_decode_generic"
+    # the Eq. 9 output rule runs on the portable kernels
+    assert ops.fwd_kernel_name(cfg3(output_key=True)) == "ttt_fwd_generic"
+    assert ops.bwd_kernel_name(cfg3(output_key=True)) == "ttt_bwd_generic"
+    assert ops.decode_kernel_name(cfg3(output_key=True)) == "ttt_decode_generic"
+    assert ops.validate(cfg3(output_key=True)) == 0
 
 
 class _FakeTensor:

@@ -90,6 +90,30 @@ def test_bwd_fp32_matches_oracle_autograd(kind, d, chunk, T, per_seq, with_dwt, 
     _compare(gpu, ora, TOL["f32"])
 
 
+@pytest.mark.parametrize("kind,d,chunk,T", [("mlp", 16, 16, 64), ("linear", 32, 8, 32),
+                                           ("mlp", 64, 16, 48)])
+def test_bwd_key_output_matches_oracle(kind, d, chunk, T):
+    """Outer-loop gradients with the Eq. 9 output rule through the portable backward: dz
+    reaches K directly and through the first LayerNorm; dQ is exactly zero."""
+    B, H = 2, 2
+    inp, dZ, dWT = _rand_case(kind, B, H, T, d, "f32", seed=d + T + 1, per_seq=False)
+    cfg = ops.Config(kind=kind, B=B, H=H, T=T, d=d, hidden=4 * d, chunk=chunk, io="f32",
+                     output_key=True, eta_scale=0.5)
+    assert ops.bwd_kernel_name(cfg) == "ttt_bwd_generic"
+    note(f"bwd key output {cfg}")
+    dv = to_dev(inp)
+    _, gpu = _gpu_grads(cfg, dv, dZ.cuda(), tuple(w.cuda() for w in dWT))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gpu["dQ"]).item() == 0
+    ora = _oracle_grads(inp, dZ, dWT, kind, chunk, False, eta_scale=0.5, output="key")
+    assert torch.count_nonzero(ora["dQ"]).item() == 0
+    for k in ("dK", "dV", "deta", "dgamma", "dbeta"):
+        e = rel_l2(gpu[k], ora[k])
+        assert e <= TOL["f32"], (k, e)
+    for i, (a, b) in enumerate(zip(gpu["dW0"], ora["dW0"])):
+        assert rel_l2(a, b) <= TOL["f32"], ("dW0", i)
+
+
 def test_bwd_cfg1_fp32_full_T():
     w = WORKLOADS[1]
     inp = make_inputs(w, with_dz=True)

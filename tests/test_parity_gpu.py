@@ -386,6 +386,34 @@ def test_decode_stream_equals_oracle(io, gelu):
             assert torch.count_nonzero(a).item() == 0
 
 
+@pytest.mark.parametrize("wid,kind", [(1, "mlp"), (2, "linear"), (3, "mlp")])
+def test_key_output_forward_and_decode(wid, kind):
+    """The Eq. 9 output rule (z_t = f(K_t; W at the chunk start)) through the portable forward
+    and the portable decode, against the oracle with the same rule; the per-token loss equals
+    ||z_t - V_t||^2 up to the output rounding."""
+    w = WORKLOADS[wid]
+    T = 64
+    bi, hi = [0], ([0, 1] if w.H > 1 else [0])
+    inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
+    B, H = len(bi), len(hi)
+    cfg = ops_config(w, T=T, B=B, H=H, output_key=True)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_generic"
+    note(f"key output cfg{wid}")
+    d = to_dev(inp)
+    res = _run(cfg, d, want_loss=True)
+    torch.cuda.synchronize()
+    pairs = [(0, h) for h in range(H)]
+    _check_heads(res, inp, pairs, w, TOL[w.io], cfg_kw=dict(output="key"))
+    Ws = tuple(x.unsqueeze(0).expand(B, *x.shape).contiguous().clone() for x in d["W0"])
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
+                          _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t % w.chunk)
+          for t in range(T)]
+    assert rel_l2(torch.stack(zs, dim=2), res["Z"]) <= TOL[w.io]
+    for a, b in zip(Ws, res["W_T"]):
+        assert rel_l2(a, b) <= TOL["f32"]
+
+
 def test_scan_then_decode_continues_the_sequence():
     """Prefill T0 tokens with the scan, decode the rest: equals the oracle on all T."""
     w = WORKLOADS[1]
