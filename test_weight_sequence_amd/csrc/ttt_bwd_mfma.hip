@@ -103,6 +103,25 @@ __device__ __forceinline__ bf16x4 tr(bf16x4 x, bf16x4 I4) { return cvt4(mfma16(x
 // k-step ks over a wave's hidden slice from an array of [.. x h] tiles
 __device__ __forceinline__ bf16x8 hcat(const bf16x4 (&x)[NHT], int ks) { return cat(x[2 * ks], x[2 * ks + 1]); }
 
+// The chunk-start weights of one wave in the transposed tile orientations: W1^T tiles
+// (C[h][d]: lane holds W1[d][h .. h+3], four consecutive hidden units of one row) and W2^T
+// tiles (C[d][h]: lane holds W2[h][d .. d+3]), so every lane reads 16 contiguous bytes per
+// tile from the row-major [d][h] / [h][d] saved copy.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void wT_load(const float* w1, const float* w2, int g, int c16, int hs,
+                                        f4 (&W1T)[NHT][NDT], f4 (&W2T)[NDT][NHT]) {
+  const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w1), 0, D * HID * 4, kBufFlags);
+  const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w2), 0, D * HID * 4, kBufFlags);
+  const int v1 = (c16 * HID + hs + 4 * g) * 4, v2 = ((hs + c16) * D + 4 * g) * 4;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      W1T[ht][dt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r1, v1, (16 * dt * HID + 16 * ht) * 4, 0));
+      W2T[dt][ht] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r2, v2, (16 * ht * D + 16 * dt) * 4, 0));
+    }
+}
+
 // rows of a [token][d] LDS array as the A operand of a contraction over d (permuted k order)
 __device__ __forceinline__ void rows2(const __bf16* a, int c16, int g, bf16x8 (&o)[2]) {
 #pragma unroll
@@ -240,18 +259,26 @@ bwd_mfma_kernel(BwdParams p) {
     float ne = 0.f;
     if (has_next) gload(c - 1, nk, nq, nv, nz, ne);
 
-    // this chunk's start weights, as bf16 operand tiles
-    bf16x4 W1b[NDT][NHT], W2b[NHT][NDT];
+    // this chunk's start weights, as bf16 operand tiles in both orientations: the transposed
+    // ones straight from memory, the others by one identity transpose each
+    bf16x4 W1b[NDT][NHT], W2b[NHT][NDT], W1T[NHT][NDT], W2T[NDT][NHT];
     {
-      f4 Wn1[NDT][NHT], Wn2[NHT][NDT];
-      wtiles_load<NHT>(saved + static_cast<size_t>(c) * 2 * D * HID,
-                       saved + static_cast<size_t>(c) * 2 * D * HID + D * HID, g, c16, hs, Wn1, Wn2);
+      f4 Wn1[NHT][NDT], Wn2[NDT][NHT];
+      wT_load(saved + static_cast<size_t>(c) * 2 * D * HID,
+              saved + static_cast<size_t>(c) * 2 * D * HID + D * HID, g, c16, hs, Wn1, Wn2);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-          W1b[dt][ht] = cvt4(Wn1[dt][ht]);
-          W2b[ht][dt] = cvt4(Wn2[ht][dt]);
+          W1T[ht][dt] = cvt4(Wn1[ht][dt]);
+          W2T[dt][ht] = cvt4(Wn2[dt][ht]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          W1b[dt][ht] = tr(W1T[ht][dt], I4);
+          W2b[ht][dt] = tr(W2T[dt][ht], I4);
         }
     }
 
@@ -362,7 +389,7 @@ bwd_mfma_kernel(BwdParams p) {
       f4 ga = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        ga = mfma32(aE[ks], cat(tr(W2b[ht][2 * ks], I4), tr(W2b[ht][2 * ks + 1], I4)), ga);
+        ga = mfma32(aE[ks], cat(W2T[2 * ks][ht], W2T[2 * ks + 1][ht]), ga);
       e1R[ht] = cvt4(ga * wide(gk[ht]));
       gg2[ht] = cvt4(ga * wide(gk2[ht]));
     }
@@ -476,7 +503,7 @@ bwd_mfma_kernel(BwdParams p) {
       f4 da = mfma16(dp2ta, akR[ht], zero4());
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        da = mfma32(aZ[ks], cat(tr(W2b[ht][2 * ks], I4), tr(W2b[ht][2 * ks + 1], I4)), da);
+        da = mfma32(aZ[ks], cat(W2T[2 * ks][ht], W2T[2 * ks + 1][ht]), da);
       dhqR[ht] = cvt4(da * wide(gq[ht]));
       // dAK, first two terms: dP2^T AQ + E2 dW2'^T
       f4 a2 = mfma16(dp2a, aqR[ht], zero4());
@@ -517,7 +544,7 @@ bwd_mfma_kernel(BwdParams p) {
       for (int ks = 0; ks < NKH; ++ks) {
         de2 = mfma32(hcat(dgT, ks), cat(W2b[2 * ks][dt], W2b[2 * ks + 1][dt]), de2);
         de2 = mfma32(hcat(akT, ks), cat(cvt4(dW2c[2 * ks][dt]), cvt4(dW2c[2 * ks + 1][dt])), de2);
-        dq = mfma32(hcat(dhqT, ks), cat(tr(W1b[dt][2 * ks], I4), tr(W1b[dt][2 * ks + 1], I4)), dq);
+        dq = mfma32(hcat(dhqT, ks), cat(W1T[2 * ks][dt], W1T[2 * ks + 1][dt]), dq);
         dk = mfma32(hcat(e1T, ks),
                     cat(tr(cvt4(dW1c[dt][2 * ks]), I4), tr(cvt4(dW1c[dt][2 * ks + 1]), I4)), dk);
       }
@@ -613,7 +640,7 @@ bwd_mfma_kernel(BwdParams p) {
       f4 da = dak[ht];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        da = mfma32(aZK[ks], cat(tr(W2b[ht][2 * ks], I4), tr(W2b[ht][2 * ks + 1], I4)), da);
+        da = mfma32(aZK[ks], cat(W2T[2 * ks][ht], W2T[2 * ks + 1][ht]), da);
       dhkR[ht] = cvt4(dhk[ht] + da * wide(gk[ht]));
     }
 #pragma unroll
@@ -623,7 +650,7 @@ bwd_mfma_kernel(BwdParams p) {
       f4 dk = get_tile(sm.red[2], w, dt, lane);
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks)
-        dk = mfma32(hcat(dhkT, ks), cat(tr(W1b[dt][2 * ks], I4), tr(W1b[dt][2 * ks + 1], I4)), dk);
+        dk = mfma32(hcat(dhkT, ks), cat(W1T[2 * ks][dt], W1T[2 * ks + 1][dt]), dk);
       if (dt == w) {
         // the terms not split over hidden units, one d tile per wave: the residual and
         // dP1^T Q into dK, dz and dP1 K into dQ
