@@ -175,8 +175,9 @@ ttt_status ttt_reset_status(void* workspace, void* stream);
  * TTT_ONE_WG_PER_HEAD is not set; if the device then cannot hold all 2*ceil(B*H/8)*8
  * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. For MLP d = 128,
  * hidden = 512, chunk 16, bf16 I/O the name is "ttt_fwd_mfma_split_d128" (four workgroups per
- * head); if the device cannot hold all 4*ceil(B*H/8)*8 of them at once, ttt_scan_fwd launches
- * "ttt_fwd_generic" instead. */
+ * head that wait for each other); ttt_scan_fwd launches it once per group of heads whose
+ * workgroups the device holds at once (64 heads on a 256-CU device), and launches
+ * "ttt_fwd_generic" instead only if not even eight heads fit. */
 const char* ttt_fwd_kernel_name(const ttt_config* cfg);
 
 /* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */

@@ -87,7 +87,8 @@ __device__ __forceinline__ int prot(int r, int lane) { return (lane + 16 * r) & 
 struct Split {
   float* xbuf;        // exchange areas, kHeadXFloats per head
   unsigned* flags;    // kFlagWords per head
-  int nheads;
+  int nheads;         // heads in the whole call
+  int head0;          // first head of this launch (heads are launched in groups the device holds)
 };
 
 // fp32 weight tiles of one wave: W1[:, hb:hb+32] as [d tile][h tile], W2[hb:hb+32, :] as
@@ -200,7 +201,7 @@ fwd_split_kernel(ScanParams p, Split x) {
   // block -> (head, part): the S parts of a head are 8 blocks apart (same XCD)
   const int b = blockIdx.x;
   const int s = (b >> 3) % S;
-  const int bh = ((b >> 3) / S) * 8 + (b & 7);
+  const int bh = x.head0 + ((b >> 3) / S) * 8 + (b & 7);
   if (bh >= x.nheads) return;  // all parts of a missing head leave together
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -533,13 +534,14 @@ size_t fwd_split_workspace_bytes(int nheads) {
 
 int fwd_split_blocks(int nheads) { return (nheads + 7) / 8 * 8 * S; }
 
-// Whether the current device can hold every workgroup of the launch at once (the parts of a
-// head wait for each other). The answer is cached per device ordinal.
-bool fwd_split_fits(int nheads) {
+// Resident workgroups of the split kernel on the current device (0 when it cannot launch
+// cooperatively). The parts of a head wait for each other, so one launch may hold at most
+// this many workgroups. Cached per device ordinal.
+static int split_capacity() {
   constexpr int kMaxDev = 64;
   static int cap[kMaxDev];  // 0 = unknown, else 1 + resident workgroups on the device
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
   if (cap[dev] == 0) {
     int coop = 0, ncu = 0, per_cu = 0;
     const bool ok =
@@ -549,11 +551,19 @@ bool fwd_split_fits(int nheads) {
             &per_cu, reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_ERF>), NT, 0) == hipSuccess;
     cap[dev] = 1 + ((ok && coop) ? ncu * per_cu : 0);
   }
-  return fwd_split_blocks(nheads) <= cap[dev] - 1;
+  return cap[dev] - 1;
 }
+
+// Heads per launch: whole groups of eight heads whose S parts all fit on the device at once.
+static int split_heads_per_launch() { return split_capacity() / (8 * S) * 8; }
+
+// Whether the split kernel can run at all here (at least one group of eight heads fits).
+bool fwd_split_fits(int) { return split_heads_per_launch() > 0; }
 
 hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t stream) {
   const int nheads = p.B * p.H;
+  const int per = split_heads_per_launch();
+  if (per <= 0) return hipErrorCooperativeLaunchTooLarge;
   Split x;
   x.xbuf = p.wbuf;
   x.flags = reinterpret_cast<unsigned*>(p.wbuf + static_cast<size_t>(nheads) * kHeadXFloats);
@@ -562,11 +572,18 @@ hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(split_reset_kernel, dim3((nflags + 255) / 256), dim3(256), 0, stream, x.flags, nflags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  ScanParams pc = p;
-  void* args[] = {&pc, &x};
   const void* fn = p.gelu == TTT_GELU_TANH ? reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_TANH>)
                                            : reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_ERF>);
-  return hipLaunchCooperativeKernel(fn, dim3(fwd_split_blocks(nheads)), dim3(NT), args, 0, stream);
+  // heads are independent: launch them in groups the device holds at once, in order
+  for (int h0 = 0; h0 < nheads; h0 += per) {
+    ScanParams pc = p;
+    x.head0 = h0;
+    void* args[] = {&pc, &x};
+    const int n = nheads - h0 < per ? nheads - h0 : per;
+    e = hipLaunchCooperativeKernel(fn, dim3(fwd_split_blocks(n)), dim3(NT), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ttt

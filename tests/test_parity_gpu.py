@@ -152,6 +152,21 @@ def test_split_partial_group_tanh_per_seq():
         assert rel_l2(g.reshape(o.shape), o) <= TOL["bf16"]
 
 
+def test_split_more_heads_than_one_launch():
+    """72 heads of the d=128 shape: more than one launch of the split kernel holds on a
+    256-CU device (64 heads); heads from both launches against the oracle."""
+    w = WORKLOADS[4]
+    B, H, T = 9, 8, 32
+    inp = make_inputs(w.with_(B=9, H=8), T=T)
+    cfg = ops_config(w, T=T, B=B, H=H)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    note("split 72 heads")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    _check_heads(res, inp, [(0, 0), (3, 5), (7, 7), (8, 0), (8, 7)], w, TOL["bf16"])
+
+
 def test_split_saved_chunk_start_weights():
     """The split kernel's saved buffer: W0 exactly at chunk 0, and at chunk 2 the W_T of a
     scan over the first two chunks."""
