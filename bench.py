@@ -37,8 +37,8 @@ def bytes_per_token_head(d: int, io_bytes: int, nW: int, T: int) -> float:
 
 
 KERNEL_SOURCES = {
-    "ttt_fwd_mfma_pair_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp"),
-    "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp"),
+    "ttt_fwd_mfma_pair_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
     "ttt_decode_stream_d64": ("ttt_decode_stream.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
 }

@@ -10,6 +10,7 @@
 #define TTT_HD __device__ __forceinline__
 #define TTT_EXP2(x) __builtin_amdgcn_exp2f(x)
 #define TTT_RCP(x) __builtin_amdgcn_rcpf(x)
+#define TTT_RELU(x) __builtin_amdgcn_fmed3f((x), 0.0f, __builtin_inff())
 #include "ttt_gelu.hpp"
 
 namespace ttt {

@@ -219,7 +219,7 @@ fwd_mfma_kernel(ScanParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v, d1;
-        act_d<GELU_KIND>(acc[r], v, d1);
+        act_d_fwd<GELU_KIND>(acc[r], v, d1);
         a[r] = v;
         gd[r] = d1;
       }
@@ -342,7 +342,7 @@ fwd_mfma_kernel(ScanParams p) {
       f4 h = mfma16(s1a, e1[ht], hq[ht]);
       f4 a;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = act<GELU_KIND>(h[r]);
+      for (int r = 0; r < 4; ++r) a[r] = act_fwd<GELU_KIND>(h[r]);
       aqR[ht] = cvt4(a);
     }
 #pragma unroll

@@ -377,7 +377,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v, d1;
-        act_d<GELU_KIND>(hk[ht][r], v, d1);
+        act_d_fwd<GELU_KIND>(hk[ht][r], v, d1);
         a[r] = v;
         gd[r] = d1;
       }
@@ -474,7 +474,6 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         sg += gg[i];
         sgx += gg[i] * xh[i];
       }
-      const float loss = sum16(l2);
       const float mg = sum16(sg) * (1.0f / D), mgx = sum16(sgx) * (1.0f / D);
       const float ne2 = neta * ls.rs;
 #pragma unroll
@@ -484,10 +483,12 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         S.E2[t * RS + d] = e;
         zp_put(S.E2z, d, t, e);
       }
-      if (c16 == 0) {
-        if (p.loss) p.loss[static_cast<size_t>(head) * T + t0 + t] = loss;
-        flag_nonfinite(p.status, loss);
+      if (p.loss) {
+        const float loss = sum16(l2);
+        if (c16 == 0) p.loss[static_cast<size_t>(head) * T + t0 + t] = loss;
       }
+      // mean(g) is non-finite whenever any residual (inputs, Z^K) is
+      if (c16 == 0) flag_nonfinite(p.status, mg);
     } else {
       w2t();
       if (c + 2 < nchunks) stage_write(c + 2, ld);
@@ -638,7 +639,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       const f4 h = mfma32(ht == 0 ? cat(s1a, zz) : cat(zz, s1a), cur.e1, hq[ht]);
       f4 a;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = act<GELU_KIND>(h[r]);
+      for (int r = 0; r < 4; ++r) a[r] = act_fwd<GELU_KIND>(h[r]);
       aqR[ht] = cvt4(a);
     }
     const bf16x8 aqR8 = cat(aqR[0], aqR[1]);

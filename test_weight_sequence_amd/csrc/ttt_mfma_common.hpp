@@ -112,6 +112,22 @@ template <int GELU_KIND>
 __device__ __forceinline__ float act(float x) {
   return GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(x) : gelu(x, GELU_KIND);
 }
+// The d = 64 forward kernels' activations (rounded to bf16 right after): the erf form
+// through the lower-order A&S 7.1.25 evaluation of ttt_gelu.hpp. Its error (1.25e-5 in Phi)
+// moves a scan's output by about 2e-5 at d = 64, far inside the bf16 rounding of the
+// operands; the d = 128 kernel, whose drifting inputs amplify perturbations more, keeps the
+// 7.1.26 form.
+template <int GELU_KIND>
+__device__ __forceinline__ void act_d_fwd(float x, float& v, float& d1) {
+  if (GELU_KIND == TTT_GELU_ERF)
+    ttt_gelu::gelu_d_fast(x, v, d1);
+  else
+    gelu_d(x, GELU_KIND, v, d1);
+}
+template <int GELU_KIND>
+__device__ __forceinline__ float act_fwd(float x) {
+  return GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu_fast(x) : gelu(x, GELU_KIND);
+}
 
 // Staged elements per thread and their load type.
 template <int EPT>
