@@ -46,7 +46,6 @@ constexpr int NT = 64 * NW;
 constexpr int HS = HID / NW;           // hidden units per wave (32)
 constexpr int NHT = HS / 16;           // h tiles per wave (2)
 constexpr int RING = 6;                // chunk slots per head
-constexpr int ZS = 40;                 // row stride (bf16) of the zero-padded [d][4 x 8] arrays (16-byte rows)
 // slot layout (bytes): E1n and A^K of wave w as one 16-byte (two-tile) operand per lane,
 // then En2 as four 8-byte (k = token, n = d) operands per lane
 constexpr int SLOT_E1 = 0;
@@ -64,33 +63,20 @@ struct Pair {
   int nheads;
 };
 
-// [d][group of 4 tokens][8] with the group's 4 values in one half and zeros in the other:
-// lo = (data, zero), hi = (zero, data). A 16-byte read gives a K = 16 operand padded to the
-// 16x16x32 MFMA's K = 32, data in the lower or upper four k-slots.
-struct ZPad2 {
-  alignas(16) __bf16 lo[D * ZS];
-  alignas(16) __bf16 hi[D * ZS];
-};
-__device__ __forceinline__ bf16x8 zp_lo(const ZPad2& z, int d, int g) {
-  return *reinterpret_cast<const bf16x8*>(&z.lo[d * ZS + 8 * g]);
+// Transposing LDS load of four bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane 4q + e receives element e of the 8-byte chunks addressed by lanes q, q+4, q+8, q+12.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const __bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const auto lp = (lds_s16x4*)((__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
-__device__ __forceinline__ bf16x8 zp_hi(const ZPad2& z, int d, int g) {
-  return *reinterpret_cast<const bf16x8*>(&z.hi[d * ZS + 8 * g]);
-}
-__device__ __forceinline__ bf16x4 zp_data(const ZPad2& z, int d, int g) {
-  return *reinterpret_cast<const bf16x4*>(&z.hi[d * ZS + 8 * g + 4]);
-}
-__device__ __forceinline__ void zp_put(ZPad2& z, int d, int t, __bf16 v) {
-  z.lo[d * ZS + 8 * (t >> 2) + (t & 3)] = v;
-  z.hi[d * ZS + 8 * (t >> 2) + 4 + (t & 3)] = v;
-}
-__device__ __forceinline__ void zp_clear(ZPad2& z, int i) {  // i < D * 4: zero halves of one group
-  const int d = i >> 2, gg = i & 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    z.lo[d * ZS + 8 * gg + 4 + j] = (__bf16)0.f;
-    z.hi[d * ZS + 8 * gg + j] = (__bf16)0.f;
-  }
+// Four consecutive tokens of one column of a staged [token][d] array: lane (g, c16) gets
+// X[4 g + r][16 dt + c16], r = 0..3 (lane (g, 4q + e) addresses row 4 g + e', columns
+// 16 dt + 4 q' .. + 3 with q' = c16 % 4, e' = c16 / 4). In the lower or upper half of a K = 32
+// operand, with zeros in the other, it is the transposed chunk as a K = 16 operand.
+__device__ __forceinline__ bf16x4 tgroup(const __bf16* X, int dt, int g, int c16) {
+  return lds_tr4(&X[(4 * g + (c16 >> 2)) * RS + 16 * dt + 4 * (c16 & 3)]);
 }
 
 struct PStage {
@@ -100,15 +86,12 @@ struct PStage {
 };
 struct ProdSmem {
   PStage st[4];   // chunk j in slot j & 3
-  ZPad2 Ktz[4];
   float red[NW][NDT][4][PS];
   alignas(16) __bf16 E2[BC * RS];  // En2 [token][d]
-  ZPad2 E2z;           // En2 zero-padded [d][token]
   alignas(16) __bf16 zeros[8];
 };
 struct ConsSmem {
   PStage st[3];   // chunk j in slot j % 3
-  ZPad2 Ktz[3];
   float red[2][NW][NDT][4][PS];
   alignas(16) __bf16 zeros[8];
 };
@@ -213,24 +196,23 @@ struct Carry {
 };
 
 // The 16 MFMAs of a chunk-end update: W1 += K^T E1n, W2 += A^K^T En2 (K = 16 over the
-// chunk's tokens, operands padded by the zero halves of the [d][token] arrays).
-__device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const ZPad2& Kt,
-                                             const ZPad2& E2t, bf16x8 e1, bf16x8 ak, int g, int c16) {
-  bf16x8 kl[NDT], kh[NDT], el[NDT], eh[NDT];
+// chunk's tokens). K^T and En2^T come from the staged [token][d] rows through transposing
+// LDS loads, each in one half of a K = 32 operand with zeros in the other.
+__device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const __bf16* Krows,
+                                             const __bf16* E2rows, bf16x8 e1, bf16x8 ak, int g, int c16,
+                                             bf16x4 zz) {
+  bf16x4 kd[NDT], ed[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    const int d = 16 * dt + c16;
-    kl[dt] = zp_lo(Kt, d, g);
-    kh[dt] = zp_hi(Kt, d, g);
-    el[dt] = zp_lo(E2t, d, g);
-    eh[dt] = zp_hi(E2t, d, g);
+    kd[dt] = tgroup(Krows, dt, g, c16);
+    ed[dt] = tgroup(E2rows, dt, g, c16);
   }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    W1c[dt][0] = mfma32(kl[dt], e1, W1c[dt][0]);
-    W1c[dt][1] = mfma32(kh[dt], e1, W1c[dt][1]);
-    W2c[0][dt] = mfma32(ak, el[dt], W2c[0][dt]);
-    W2c[1][dt] = mfma32(ak, eh[dt], W2c[1][dt]);
+    W1c[dt][0] = mfma32(cat(kd[dt], zz), e1, W1c[dt][0]);
+    W1c[dt][1] = mfma32(cat(zz, kd[dt]), e1, W1c[dt][1]);
+    W2c[0][dt] = mfma32(ak, cat(ed[dt], zz), W2c[0][dt]);
+    W2c[1][dt] = mfma32(ak, cat(zz, ed[dt]), W2c[1][dt]);
   }
 }
 
@@ -304,13 +286,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   const float* gam = hst.gam;
   const float* bet = hst.bet;
   const Ident& id = hst.id;
-  // all padded [d][token] arrays start at zero: their zero halves stay zero, and the
-  // update applied at chunk 0 (from the zero carry of "chunk -1") reads finite values
+  // the update applied at chunk 0 (from the zero carry of "chunk -1") reads stage slot 3
+  // and the En2 rows before anything is written there: they start at zero (finite)
   {
-    uint4* z4 = reinterpret_cast<uint4*>(&S.Ktz[0]);
-    for (int i = tid; i < 4 * static_cast<int>(sizeof(ZPad2)) / 16; i += NT) z4[i] = uint4{0u, 0u, 0u, 0u};
-    uint4* e4 = reinterpret_cast<uint4*>(&S.E2z);
-    for (int i = tid; i < static_cast<int>(sizeof(ZPad2)) / 16; i += NT) e4[i] = uint4{0u, 0u, 0u, 0u};
+    uint4* z4 = reinterpret_cast<uint4*>(S.st[3].K);
+    for (int i = tid; i < static_cast<int>(sizeof(S.st[3].K)) / 16; i += NT) z4[i] = uint4{0u, 0u, 0u, 0u};
+    uint4* e4 = reinterpret_cast<uint4*>(S.E2);
+    for (int i = tid; i < static_cast<int>(sizeof(S.E2)) / 16; i += NT) e4[i] = uint4{0u, 0u, 0u, 0u};
   }
   if (tid < 8) S.zeros[tid] = (__bf16)0.f;
   // staging by waves 4..7: thread -> (token, 4 consecutive d). Every wave issues exactly
@@ -334,9 +316,6 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     PStage& st = S.st[chunk & 3];
     *reinterpret_cast<uint2*>(&st.K[st_t * RS + st_d]) = r.k;
     *reinterpret_cast<uint2*>(&st.X[st_t * RS + st_d]) = r.x;
-    const bf16x4 kv = __builtin_bit_cast(bf16x4, r.k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zp_put(S.Ktz[chunk & 3], st_d + j, st_t, kv[j]);
     if (lt < BC) st.eta[lt] = r.e * p.eta_scale;
   };
   if (w >= 4) {
@@ -367,7 +346,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
     // the update of chunk c - 1 (W(c) = W(c-1) + ...), next to the GELU work
     // (at chunk 0 the carry is zero and the operands are zero-filled: an exact no-op)
-    chunk_update(W1c, W2c, S.Ktz[(c - 1) & 3], S.E2z, in.e1, in.ak, g, c16);
+    chunk_update(W1c, W2c, S.st[(c - 1) & 3].K, S.E2, in.e1, in.ak, g, c16, zz);
     // A^K (R layout: m = h, k = token), G
     bf16x4 akR[NHT];
     f4 gk[NHT];
@@ -481,7 +460,6 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         const int d = 16 * i + c16;
         const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
         S.E2[t * RS + d] = e;
-        zp_put(S.E2z, d, t, e);
       }
       if (p.loss) {
         const float loss = sum16(l2);
@@ -516,8 +494,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
     ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
     if (w == 0) {
-      ho.st16(base + SLOT_E2 + lane * 32, cat(zp_data(S.E2z, c16, g), zp_data(S.E2z, 16 + c16, g)));
-      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(zp_data(S.E2z, 32 + c16, g), zp_data(S.E2z, 48 + c16, g)));
+      ho.st16(base + SLOT_E2 + lane * 32, cat(tgroup(S.E2, 0, g, c16), tgroup(S.E2, 1, g, c16)));
+      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, 2, g, c16), tgroup(S.E2, 3, g, c16)));
     }
     compiler_fence();
   };
@@ -532,8 +510,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   const Carry& last = (nchunks & 1) ? cb : ca;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (lane == 0) ho.st(w, static_cast<unsigned>(nchunks));
-  // the last chunk's update (its En2 is still in E2z)
-  chunk_update(W1c, W2c, S.Ktz[(nchunks - 1) & 3], S.E2z, last.e1, last.ak, g, c16);
+  // the last chunk's update (its En2 is still in E2)
+  chunk_update(W1c, W2c, S.st[(nchunks - 1) & 3].K, S.E2, last.e1, last.ak, g, c16, zz);
   if (p.wt_1)
     wtiles_store(p.wt_1 + static_cast<size_t>(head) * D * HID, p.wt_2 + static_cast<size_t>(head) * HID * D,
                  g, c16, hs, W1c, W2c);
@@ -555,10 +533,6 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
   const float* gam = hst.gam;
   const float* bet = hst.bet;
   const Ident& id = hst.id;
-  for (int i = tid; i < D * 4; i += NT) {
-#pragma unroll
-    for (int s3 = 0; s3 < 3; ++s3) zp_clear(S.Ktz[s3], i);
-  }
   if (tid < 8) S.zeros[tid] = (__bf16)0.f;
   // staging by all waves: thread -> (token, 2 consecutive d)
   const int st_t = tid >> 5, st_d = (tid & 31) * 2;
@@ -576,9 +550,6 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     PStage& st = S.st[slot];
     *reinterpret_cast<unsigned*>(&st.K[st_t * RS + st_d]) = r.k;
     *reinterpret_cast<unsigned*>(&st.X[st_t * RS + st_d]) = r.x;
-    const bf16x2 kv = __builtin_bit_cast(bf16x2, r.k);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) zp_put(S.Ktz[slot], st_d + j, st_t, kv[j]);
   };
   stage_write(0, gload(0));
   __syncthreads();
@@ -661,9 +632,9 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     // the producer's chunk-end update, from the same operands
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + c16;
-      W1c[dt][0] = mfma32(zp_lo(S.Ktz[sl], d, g), cur.e1, W1c[dt][0]);
-      W1c[dt][1] = mfma32(zp_hi(S.Ktz[sl], d, g), cur.e1, W1c[dt][1]);
+      const bf16x4 kd = tgroup(st.K, dt, g, c16);
+      W1c[dt][0] = mfma32(cat(kd, zz), cur.e1, W1c[dt][0]);
+      W1c[dt][1] = mfma32(cat(zz, kd), cur.e1, W1c[dt][1]);
       W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);
       W2c[1][dt] = mfma32(cur.ak, cat(zz, slot_e2(cur, dt)), W2c[1][dt]);
     }
