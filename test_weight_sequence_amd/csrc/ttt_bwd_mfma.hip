@@ -42,6 +42,7 @@ constexpr int NT = 64 * NW;
 constexpr int HS = HID / NW;    // hidden units per wave
 constexpr int NHT = HS / 16;    // h tiles per wave
 constexpr int NKH = NHT / 2;    // 32-wide k-steps over a wave's hidden slice
+constexpr int TS = BC + 8;  // padded row stride of the [16 x 16] dP1 arrays
 static_assert(NW == 4 && NT == BC * 16, "LayerNorm phases: 16 lanes per token, all waves");
 
 // One chunk's rows.
@@ -50,8 +51,6 @@ struct BStage {
   alignas(16) __bf16 Q[BC * RS];
   alignas(16) __bf16 V[BC * RS];
   alignas(16) __bf16 dZ[BC * RS];
-  alignas(16) __bf16 Kt[D * TS];
-  alignas(16) __bf16 Qt[D * TS];
   float eta[BC];
 };
 
@@ -66,11 +65,8 @@ __device__ __forceinline__ int prot(int r, int lane) { return (lane + 16 * r) & 
 struct BSmem {
   BStage st[2];                       // chunk c lives in st[c & 1]
   alignas(16) __bf16 E2[BC * RS];     // E2 (= -eta d2): [token][d]
-  alignas(16) __bf16 E2t[D * TS];     //                 [d][token]
   alignas(16) __bf16 dZQ[BC * RS];
-  alignas(16) __bf16 dZQt[D * TS];
   alignas(16) __bf16 dZK[BC * RS];
-  alignas(16) __bf16 dZKt[D * TS];
   alignas(16) __bf16 dP1r[BC * TS];   // dP1 [t][u]
   alignas(16) __bf16 dP1c[BC * TS];   // dP1 [u][t]
   float dKres[BC * D];                // residual part of dK, [t][d]
@@ -128,9 +124,10 @@ __device__ __forceinline__ void rows2(const __bf16* a, int c16, int g, bf16x8 (&
   for (int ks = 0; ks < 2; ++ks)
     o[ks] = cat(lds4(&a[c16 * RS + 32 * ks + 4 * g]), lds4(&a[c16 * RS + 32 * ks + 16 + 4 * g]));
 }
-// [d][token] LDS array as the B operand of a contraction over tokens (k = token, n = d)
+// [token][d] LDS array as the B operand of a contraction over tokens (k = token, n = d),
+// through the transposing LDS load
 __device__ __forceinline__ bf16x4 colsT(const __bf16* a, int dt, int c16, int g) {
-  return lds4(&a[(16 * dt + c16) * TS + 4 * g]);
+  return tgroup(a, RS, dt, g, c16);
 }
 // four d values of one token, [token][d] array
 __device__ __forceinline__ float red_sum(const Partials& P, int i, int t, int c16) {
@@ -216,12 +213,6 @@ bwd_mfma_kernel(BwdParams p) {
     *reinterpret_cast<uint2*>(&S.Q[st_t * RS + st_d]) = qq;
     *reinterpret_cast<uint2*>(&S.V[st_t * RS + st_d]) = vv;
     *reinterpret_cast<uint2*>(&S.dZ[st_t * RS + st_d]) = zz;
-    const bf16x4 kv = __builtin_bit_cast(bf16x4, kk), qv = __builtin_bit_cast(bf16x4, qq);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      S.Kt[(st_d + j) * TS + st_t] = kv[j];
-      S.Qt[(st_d + j) * TS + st_t] = qv[j];
-    }
     if (tid < BC) S.eta[tid] = e * p.eta_scale;
   };
   // Final dQ, dK of chunk cc from the per-wave partials (four elements per thread).
@@ -372,7 +363,6 @@ bwd_mfma_kernel(BwdParams p) {
         d2k[i] = (gg[i] - mg - xk[i] * mgxk) * rsk;
         const __bf16 e = (__bf16)(-etak * d2k[i]);
         sm.E2[t * RS + d] = e;
-        sm.E2t[d * TS + t] = e;
       }
     }
     if (c + 1 < nchunks) emit_dqdk(c + 1);
@@ -432,7 +422,7 @@ bwd_mfma_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      f4 acc = mfma16(s2a, colsT(sm.E2t, dt, c16, g), zero4());
+      f4 acc = mfma16(s2a, colsT(sm.E2, dt, c16, g), zero4());
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks)
         acc = mfma32(hcat(aqT, ks), cat(W2b[2 * ks][dt], W2b[2 * ks + 1][dt]), acc);
@@ -465,7 +455,6 @@ bwd_mfma_kernel(BwdParams p) {
         const int d = 16 * i + c16;
         const __bf16 e = (__bf16)((v[i] - mv - x[i] * mvx) * ls.rs);
         sm.dZQ[t * RS + d] = e;
-        sm.dZQt[d * TS + t] = e;
       }
     }
     __syncthreads();  // ---- 4
@@ -538,7 +527,7 @@ bwd_mfma_kernel(BwdParams p) {
     // first dK term E1 dW1'^T (all before dW takes this chunk's terms)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      f4 de2 = mfma16(p2a, colsT(sm.dZQt, dt, c16, g), zero4());
+      f4 de2 = mfma16(p2a, colsT(sm.dZQ, dt, c16, g), zero4());
       f4 dq = zero4(), dk = zero4();
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks) {
@@ -555,9 +544,9 @@ bwd_mfma_kernel(BwdParams p) {
     // this chunk's direct dW terms
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 qt = colsT(S.Qt, dt, c16, g);
-      const bf16x4 zq = colsT(sm.dZQt, dt, c16, g);
-      const bf16x4 e2 = colsT(sm.E2t, dt, c16, g);
+      const bf16x4 qt = colsT(S.Q, dt, c16, g);
+      const bf16x4 zq = colsT(sm.dZQ, dt, c16, g);
+      const bf16x4 e2 = colsT(sm.E2, dt, c16, g);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         dW1c[dt][ht] = mfma16(qt, dhqR[ht], dW1c[dt][ht]);
@@ -608,7 +597,6 @@ bwd_mfma_kernel(BwdParams p) {
         const int d = 16 * i + c16;
         const __bf16 e = (__bf16)(rsk * (dx[i] - mdx - xk[i] * mdxx) + ds * xk[i] * (1.0f / D));
         sm.dZK[t * RS + d] = e;
-        sm.dZKt[d * TS + t] = e;
         sm.dKres[t * D + d] = dr[i];
         dVg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)(-dr[i]);
       }
@@ -654,18 +642,18 @@ bwd_mfma_kernel(BwdParams p) {
       if (dt == w) {
         // the terms not split over hidden units, one d tile per wave: the residual and
         // dP1^T Q into dK, dz and dP1 K into dQ
-        dk = mfma16(lds4(&sm.dP1c[c16 * TS + 4 * g]), colsT(S.Qt, dt, c16, g), dk);
+        dk = mfma16(lds4(&sm.dP1c[c16 * TS + 4 * g]), colsT(S.Q, dt, c16, g), dk);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dk[r] += sm.dKres[(4 * g + r) * D + 16 * dt + c16];
         f4 dq = get_tile(sm.red[1], w, dt, lane);
-        dq = mfma16(lds4(&sm.dP1r[c16 * TS + 4 * g]), colsT(S.Kt, dt, c16, g), dq);
+        dq = mfma16(lds4(&sm.dP1r[c16 * TS + 4 * g]), colsT(S.K, dt, c16, g), dq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dq[r] += bf(S.dZ[(4 * g + r) * RS + 16 * dt + c16]);
         put_tile(sm.red[1], w, dt, lane, dq);
       }
       put_tile(sm.red[2], w, dt, lane, dk);
-      const bf16x4 kt = colsT(S.Kt, dt, c16, g);
-      const bf16x4 zkt = colsT(sm.dZKt, dt, c16, g);
+      const bf16x4 kt = colsT(S.K, dt, c16, g);
+      const bf16x4 zkt = colsT(sm.dZK, dt, c16, g);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         dW1c[dt][ht] = mfma16(kt, dhkR[ht], dW1c[dt][ht]);

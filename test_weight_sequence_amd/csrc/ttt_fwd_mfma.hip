@@ -36,8 +36,7 @@ template <int NW>
 struct Smem {
   Stage st[3];                   // chunk c lives in st[c % 3]
   float red[2][NW][NDT][4][PS];  // [0]: Z^K partials, [1]: Z^Q partials (64 used per row)
-  __bf16 E2[BC * RS];            // En2, [token][d]
-  __bf16 E2t[D * TS];            // En2, [d][token]
+  alignas(16) __bf16 E2[BC * RS];  // En2, [token][d]
 };
 
 template <int GELU_KIND, int NW>
@@ -107,9 +106,6 @@ fwd_mfma_kernel(ScanParams p) {
     *reinterpret_cast<LdT*>(&S.K[st_t * RS + st_d]) = kk;
     *reinterpret_cast<LdT*>(&S.Q[st_t * RS + st_d]) = qq;
     *reinterpret_cast<LdT*>(&S.V[st_t * RS + st_d]) = vv;
-    const typename SV::B kv = __builtin_bit_cast(typename SV::B, kk);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) S.Kt[(st_d + j) * TS + st_t] = kv[j];
     if (tid < BC) S.eta[tid] = e * p.eta_scale;
   };
   auto gload = [&](int chunk, LdT& kk, LdT& qq, LdT& vv, float& e) {
@@ -292,7 +288,6 @@ fwd_mfma_kernel(ScanParams p) {
         const int d = 16 * i + c16;
         const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
         sm.E2[t * RS + d] = e;
-        sm.E2t[d * TS + t] = e;
       }
       if (c16 == 0) {
         if (p.loss) p.loss[static_cast<size_t>(bh) * T + t0 + t] = loss;
@@ -312,7 +307,7 @@ fwd_mfma_kernel(ScanParams p) {
       aE[ks] = cat(lds4(&sm.E2[c16 * RS + 32 * ks + 4 * g]), lds4(&sm.E2[c16 * RS + 32 * ks + 16 + 4 * g]));
     bf16x4 bE[NDT];  // En2 with k = token (4g + j), n = d (lane%16)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) bE[dt] = lds4(&sm.E2t[(16 * dt + c16) * TS + 4 * g]);
+    for (int dt = 0; dt < NDT; ++dt) bE[dt] = tgroup(sm.E2, RS, dt, g, c16);
     bf16x4 e1[NHT];
     {
       // W2^T tiles (d x h) from the bf16 W2 tiles: exact transpose through the identity
@@ -369,7 +364,7 @@ fwd_mfma_kernel(ScanParams p) {
     // ---- chunk-end update of the fp32 fast weights ----
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 kt = lds4(&S.Kt[(16 * dt + c16) * TS + 4 * g]);  // K^T: m = d, k = token
+      const bf16x4 kt = tgroup(S.K, RS, dt, g, c16);  // K^T: m = d, k = token
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         W1c[dt][ht] = mfma16(kt, e1[ht], W1c[dt][ht]);

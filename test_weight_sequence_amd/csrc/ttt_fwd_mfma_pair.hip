@@ -63,22 +63,6 @@ struct Pair {
   int nheads;
 };
 
-// Transposing LDS load of four bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane 4q + e receives element e of the 8-byte chunks addressed by lanes q, q+4, q+8, q+12.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 lds_tr4(const __bf16* p) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const auto lp = (lds_s16x4*)((__attribute__((address_space(3))) char*)(p));
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
-}
-// Four consecutive tokens of one column of a staged [token][d] array: lane (g, c16) gets
-// X[4 g + r][16 dt + c16], r = 0..3 (lane (g, 4q + e) addresses row 4 g + e', columns
-// 16 dt + 4 q' .. + 3 with q' = c16 % 4, e' = c16 / 4). In the lower or upper half of a K = 32
-// operand, with zeros in the other, it is the transposed chunk as a K = 16 operand.
-__device__ __forceinline__ bf16x4 tgroup(const __bf16* X, int dt, int g, int c16) {
-  return lds_tr4(&X[(4 * g + (c16 >> 2)) * RS + 16 * dt + 4 * (c16 & 3)]);
-}
-
 struct PStage {
   alignas(16) __bf16 K[BC * RS];
   alignas(16) __bf16 X[BC * RS];  // V (producer) or Q (consumer)
@@ -204,8 +188,8 @@ __device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT]
   bf16x4 kd[NDT], ed[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    kd[dt] = tgroup(Krows, dt, g, c16);
-    ed[dt] = tgroup(E2rows, dt, g, c16);
+    kd[dt] = tgroup(Krows, RS, dt, g, c16);
+    ed[dt] = tgroup(E2rows, RS, dt, g, c16);
   }
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -494,8 +478,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
     ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
     if (w == 0) {
-      ho.st16(base + SLOT_E2 + lane * 32, cat(tgroup(S.E2, 0, g, c16), tgroup(S.E2, 1, g, c16)));
-      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, 2, g, c16), tgroup(S.E2, 3, g, c16)));
+      ho.st16(base + SLOT_E2 + lane * 32, cat(tgroup(S.E2, RS, 0, g, c16), tgroup(S.E2, RS, 1, g, c16)));
+      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, RS, 2, g, c16), tgroup(S.E2, RS, 3, g, c16)));
     }
     compiler_fence();
   };
@@ -632,7 +616,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     // the producer's chunk-end update, from the same operands
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 kd = tgroup(st.K, dt, g, c16);
+      const bf16x4 kd = tgroup(st.K, RS, dt, g, c16);
       W1c[dt][0] = mfma32(cat(kd, zz), cur.e1, W1c[dt][0]);
       W1c[dt][1] = mfma32(cat(zz, kd), cur.e1, W1c[dt][1]);
       W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);

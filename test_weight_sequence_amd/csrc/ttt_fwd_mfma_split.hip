@@ -55,7 +55,6 @@ constexpr int HS = HID / (S * NW);   // hidden units per wave
 constexpr int NHT = HS / 16;         // h tiles per wave
 constexpr int NKD = D / 32;          // 32-wide k-steps over d
 constexpr int RS = D + 8;            // row stride (bf16) of [token][d] arrays
-constexpr int TS = BC + 8;           // row stride of [d][token] arrays
 constexpr int DPL = D / 16;          // d values per LayerNorm lane
 constexpr int kSpinLimit = 1 << 20;
 static_assert(NHT == 2 && NW * 4 == BC, "tile split");
@@ -71,7 +70,6 @@ struct Stage {
   alignas(16) __bf16 K[BC * RS];
   alignas(16) __bf16 Q[BC * RS];
   alignas(16) __bf16 V[BC * RS];
-  alignas(16) __bf16 Kt[D * TS];
   float eta[BC];
 };
 
@@ -79,7 +77,6 @@ struct Smem {
   Stage st[3];                        // chunk c lives in st[c % 3]
   float red[NW][NDT][4][64];          // per-wave [token x d] partial tiles (lane-rotated rows)
   alignas(16) __bf16 E2[BC * RS];     // En2, [token][d]
-  alignas(16) __bf16 E2t[D * TS];     // En2, [d][token]
 };
 
 __device__ __forceinline__ int prot(int r, int lane) { return (lane + 16 * r) & 63; }
@@ -275,9 +272,6 @@ fwd_split_kernel(ScanParams p, Split x) {
     *reinterpret_cast<uint4*>(&St.K[st_t * RS + st_d]) = kk;
     *reinterpret_cast<uint4*>(&St.Q[st_t * RS + st_d]) = qq;
     *reinterpret_cast<uint4*>(&St.V[st_t * RS + st_d]) = vv;
-    const bf16x8 kv = __builtin_bit_cast(bf16x8, kk);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) St.Kt[(st_d + j) * TS + st_t] = kv[j];
     if (tid < BC) St.eta[tid] = e * p.eta_scale;
   };
   // this workgroup's [16 x 128] partial for the LayerNorm lanes' elements, from the waves'
@@ -445,7 +439,6 @@ fwd_split_kernel(ScanParams p, Split x) {
         const int d = 16 * i + c16;
         const __bf16 e = (__bf16)(ne2 * (gg[i] - mg - xh[i] * mgx));
         sm.E2[t * RS + d] = e;
-        sm.E2t[d * TS + t] = e;
       }
       if (c16 == 0 && s == 0) {
         if (p.loss) p.loss[static_cast<size_t>(bh) * T + t0 + t] = loss;
@@ -490,13 +483,13 @@ fwd_split_kernel(ScanParams p, Split x) {
     const bf16x4 s2a = cvt4(s2m);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 be = lds4(&sm.E2t[(16 * dt + c16) * TS + 4 * g]);
+      const bf16x4 be = mfma::tgroup(sm.E2, RS, dt, g, c16);
       f4 acc = mfma32(cat(aqT[0], aqT[1]), cat(W2b[0][dt], W2b[1][dt]), zero4());
       acc = mfma16(s2a, be, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
       // chunk-end update of this wave's fp32 weights
-      const bf16x4 kt = lds4(&St.Kt[(16 * dt + c16) * TS + 4 * g]);
+      const bf16x4 kt = mfma::tgroup(St.K, RS, dt, g, c16);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         W1c[dt][ht] = mfma16(kt, e1[ht], W1c[dt][ht]);

@@ -25,18 +25,32 @@ constexpr int HID = 256;
 constexpr int BC = 16;             // chunk
 constexpr int NDT = D / 16;        // d tiles
 constexpr int RS = D + 8;          // padded row stride (bf16 elements) of [token][d] arrays
-constexpr int TS = BC + 8;         // padded row stride of [d][token] arrays
 // Row stride (floats) of the cross-wave partial-sum rows. LayerNorm lanes read four rows at
 // once (16 lanes each); 80 = 64 + 16 puts the four rows on different banks.
 constexpr int PS = 80;
 
 struct Stage {
-  __bf16 K[BC * RS];
-  __bf16 Q[BC * RS];
-  __bf16 V[BC * RS];
-  __bf16 Kt[D * TS];
+  alignas(16) __bf16 K[BC * RS];
+  alignas(16) __bf16 Q[BC * RS];
+  alignas(16) __bf16 V[BC * RS];
   float eta[BC];
 };
+
+// Transposing LDS load of four bf16 (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane 4q + e receives element e of the 8-byte chunks addressed by lanes q, q+4, q+8, q+12.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const __bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const auto lp = (lds_s16x4*)((__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+// Four consecutive tokens of one column of a [token][d] LDS array with row stride rs: lane
+// (g, c16) gets X[4 g + r][16 dt + c16], r = 0..3 (lane (g, 4q + e) addresses row 4 g + e',
+// columns 16 dt + 4 q' .. + 3 with q' = c16 % 4, e' = c16 / 4). As an MFMA operand that is the
+// transposed chunk with k = token: K^T or En2^T for the K = 16 update products.
+__device__ __forceinline__ bf16x4 tgroup(const __bf16* X, int rs, int dt, int g, int c16) {
+  return lds_tr4(&X[(4 * g + (c16 >> 2)) * rs + 16 * dt + 4 * (c16 & 3)]);
+}
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
