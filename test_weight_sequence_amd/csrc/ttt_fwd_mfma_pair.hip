@@ -179,25 +179,41 @@ struct Carry {
   bf16x8 e1, ak;   // E1n(c-1), A^K(c-1): k = token (two h tiles)
 };
 
+// W1 += K^T E1n, W2 += A^K^T En2 from K^T / En2^T operands that hold two d tiles each
+// (k01: d tiles 0 and 1 in the lower and upper half, k23: 2 and 3; likewise e01, e23) and
+// E1n / A^K operands holding the two h tiles of the wave (e1, ak).
+__device__ __forceinline__ void update_mfmas(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], bf16x8 k01, bf16x8 k23,
+                                             bf16x8 e01, bf16x8 e23, bf16x8 e1, bf16x8 ak, bf16x4 zz) {
+  const bf16x8 b_lo[NHT] = {cat(lo4(e1), zz), cat(hi4(e1), zz)};  // E1n of h tile ht, lower half
+  const bf16x8 b_hi[NHT] = {cat(zz, lo4(e1)), cat(zz, hi4(e1))};  // upper half
+  const bf16x8 a_lo[NHT] = {cat(lo4(ak), zz), cat(hi4(ak), zz)};  // A^K^T of h tile ht
+  const bf16x8 a_hi[NHT] = {cat(zz, lo4(ak)), cat(zz, hi4(ak))};
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    W1c[0][ht] = mfma32(k01, b_lo[ht], W1c[0][ht]);
+    W1c[1][ht] = mfma32(k01, b_hi[ht], W1c[1][ht]);
+    W1c[2][ht] = mfma32(k23, b_lo[ht], W1c[2][ht]);
+    W1c[3][ht] = mfma32(k23, b_hi[ht], W1c[3][ht]);
+    W2c[ht][0] = mfma32(a_lo[ht], e01, W2c[ht][0]);
+    W2c[ht][1] = mfma32(a_hi[ht], e01, W2c[ht][1]);
+    W2c[ht][2] = mfma32(a_lo[ht], e23, W2c[ht][2]);
+    W2c[ht][3] = mfma32(a_hi[ht], e23, W2c[ht][3]);
+  }
+}
+
 // The 16 MFMAs of a chunk-end update: W1 += K^T E1n, W2 += A^K^T En2 (K = 16 over the
 // chunk's tokens). K^T and En2^T come from the staged [token][d] rows through transposing
 // LDS loads, each in one half of a K = 32 operand with zeros in the other.
 __device__ __forceinline__ void chunk_update(f4 (&W1c)[NDT][NHT], f4 (&W2c)[NHT][NDT], const __bf16* Krows,
                                              const __bf16* E2rows, bf16x8 e1, bf16x8 ak, int g, int c16,
                                              bf16x4 zz) {
-  bf16x4 kd[NDT], ed[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    kd[dt] = tgroup(Krows, RS, dt, g, c16);
-    ed[dt] = tgroup(E2rows, RS, dt, g, c16);
-  }
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    W1c[dt][0] = mfma32(cat(kd[dt], zz), e1, W1c[dt][0]);
-    W1c[dt][1] = mfma32(cat(zz, kd[dt]), e1, W1c[dt][1]);
-    W2c[0][dt] = mfma32(ak, cat(ed[dt], zz), W2c[0][dt]);
-    W2c[1][dt] = mfma32(ak, cat(zz, ed[dt]), W2c[1][dt]);
-  }
+  // K^T and En2^T of d tiles (0, 1) and (2, 3) fill both halves of an operand; the other
+  // operand carries its data in one half and zeros in the other, which selects the d tile
+  const bf16x8 k01 = cat(tgroup(Krows, RS, 0, g, c16), tgroup(Krows, RS, 1, g, c16));
+  const bf16x8 k23 = cat(tgroup(Krows, RS, 2, g, c16), tgroup(Krows, RS, 3, g, c16));
+  const bf16x8 e01 = cat(tgroup(E2rows, RS, 0, g, c16), tgroup(E2rows, RS, 1, g, c16));
+  const bf16x8 e23 = cat(tgroup(E2rows, RS, 2, g, c16), tgroup(E2rows, RS, 3, g, c16));
+  update_mfmas(W1c, W2c, k01, k23, e01, e23, e1, ak, zz);
 }
 
 // Operands of a staged [token][d] chunk: rows (token = lane%16), permuted d order.
@@ -605,23 +621,19 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     f4 s2m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) s2m[r] = (4 * g + r) <= c16 ? s2t[r] : 0.f;
-    const bf16x8 s2a8 = cat(cvt4(s2m), zz);
+    const bf16x4 s2a = cvt4(s2m);
+    const bf16x8 s2lo = cat(s2a, zz), s2hi = cat(zz, s2a);  // select the d tile of the En2 operand
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       f4 acc = mfma32(aqT8, W2b8[dt], zero4());
-      acc = mfma32(s2a8, cat(slot_e2(cur, dt), zz), acc);
+      acc = mfma32(dt & 1 ? s2hi : s2lo, cur.e2[dt >> 1], acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.red[c & 1][w][dt][r][lane] = acc[r];
     }
     // the producer's chunk-end update, from the same operands
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 kd = tgroup(st.K, RS, dt, g, c16);
-      W1c[dt][0] = mfma32(cat(kd, zz), cur.e1, W1c[dt][0]);
-      W1c[dt][1] = mfma32(cat(zz, kd), cur.e1, W1c[dt][1]);
-      W2c[0][dt] = mfma32(cur.ak, cat(slot_e2(cur, dt), zz), W2c[0][dt]);
-      W2c[1][dt] = mfma32(cur.ak, cat(zz, slot_e2(cur, dt)), W2c[1][dt]);
-    }
+    update_mfmas(W1c, W2c, cat(tgroup(st.K, RS, 0, g, c16), tgroup(st.K, RS, 1, g, c16)),
+                 cat(tgroup(st.K, RS, 2, g, c16), tgroup(st.K, RS, 3, g, c16)), cur.e2[0], cur.e2[1], cur.e1,
+                 cur.ak, zz);
     // this wave is done with slot c (its loads have returned: the dependency forces the
     // wait); wave 0 releases the slot after the barrier below. Then prefetch chunk c + 1.
     {
