@@ -60,9 +60,13 @@ constexpr int kSpinLimit = 1 << 20;
 static_assert(NHT == 2 && NW * 4 == BC, "tile split");
 
 // Workspace per head: two exchange areas (Z^K, Z^Q) of two chunk-parity slots of S partial
-// [16 x 128] fp32 sums, then (after all heads) 32 counter words per head.
+// [16 x 128] fp32 sums, then (after all heads) 32 counter words per head. On one XCD the
+// partials carry their own readiness: each element is stored with the chunk's tag in one
+// 8-byte store, and a reader polls its elements until the tags match (the area is cleared
+// before every launch). Across XCDs the parts exchange counters with device-scope fences.
 constexpr size_t kPartFloats = static_cast<size_t>(BC) * D;
-constexpr size_t kHeadXFloats = 2 * 2 * S * kPartFloats;
+// Each element travels as a (value, tag) pair of 32-bit words, the tag being the chunk index + 1.
+constexpr size_t kHeadXFloats = 2 * 2 * S * kPartFloats * 2;
 constexpr int kFlagWords = 32;  // [0, S): Z^K counters, [8, 8 + S): Z^Q, [16, 16 + S): XCD ids
 constexpr int kLoadL2 = 16;     // cache policy of exchange loads on one XCD: device scope (sc1)
 
@@ -178,17 +182,21 @@ __device__ __forceinline__ void wait_all(const XMem& m, int base, int s, unsigne
   if (!m.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// one element of a partial slot area (float offset)
-__device__ __forceinline__ float part_load(const XMem& m, bool zq, int off) {
-  if (m.local)
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(zq ? m.qr : m.zr, 4 * off, 0, kLoadL2));
-  return (zq ? m.xq : m.xz)[off];
+// one element of a partial slot area (element offset; elements are (value, tag) pairs)
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 part_load_tagged(const XMem& m, bool zq, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(zq ? m.qr : m.zr, 8 * off, 0, kLoadL2));
 }
-__device__ __forceinline__ void part_store(const XMem& m, bool zq, int off, float v) {
-  if (m.local)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), zq ? m.qr : m.zr, 4 * off, 0, 0);
-  else
-    (zq ? m.xq : m.xz)[off] = v;
+__device__ __forceinline__ float part_load(const XMem& m, bool zq, int off) {
+  return (zq ? m.xq : m.xz)[2 * off];
+}
+__device__ __forceinline__ void part_store(const XMem& m, bool zq, int off, float v, unsigned tag) {
+  if (m.local) {
+    const u32x2 pv = {__float_as_uint(v), tag};
+    __builtin_amdgcn_raw_buffer_store_b64(pv, zq ? m.qr : m.zr, 8 * off, 0, 0);
+  } else {
+    (zq ? m.xq : m.xz)[2 * off] = v;
+  }
 }
 
 template <int GELU_KIND>
@@ -209,11 +217,11 @@ fwd_split_kernel(ScanParams p, Split x) {
   __shared__ unsigned sh_local;
   XMem m;
   m.xz = x.xbuf + static_cast<size_t>(bh) * kHeadXFloats;  // [slot][S][16 x 128]
-  m.xq = m.xz + 2 * S * kPartFloats;
+  m.xq = m.xz + 2 * 2 * S * kPartFloats;
   m.cnt = x.flags + static_cast<size_t>(bh) * kFlagWords;
   m.fr = __builtin_amdgcn_make_buffer_rsrc(m.cnt, 0, kFlagWords * 4, mfma::kBufFlags);
-  m.zr = __builtin_amdgcn_make_buffer_rsrc(m.xz, 0, 2 * S * kPartFloats * 4, mfma::kBufFlags);
-  m.qr = __builtin_amdgcn_make_buffer_rsrc(m.xq, 0, 2 * S * kPartFloats * 4, mfma::kBufFlags);
+  m.zr = __builtin_amdgcn_make_buffer_rsrc(m.xz, 0, 2 * S * kPartFloats * 8, mfma::kBufFlags);
+  m.qr = __builtin_amdgcn_make_buffer_rsrc(m.xq, 0, 2 * S * kPartFloats * 8, mfma::kBufFlags);
   {
     // placement: every part publishes its XCD id + 1 (device scope) and reads the others'
     unsigned xcc;
@@ -297,29 +305,61 @@ fwd_split_kernel(ScanParams p, Split x) {
     rs = __builtin_amdgcn_rsqf(sum16(v) * (1.0f / D) + p.eps);
   };
   // store this part's partial of chunk parity `slot` (the LayerNorm lanes' elements)
-  auto put_own = [&](bool zq, int slot) {
-    float own[DPL];
+  auto put_own = [&](bool zq, int slot, unsigned tag, float (&own)[DPL]) {
     own_partial(own);
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) part_store(m, zq, (slot * S + s) * kPartFloats + ln_t * D + 16 * i + c16, own[i]);
+    for (int i = 0; i < DPL; ++i)
+      part_store(m, zq, (slot * S + s) * kPartFloats + ln_t * D + 16 * i + c16, own[i], tag);
   };
-  // the head's total from the S partials of a slot (fixed part order)
-  auto total = [&](bool zq, int slot, float (&z)[DPL]) {
+  // the head's total from the S partials of a slot (fixed part order; this part's own from
+  // registers). On one XCD each lane polls its elements until every tag reads `tag` (bounded;
+  // on expiry the timeout bit is set and the values are whatever was read).
+  auto total = [&](bool zq, int slot, unsigned tag, const float (&own)[DPL], float (&z)[DPL]) {
+    float v[S][DPL];
+    if (m.local) {
+      for (int it = 0;; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int o = 0; o < S; ++o) {
+          if (o == s) continue;
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) {
+            const u32x2 pv = part_load_tagged(m, zq, (slot * S + o) * kPartFloats + ln_t * D + 16 * i + c16);
+            v[o][i] = __uint_as_float(pv[0]);
+            all = all && pv[1] == tag;
+          }
+        }
+        if (all) break;
+        if (it + 1 >= kSpinLimit) {
+          atomicOr(p.status, kStatusTimeout);
+          break;
+        }
+        if ((it & 63) == 63 &&
+            (__hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusTimeout))
+          break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    } else {
+#pragma unroll
+      for (int o = 0; o < S; ++o)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) v[o][i] = part_load(m, zq, (slot * S + o) * kPartFloats + ln_t * D + 16 * i + c16);
+    }
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-      const int off = slot * S * kPartFloats + ln_t * D + 16 * i + c16;
       float a = 0.f;
 #pragma unroll
-      for (int o = 0; o < S; ++o) a += part_load(m, zq, off + o * static_cast<int>(kPartFloats));
+      for (int o = 0; o < S; ++o) a += o == s ? own[i] : v[o][i];
       z[i] = a;
     }
   };
   // output z = Q + LN(Z^Q) of chunk cc for this part's tokens (wave s: tokens 4 s .. 4 s + 3)
+  float ownQ[DPL];  // this part's Z^Q partial of the chunk whose output is still to be written
   auto ln_out = [&](int cc) {
     const Stage& So = sm.st[cc % 3];
     const int t = ln_t;
     float z[DPL];
-    total(true, cc & 1, z);
+    total(true, cc & 1, static_cast<unsigned>(cc) + 1u, ownQ, z);
     float mu, rs;
     ln_stats8(z, mu, rs);
     float chk = 0.f;
@@ -410,14 +450,17 @@ fwd_split_kernel(ScanParams p, Split x) {
 
     // ---- Z^K over all hidden units (this wait also covers the Z^Q partials of chunk c - 1,
     // whose output is written now), LayerNorm forward/backward -> En2 ----
-    put_own(false, slot);
-    publish(m, 0, s, c1);
-    wait_all(m, 0, s, c1, p.status);
+    float ownK[DPL];
+    put_own(false, slot, c1, ownK);
+    if (!m.local) {
+      publish(m, 0, s, c1);
+      wait_all(m, 0, s, c1, p.status);
+    }
     if (c > 0 && w == s) ln_out(c - 1);
     {
       const int t = ln_t;
       float z[DPL];
-      total(false, slot, z);
+      total(false, slot, c1, ownK, z);
       float mu, rs;
       ln_stats8(z, mu, rs);
       float xh[DPL], gg[DPL], l2 = 0.f, sg = 0.f, sgx = 0.f;
@@ -499,10 +542,10 @@ fwd_split_kernel(ScanParams p, Split x) {
     __syncthreads();
 
     // ---- publish this part's Z^Q partial of chunk c (its output is written next chunk) ----
-    put_own(true, slot);
-    publish(m, 8, s, c1);
+    put_own(true, slot, c1, ownQ);
+    if (!m.local) publish(m, 8, s, c1);
   }
-  wait_all(m, 8, s, static_cast<unsigned>(nchunks), p.status);
+  if (!m.local) wait_all(m, 8, s, static_cast<unsigned>(nchunks), p.status);
   if (w == s) ln_out(nchunks - 1);
 
   if (p.wt_1)
@@ -510,9 +553,11 @@ fwd_split_kernel(ScanParams p, Split x) {
             g, c16, hb, W1c, W2c);
 }
 
-__global__ void split_reset_kernel(unsigned* flags, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = 0u;
+// Clears the exchange areas (their tags) and the counter words of every head.
+__global__ void split_reset_kernel(uint4* w, size_t n4) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    w[i] = uint4{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
@@ -561,8 +606,9 @@ hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t stream) {
   x.xbuf = p.wbuf;
   x.flags = reinterpret_cast<unsigned*>(p.wbuf + static_cast<size_t>(nheads) * kHeadXFloats);
   x.nheads = nheads;
-  const int nflags = nheads * kFlagWords;
-  hipLaunchKernelGGL(split_reset_kernel, dim3((nflags + 255) / 256), dim3(256), 0, stream, x.flags, nflags);
+  const size_t n4 = static_cast<size_t>(nheads) * (kHeadXFloats + kFlagWords) / 4;
+  const unsigned rblocks = static_cast<unsigned>(n4 / 256 + 1 < 2048 ? n4 / 256 + 1 : 2048);
+  hipLaunchKernelGGL(split_reset_kernel, dim3(rblocks), dim3(256), 0, stream, reinterpret_cast<uint4*>(p.wbuf), n4);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* fn = p.gelu == TTT_GELU_TANH ? reinterpret_cast<const void*>(fwd_split_kernel<TTT_GELU_TANH>)
