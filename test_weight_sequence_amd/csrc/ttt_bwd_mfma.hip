@@ -5,12 +5,13 @@
 // Context", section 2.2, applied to the layer of "Test-Time Training(TTT)과 LLM 메모리",
 // section "TTT layer", Eq. 2/4/5 with the mini-batch rule of the review's Eq. 5).
 //
-// One workgroup of 4 waves per (batch, head) walks the chunks backwards, one wave per SIMD so
-// that each wave has the whole register file of its SIMD. Wave w owns hidden units
-// [64w, 64w + 64): its slices of the chunk-start weights (read from the forward's
-// saved copy) become bf16 MFMA operand tiles, and its slices of dW (the adjoint of the
-// chunk-start weights, carried from chunk to chunk) stay in fp32 accumulator registers for
-// the whole scan. Same register-layout rule and identity-operand transposes as the forward
+// One workgroup of 8 waves per (batch, head) walks the chunks backwards, two waves per SIMD
+// (each with half of the SIMD's registers, and each able to run while the other waits).
+// Wave w owns hidden units [32w, 32w + 32): its slices of the chunk-start weights (read from
+// the forward's saved copy) become bf16 MFMA operand tiles, and its slices of dW (the adjoint
+// of the chunk-start weights, carried from chunk to chunk) stay in fp32 accumulator registers
+// for the whole scan. The per-token phases (LayerNorm forward and backward) run on waves 0..3,
+// 16 lanes per token. Same register-layout rule and identity-operand transposes as the forward
 // MFMA kernels (ttt_mfma_common.hpp).
 //
 // Forward of one chunk, recomputed from its start weights W1, W2 (E rows carry -eta):
@@ -37,13 +38,14 @@ namespace {
 
 using namespace mfma;
 
-constexpr int NW = 4;           // waves per workgroup (one per SIMD)
+constexpr int NW = 8;           // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
 constexpr int HS = HID / NW;    // hidden units per wave
 constexpr int NHT = HS / 16;    // h tiles per wave
 constexpr int NKH = NHT / 2;    // 32-wide k-steps over a wave's hidden slice
 constexpr int TS = BC + 8;  // padded row stride of the [16 x 16] dP1 arrays
-static_assert(NW == 4 && NT == BC * 16, "LayerNorm phases: 16 lanes per token, all waves");
+constexpr int NLN = 4;          // waves 0..3 run the per-token phases: 16 lanes per token
+static_assert(NLN * 64 == BC * 16, "LayerNorm phases: 16 lanes per token");
 
 // One chunk's rows.
 struct BStage {
@@ -148,7 +150,7 @@ __device__ __forceinline__ f4 get_tile(const Partials& P, int w, int dt, int lan
 }
 
 template <int GELU_KIND>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_mfma_kernel(BwdParams p) {
   __shared__ BSmem sm;
   const int tid = threadIdx.x;
@@ -202,6 +204,7 @@ bwd_mfma_kernel(BwdParams p) {
   const int st_t = tid >> 4, st_d = (tid & 15) * 4;
   auto gload = [&](int chunk, uint2& kk, uint2& qq, uint2& vv, uint2& zz, float& e) {
     const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
+    if (tid >= NLN * 64) return;
     kk = *reinterpret_cast<const uint2*>(Kg + off);
     qq = *reinterpret_cast<const uint2*>(Qg + off);
     vv = *reinterpret_cast<const uint2*>(Vg + off);
@@ -209,6 +212,7 @@ bwd_mfma_kernel(BwdParams p) {
     e = tid < BC ? etag[chunk * BC + tid] : 0.f;
   };
   auto stage_write = [&](BStage& S, uint2 kk, uint2 qq, uint2 vv, uint2 zz, float e) {
+    if (tid >= NLN * 64) return;
     *reinterpret_cast<uint2*>(&S.K[st_t * RS + st_d]) = kk;
     *reinterpret_cast<uint2*>(&S.Q[st_t * RS + st_d]) = qq;
     *reinterpret_cast<uint2*>(&S.V[st_t * RS + st_d]) = vv;
@@ -217,6 +221,7 @@ bwd_mfma_kernel(BwdParams p) {
   };
   // Final dQ, dK of chunk cc from the per-wave partials (four elements per thread).
   auto emit_dqdk = [&](int cc) {
+    if (tid >= NLN * 64) return;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t = st_t, d = st_d + k;
@@ -336,8 +341,8 @@ bwd_mfma_kernel(BwdParams p) {
 
     // ================= B: inner-gradient LayerNorm of Z^K; dQ, dK of chunk c + 1; staging
     // of chunk c - 1 =================
-    float xk[NDT], rk_[NDT], d2k[NDT], rsk, mgxk, etak;
-    {
+    float xk[NDT], rk_[NDT], d2k[NDT], rsk = 0.f, mgxk = 0.f, etak = 0.f;
+    if (w < NLN) {
       const int t = ln_t;
       float z[NDT];
 #pragma unroll
@@ -431,7 +436,7 @@ bwd_mfma_kernel(BwdParams p) {
     __syncthreads();  // ---- 3
 
     // ================= D: output LayerNorm backward =================
-    {
+    if (w < NLN) {
       const int t = ln_t;
       float z[NDT];
 #pragma unroll
@@ -557,7 +562,7 @@ bwd_mfma_kernel(BwdParams p) {
     __syncthreads();  // ---- 5
 
     // ================= F: inner-gradient backward per token; dP1 =================
-    {
+    if (w < NLN) {
       const int t = ln_t;
       float de[NDT];
 #pragma unroll
@@ -605,7 +610,7 @@ bwd_mfma_kernel(BwdParams p) {
         flag_nonfinite(p.status, deta);
       }
     }
-    {
+    if (tid < NLN * 64) {
       // dP1 = sum of the waves' partials, as two bf16 operand layouts
       const int t = tid >> 4, u = tid & 15;
       const int r = t & 3, l = 16 * (t >> 2) + u;
