@@ -10,8 +10,8 @@
 // Wave w owns hidden units [32w, 32w + 32): its slices of the chunk-start weights (read from
 // the forward's saved copy) become bf16 MFMA operand tiles, and its slices of dW (the adjoint
 // of the chunk-start weights, carried from chunk to chunk) stay in fp32 accumulator registers
-// for the whole scan. The per-token phases (LayerNorm forward and backward) run on waves 0..3,
-// 16 lanes per token. Same register-layout rule and identity-operand transposes as the forward
+// for the whole scan. The per-token phases (LayerNorm forward and backward) run on all waves,
+// two tokens per wave and 32 lanes per token. Same register-layout rule and identity-operand transposes as the forward
 // MFMA kernels (ttt_mfma_common.hpp).
 //
 // Forward of one chunk, recomputed from its start weights W1, W2 (E rows carry -eta):
@@ -138,6 +138,21 @@ __device__ __forceinline__ float red_sum(const Partials& P, int i, int t, int c1
   for (int ww = 0; ww < NW; ++ww) s += P.v[ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
   return s;
 }
+// Per-token phases: 32 lanes per token (two tokens per wave); lane value i is d = 32 i + lane % 32.
+constexpr int PL = 2;
+__device__ __forceinline__ float sum32(float v) {
+  v = sum16(v);
+  // add the other row of the 32-lane half (lane ^ 16), through the LDS crossbar (no memory)
+  return v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ __forceinline__ LnStats ln_stats32(const float (&z)[PL], float eps) {
+  const float mu = sum32(z[0] + z[1]) * (1.0f / D);
+  float var = 0.f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) var += (z[i] - mu) * (z[i] - mu);
+  var = sum32(var) * (1.0f / D);
+  return LnStats{mu, __builtin_amdgcn_rsqf(var + eps)};
+}
 __device__ __forceinline__ void put_tile(Partials& P, int w, int dt, int lane, f4 v) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) P.v[w][dt][r][prot(r, lane)] = v[r];
@@ -179,12 +194,12 @@ bwd_mfma_kernel(BwdParams p) {
   }
 
   // LayerNorm lane mapping (all waves): token 4w + lane/16, 16 lanes per token, d = 16 i + lane%16
-  const int ln_t = 4 * w + g;
-  float gam[NDT], bet[NDT], dgam[NDT], dbet[NDT];
+  const int ln_t = 2 * w + (lane >> 5), c32 = lane & 31;
+  float gam[PL], bet[PL], dgam[PL], dbet[PL];
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) {
-    gam[i] = p.gamma[hidx * D + 16 * i + c16];
-    bet[i] = p.beta[hidx * D + 16 * i + c16];
+  for (int i = 0; i < PL; ++i) {
+    gam[i] = p.gamma[hidx * D + 32 * i + c32];
+    bet[i] = p.beta[hidx * D + 32 * i + c32];
     dgam[i] = 0.f;
     dbet[i] = 0.f;
   }
@@ -341,30 +356,30 @@ bwd_mfma_kernel(BwdParams p) {
 
     // ================= B: inner-gradient LayerNorm of Z^K; dQ, dK of chunk c + 1; staging
     // of chunk c - 1 =================
-    float xk[NDT], rk_[NDT], d2k[NDT], rsk = 0.f, mgxk = 0.f, etak = 0.f;
-    if (w < NLN) {
+    float xk[PL], rk_[PL], d2k[PL], rsk, mgxk, etak;
+    {
       const int t = ln_t;
-      float z[NDT];
+      float z[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) z[i] = red_sum(sm.red[0], i, t, c16);
-      const LnStats ls = ln_stats(z, p.eps);
-      float sg = 0.f, sgx = 0.f, gg[NDT];
+      for (int i = 0; i < PL; ++i) z[i] = red_sum(sm.red[0], 2 * i + (c32 >> 4), t, c32 & 15);
+      const LnStats ls = ln_stats32(z, p.eps);
+      float sg = 0.f, sgx = 0.f, gg[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int d = 16 * i + c16;
+      for (int i = 0; i < PL; ++i) {
+        const int d = 32 * i + c32;
         xk[i] = (z[i] - ls.mu) * ls.rs;
         rk_[i] = bf(S.K[t * RS + d]) + gam[i] * xk[i] + bet[i] - bf(S.V[t * RS + d]);
         gg[i] = 2.f * rk_[i] * gam[i];
         sg += gg[i];
         sgx += gg[i] * xk[i];
       }
-      const float mg = sum16(sg) * (1.0f / D);
-      mgxk = sum16(sgx) * (1.0f / D);
+      const float mg = sum32(sg) * (1.0f / D);
+      mgxk = sum32(sgx) * (1.0f / D);
       rsk = ls.rs;
       etak = S.eta[t];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int d = 16 * i + c16;
+      for (int i = 0; i < PL; ++i) {
+        const int d = 32 * i + c32;
         d2k[i] = (gg[i] - mg - xk[i] * mgxk) * rsk;
         const __bf16 e = (__bf16)(-etak * d2k[i]);
         sm.E2[t * RS + d] = e;
@@ -436,16 +451,16 @@ bwd_mfma_kernel(BwdParams p) {
     __syncthreads();  // ---- 3
 
     // ================= D: output LayerNorm backward =================
-    if (w < NLN) {
+    {
       const int t = ln_t;
-      float z[NDT];
+      float z[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) z[i] = red_sum(sm.red[0], i, t, c16);
-      const LnStats ls = ln_stats(z, p.eps);
-      float x[NDT], v[NDT], sv = 0.f, svx = 0.f;
+      for (int i = 0; i < PL; ++i) z[i] = red_sum(sm.red[0], 2 * i + (c32 >> 4), t, c32 & 15);
+      const LnStats ls = ln_stats32(z, p.eps);
+      float x[PL], v[PL], sv = 0.f, svx = 0.f;
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int d = 16 * i + c16;
+      for (int i = 0; i < PL; ++i) {
+        const int d = 32 * i + c32;
         x[i] = (z[i] - ls.mu) * ls.rs;
         const float o = bf(S.dZ[t * RS + d]);
         dgam[i] += o * x[i];
@@ -454,10 +469,10 @@ bwd_mfma_kernel(BwdParams p) {
         sv += v[i];
         svx += v[i] * x[i];
       }
-      const float mv = sum16(sv) * (1.0f / D), mvx = sum16(svx) * (1.0f / D);
+      const float mv = sum32(sv) * (1.0f / D), mvx = sum32(svx) * (1.0f / D);
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int d = 16 * i + c16;
+      for (int i = 0; i < PL; ++i) {
+        const int d = 32 * i + c32;
         const __bf16 e = (__bf16)((v[i] - mv - x[i] * mvx) * ls.rs);
         sm.dZQ[t * RS + d] = e;
       }
@@ -562,24 +577,24 @@ bwd_mfma_kernel(BwdParams p) {
     __syncthreads();  // ---- 5
 
     // ================= F: inner-gradient backward per token; dP1 =================
-    if (w < NLN) {
+    {
       const int t = ln_t;
-      float de[NDT];
+      float de[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) de[i] = -red_sum(sm.red[0], i, t, c16);  // adjoint of eta d2
-      float sq = 0.f, su = 0.f, sux = 0.f, u[NDT];
+      for (int i = 0; i < PL; ++i) de[i] = -red_sum(sm.red[0], 2 * i + (c32 >> 4), t, c32 & 15);  // adjoint of eta d2
+      float sq = 0.f, su = 0.f, sux = 0.f, u[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
+      for (int i = 0; i < PL; ++i) {
         sq += de[i] * d2k[i];
         u[i] = etak * de[i];
         su += u[i];
         sux += u[i] * xk[i];
       }
-      const float deta = sum16(sq) * p.eta_scale;
-      const float mu = sum16(su) * (1.0f / D), mux = sum16(sux) * (1.0f / D);
-      float suq = 0.f, dx[NDT], dr[NDT];
+      const float deta = sum32(sq) * p.eta_scale;
+      const float mu = sum32(su) * (1.0f / D), mux = sum32(sux) * (1.0f / D);
+      float suq = 0.f, dx[PL], dr[PL];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
+      for (int i = 0; i < PL; ++i) {
         suq += u[i] * d2k[i];
         const float ggi = 2.f * rk_[i] * gam[i];
         const float dg = rsk * (u[i] - mu - xk[i] * mux);
@@ -589,23 +604,23 @@ bwd_mfma_kernel(BwdParams p) {
         dbet[i] += dr[i];
         dx[i] += gam[i] * dr[i];
       }
-      const float ds = -rsk * sum16(suq);
+      const float ds = -rsk * sum32(suq);
       float sdx = 0.f, sdxx = 0.f;
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
+      for (int i = 0; i < PL; ++i) {
         sdx += dx[i];
         sdxx += dx[i] * xk[i];
       }
-      const float mdx = sum16(sdx) * (1.0f / D), mdxx = sum16(sdxx) * (1.0f / D);
+      const float mdx = sum32(sdx) * (1.0f / D), mdxx = sum32(sdxx) * (1.0f / D);
 #pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const int d = 16 * i + c16;
+      for (int i = 0; i < PL; ++i) {
+        const int d = 32 * i + c32;
         const __bf16 e = (__bf16)(rsk * (dx[i] - mdx - xk[i] * mdxx) + ds * xk[i] * (1.0f / D));
         sm.dZK[t * RS + d] = e;
         sm.dKres[t * D + d] = dr[i];
         dVg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)(-dr[i]);
       }
-      if (c16 == 0) {
+      if (c32 == 0) {
         p.deta[static_cast<size_t>(bh) * T + t0 + t] = deta;
         flag_nonfinite(p.status, deta);
       }
@@ -672,16 +687,14 @@ bwd_mfma_kernel(BwdParams p) {
   // dW of the first chunk's start = dW0 of this head; dgamma / dbeta partials
   wtiles_store<NHT>(work, work + D * HID, g, c16, hs, dW1c, dW2c);
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) {
-    // sum over the four tokens of this wave (lanes with equal lane%16)
+  for (int i = 0; i < PL; ++i) {
+    // sum over the two tokens of this wave (lanes with equal lane%32)
     float a = dgam[i], b = dbet[i];
-    a += __shfl_xor(a, 16, 64);
     a += __shfl_xor(a, 32, 64);
-    b += __shfl_xor(b, 16, 64);
     b += __shfl_xor(b, 32, 64);
-    if (g == 0) {
-      sm.dgb[w][0][16 * i + c16] = a;
-      sm.dgb[w][1][16 * i + c16] = b;
+    if (lane < 32) {
+      sm.dgb[w][0][32 * i + c32] = a;
+      sm.dgb[w][1][32 * i + c32] = b;
     }
   }
   __syncthreads();
