@@ -79,11 +79,15 @@ enum {
   TTT_FORCE_GENERIC = 1 << 1, /* use the portable fp32 kernel even where a tuned one exists */
   TTT_ONE_WG_PER_HEAD = 1 << 2, /* tuned forward: one workgroup per (batch, head) instead of a
                                    producer/consumer pair of workgroups                      */
-  TTT_OUTPUT_KEY = 1 << 3 /* output rule of Eq. 9 in the E2E paper review, section 2.4.2:
+  TTT_OUTPUT_KEY = 1 << 3, /* output rule of Eq. 9 in the E2E paper review, section 2.4.2:
                              z_t = f(K_t; W) with W the weights the token's gradient is taken at
                              (the chunk start; W_{t-1} when chunk = 1), i.e. the key-side
                              prediction reused as the output. Q does not enter it (dQ = 0). Runs on
                              the portable kernels. */
+  TTT_FORCE_DEVICE_SCOPE = 1 << 4 /* tuned forward: the workgroups of a head hand partial results
+                                     to each other with device-scope atomics and fences even
+                                     when they share an XCD (slower). This is the path taken when
+                                     they do not; the flag lets a test run it. */
 };
 /* op codes for ttt_workspace_size */
 enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2 };
@@ -96,7 +100,8 @@ typedef struct {
   int32_t chunk;     /* mini-batch size b, 1 <= b <= 16; T % b == 0 for scans          */
   int32_t io_dtype;  /* TTT_F32 or TTT_BF16 for Q, K, V, Z, dQ, dK, dV, dZ             */
   int32_t gelu;      /* TTT_GELU_ERF (exact) or TTT_GELU_TANH                          */
-  int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD       */
+  int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD |
+                        TTT_OUTPUT_KEY | TTT_FORCE_DEVICE_SCOPE                       */
   float ln_eps;      /* LayerNorm epsilon inside the square root (e.g. 1e-6)           */
   float eta_scale;   /* multiplies every eta_t (1 = plain sum; 1/b = averaged sum)     */
 } ttt_config;

@@ -23,7 +23,8 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   if (c->kind != TTT_LINEAR && c->kind != TTT_MLP) return TTT_ERR_UNSUPPORTED;
   if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
   if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH) return TTT_ERR_UNSUPPORTED;
-  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD | TTT_OUTPUT_KEY))
+  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD | TTT_OUTPUT_KEY |
+                   TTT_FORCE_DEVICE_SCOPE))
     return TTT_ERR_ARG;
   if (c->B < 1 || c->H < 1 || c->d < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
   if (need_T && c->T < 1) return TTT_ERR_SHAPE;

@@ -706,7 +706,7 @@ fwd_mfma_pair_kernel(ScanParams p, Pair q) {
     __builtin_amdgcn_s_sleep(2);
   }
   if (other == 0 && x.tid == 0) atomicOr(p.status, kStatusTimeout);
-  const bool local = other == xcc + 1;
+  const bool local = other == xcc + 1 && !(p.flags & TTT_FORCE_DEVICE_SCOPE);
   if (producer) {
     if (local)
       producer_body<GELU_KIND, true>(p, x, sm.p);

@@ -238,7 +238,7 @@ fwd_split_kernel(ScanParams p, Split x) {
         if (v == 0) atomicOr(p.status, kStatusTimeout);
         same = same && v == xcc + 1;
       }
-      sh_local = same ? 1u : 0u;
+      sh_local = same && !(p.flags & TTT_FORCE_DEVICE_SCOPE) ? 1u : 0u;
     }
     __syncthreads();
     m.local = sh_local != 0;

@@ -22,6 +22,7 @@ TTT_LINEAR, TTT_MLP = 0, 1
 TTT_F32, TTT_BF16 = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
 TTT_W0_PER_SEQ, TTT_FORCE_GENERIC, TTT_ONE_WG_PER_HEAD, TTT_OUTPUT_KEY = 1, 2, 4, 8
+TTT_FORCE_DEVICE_SCOPE = 16
 TTT_OP_FWD, TTT_OP_BWD, TTT_OP_DECODE = 0, 1, 2
 
 STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE",
@@ -106,6 +107,7 @@ class Config:
     force_generic: bool = False
     one_wg_per_head: bool = False  # tuned forward without the producer/consumer pairing
     output_key: bool = False       # Eq. 9 output rule: z_t = f(K_t; W at the chunk start)
+    device_scope: bool = False     # tuned forward: device-scope hand-offs between workgroups
     ln_eps: float = 1e-6
     eta_scale: float = 1.0
 
@@ -113,7 +115,8 @@ class Config:
         flags = (TTT_W0_PER_SEQ if self.w0_per_seq else 0) | \
                 (TTT_FORCE_GENERIC if self.force_generic else 0) | \
                 (TTT_ONE_WG_PER_HEAD if self.one_wg_per_head else 0) | \
-                (TTT_OUTPUT_KEY if self.output_key else 0)
+                (TTT_OUTPUT_KEY if self.output_key else 0) | \
+                (TTT_FORCE_DEVICE_SCOPE if self.device_scope else 0)
         return CConfig(TTT_MLP if self.kind == "mlp" else TTT_LINEAR, self.B, self.H, self.T,
                        self.d, self.hidden if self.kind == "mlp" else self.d, self.chunk,
                        TTT_BF16 if self.io == "bf16" else TTT_F32,

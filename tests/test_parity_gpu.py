@@ -480,3 +480,27 @@ def test_nonfinite_input_sets_status(force_generic):
     clean = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
     _run(cfg, to_dev(clean), workspace=ws)
     assert ops.read_status(ws) == 0
+
+
+@pytest.mark.parametrize("kernel", ["pair", "split"])
+def test_device_scope_handoff(kernel):
+    """The tuned forwards with their cross-workgroup hand-offs forced onto the device-scope
+    path (atomics and fences, as when the workgroups of a head sit on different XCDs): same
+    kernel, status clean, every head against the oracle, and the same result as the default
+    same-XCD path up to bf16 noise."""
+    w = WORKLOADS[3] if kernel == "pair" else WORKLOADS[4]
+    B, H, T = (2, 5, 96) if kernel == "pair" else (1, 3, 64)
+    inp = make_inputs(w, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
+    cfg = ops_config(w, B=B, H=H, T=T, device_scope=True)
+    name = "ttt_fwd_mfma_pair_d64" if kernel == "pair" else "ttt_fwd_mfma_split_d128"
+    assert ops.fwd_kernel_name(cfg) == name
+    note(f"device-scope hand-off {name} B={B} H={H} T={T}")
+    d = to_dev(inp)
+    res = _run(cfg, d, want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    _check_heads(res, inp, [(b, h) for b in range(B) for h in range(H)], w, TOL["bf16"])
+    ref = _run(ops_config(w, B=B, H=H, T=T), d)
+    torch.cuda.synchronize()
+    # the two paths move the same values; only the hand-off mechanism differs
+    assert torch.equal(res["Z"], ref["Z"])
