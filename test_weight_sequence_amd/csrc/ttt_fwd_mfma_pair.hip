@@ -364,12 +364,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       akR[ht] = cvt4(a);
     }
     out.ak = cat(akR[0], akR[1]);
-    // scheduling hint: issue the 16 update MFMAs one at a time between runs of 8 VALU
+    // scheduling hint: issue the 16 update MFMAs one at a time between runs of 4 VALU
     // instructions of the GELU above, so the matrix unit works while the VALU does
+    // (runs of 2, 3, 5, 6 or 8 measured slower)
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     bf16x4 W1b[NDT][NHT];
     bf16x8 W2b8[NDT];
