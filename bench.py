@@ -139,13 +139,14 @@ def _device_inputs(w, dev, with_dz=False):
             for k, v in inp.items()}
 
 
-def bench_scan_fwd(args, wid: int) -> dict:
+def bench_scan_fwd(args, wid: str) -> dict:
     """One step = one ttt_scan_fwd over the whole batch."""
     import ctypes
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS
     w = WORKLOADS[wid]
+    headline = wid == "ttt_mlp_bf16_d64_T8k"
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
                      io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
     kernel = ops.fwd_kernel_name(cfg)
@@ -178,18 +179,18 @@ def bench_scan_fwd(args, wid: int) -> dict:
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
     io_bytes = 2 if w.io == "bf16" else 4
     metric = ("TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)"
-              if wid == 3 else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}")
+              if headline else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}")
     out = _base_record(args, metric, units / (ms_step * 1e-3), ms_step, w, kernel,
                        "bf16" if mfma else "f32")
     out["roofline"] = {
         "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
         "unit": "TFLOP/s", "frac": achieved / peak,
-        "traffic": _traffic(kernel, units) if wid == 3 else None,
+        "traffic": _traffic(kernel, units) if headline else None,
         "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
         "algorithmic_bytes_per_launch": units * bytes_per_token_head(
             w.d, io_bytes, 2 * w.d * w.hidden, w.T)}
     if not args.no_cpu_baseline:
-        if wid == 3:
+        if headline:
             out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_T)
         else:
             out["cpu_baseline"] = cpu_baseline(w, 1, 2048)
@@ -210,7 +211,7 @@ def bench_scan_bwd(args) -> dict:
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS
-    w = WORKLOADS[5]
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
                      io=w.io)
     kernel = ops.bwd_kernel_name(cfg)
@@ -251,12 +252,12 @@ def bench_scan_bwd(args) -> dict:
 
 def bench_decode(args) -> dict:
     """One step = one full chunk of decode calls (16 tokens for every (batch, head) of the
-    config-3 shape), so every step includes one commit."""
+    d = 64 bf16 MLP shape), so every step includes one commit."""
     import ctypes
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     b = w.chunk
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=b, d=w.d, hidden=w.hidden, chunk=b, io=w.io)
     dev = torch.device("cuda:0")
@@ -337,7 +338,7 @@ def main():
     if args.warmup is None:
         args.warmup = 1 if long_run else 5
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the scan's heads would be "
+        print("bench.py: runs on exactly one GPU; the scan's heads would be "
               "sharded across GPUs with no communication, which is not built here.",
               file=sys.stderr)
         sys.exit(2)
@@ -362,9 +363,9 @@ def main():
         return
 
     if args.workload == "scan_fwd":
-        out = bench_scan_fwd(args, 3)
+        out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k")
     elif args.workload == "scan_fwd_d128":
-        out = bench_scan_fwd(args, 4)
+        out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
     elif args.workload == "scan_bwd":
         out = bench_scan_bwd(args)
     else:

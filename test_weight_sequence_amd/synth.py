@@ -43,17 +43,17 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads of the scan (sizes, dtypes and distributions as specified
-# for this build); seed 1000 + index.
+# The five seeded workloads of the scan, keyed by name (shapes, dtypes and value
+# distributions).
 WORKLOADS = {
-    1: Workload("ttt_mlp_fp32_d16", "mlp", 1, 1, 256, 16, 64, 16, "f32", 0.1, "normal", seed=1001),
-    2: Workload("ttt_linear_fp32_d64", "linear", 4, 12, 2048, 64, 64, 16, "f32", 1.0,
+    "ttt_mlp_fp32_d16": Workload("ttt_mlp_fp32_d16", "mlp", 1, 1, 256, 16, 64, 16, "f32", 0.1, "normal", seed=1001),
+    "ttt_linear_fp32_d64": Workload("ttt_linear_fp32_d64", "linear", 4, 12, 2048, 64, 64, 16, "f32", 1.0,
                 "identity_plus", seed=1002),
-    3: Workload("ttt_mlp_bf16_d64_T8k", "mlp", 8, 12, 8192, 64, 256, 16, "bf16", 0.1, "normal",
+    "ttt_mlp_bf16_d64_T8k": Workload("ttt_mlp_bf16_d64_T8k", "mlp", 8, 12, 8192, 64, 256, 16, "bf16", 0.1, "normal",
                 seed=1003),
-    4: Workload("ttt_mlp_bf16_d128_T128k", "mlp", 1, 24, 131072, 128, 512, 16, "bf16", 0.1,
+    "ttt_mlp_bf16_d128_T128k": Workload("ttt_mlp_bf16_d128_T128k", "mlp", 1, 24, 131072, 128, 512, 16, "bf16", 0.1,
                 "normal", drift=0.999, seed=1004),
-    5: Workload("ttt_mlp_bf16_d64_fwd_bwd", "mlp", 4, 16, 8192, 64, 256, 16, "bf16", 0.1,
+    "ttt_mlp_bf16_d64_fwd_bwd": Workload("ttt_mlp_bf16_d64_fwd_bwd", "mlp", 4, 16, 8192, 64, 256, 16, "bf16", 0.1,
                 "normal", seed=1005),
 }
 

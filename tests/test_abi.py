@@ -36,7 +36,7 @@ def test_abi_version_and_status_strings():
     assert L.ttt_status_str(99).decode() == "unknown status"
 
 
-def cfg3(**kw):
+def mlp_d64(**kw):
     base = dict(kind="mlp", B=8, H=12, T=8192, d=64, hidden=256, chunk=16, io="bf16")
     base.update(kw)
     return ops.Config(**base)
@@ -61,28 +61,28 @@ def cfg3(**kw):
     (dict(eta_scale=float("inf")), 9),
 ])
 def test_validate(kw, code):
-    assert ops.validate(cfg3(**kw)) == code
+    assert ops.validate(mlp_d64(**kw)) == code
 
 
 def test_validate_bad_enums_and_flags():
     L = ops.lib()
-    c = cfg3().c()
+    c = mlp_d64().c()
     c.io_dtype = 7
     assert L.ttt_validate(ctypes.byref(c)) == 3
-    c = cfg3().c()
+    c = mlp_d64().c()
     c.kind = 5
     assert L.ttt_validate(ctypes.byref(c)) == 4
-    c = cfg3().c()
+    c = mlp_d64().c()
     c.gelu = 3
     assert L.ttt_validate(ctypes.byref(c)) == 4
-    c = cfg3().c()
+    c = mlp_d64().c()
     c.flags = 1 << 7
     assert L.ttt_validate(ctypes.byref(c)) == 9
     assert L.ttt_validate(None) == 1
 
 
 def test_workspace_and_saved_sizes():
-    c = cfg3()
+    c = mlp_d64()
     assert ops.workspace_size(c, ops.TTT_OP_DECODE) == 256
     gen = ops.workspace_size(ops.Config(**{**c.__dict__, "force_generic": True}))
     assert gen == 256 + 8 * 12 * 2 * 64 * 256 * 4
@@ -93,22 +93,22 @@ def test_workspace_and_saved_sizes():
     with pytest.raises(ops.TTTError):
         ops.workspace_size(c, 17)
     with pytest.raises(ops.TTTError):
-        ops.workspace_size(cfg3(T=3))
+        ops.workspace_size(mlp_d64(T=3))
 
 
 def test_kernel_selection_names():
-    assert ops.fwd_kernel_name(cfg3(force_generic=True)) == "ttt_fwd_generic"
-    assert ops.fwd_kernel_name(cfg3(io="f32")) == "ttt_fwd_generic"
-    assert ops.fwd_kernel_name(cfg3(T=7)) == ""
-    assert ops.bwd_kernel_name(cfg3(io="f32")) == "ttt_bwd_generic"
-    assert ops.bwd_kernel_name(cfg3(T=7)) == ""
-    assert ops.decode_kernel_name(cfg3()) == "ttt_decode_stream_d64"
-    assert ops.decode_kernel_name(cfg3(force_generic=True)) == "ttt_decode_generic"
+    assert ops.fwd_kernel_name(mlp_d64(force_generic=True)) == "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(mlp_d64(io="f32")) == "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(mlp_d64(T=7)) == ""
+    assert ops.bwd_kernel_name(mlp_d64(io="f32")) == "ttt_bwd_generic"
+    assert ops.bwd_kernel_name(mlp_d64(T=7)) == ""
+    assert ops.decode_kernel_name(mlp_d64()) == "ttt_decode_stream_d64"
+    assert ops.decode_kernel_name(mlp_d64(force_generic=True)) == "ttt_decode_generic"
     # the Eq. 9 output rule runs on the portable kernels
-    assert ops.fwd_kernel_name(cfg3(output_key=True)) == "ttt_fwd_generic"
-    assert ops.bwd_kernel_name(cfg3(output_key=True)) == "ttt_bwd_generic"
-    assert ops.decode_kernel_name(cfg3(output_key=True)) == "ttt_decode_generic"
-    assert ops.validate(cfg3(output_key=True)) == 0
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True)) == "ttt_fwd_generic"
+    assert ops.bwd_kernel_name(mlp_d64(output_key=True)) == "ttt_bwd_generic"
+    assert ops.decode_kernel_name(mlp_d64(output_key=True)) == "ttt_decode_generic"
+    assert ops.validate(mlp_d64(output_key=True)) == 0
 
 
 class _FakeTensor:
@@ -134,19 +134,19 @@ def _fwd_call(cfg, ptrs, ws_bytes=1 << 40, W0=(0x10000, 0x20000)):
 
 
 def test_fwd_rejects_null_misaligned_and_small_workspace():
-    c = cfg3()
+    c = mlp_d64()
     good = [0x1000 * (i + 1) for i in range(6)]
     assert _fwd_call(c, [0] + good[1:]) == 1
     assert _fwd_call(c, good, W0=(0x10000, 0)) == 1
     assert _fwd_call(c, [0x1008] + good[1:]) == 5
     assert _fwd_call(c, good, ws_bytes=16) == 6
-    assert _fwd_call(cfg3(T=17), good) == 2
+    assert _fwd_call(mlp_d64(T=17), good) == 2
 
 
 def test_decode_rejects_bad_position():
     L = ops.lib()
     P = ctypes.c_void_p
-    c = cfg3()
+    c = mlp_d64()
     w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
     args = [P(0x1000 * (i + 1)) for i in range(6)]
     for pos in (-1, 16):
@@ -159,7 +159,7 @@ def test_decode_rejects_bad_position():
 def test_bwd_rejects_missing_saved_buffer():
     L = ops.lib()
     P = ctypes.c_void_p
-    c = cfg3()
+    c = mlp_d64()
     w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
     args = [P(0x1000 * (i + 1)) for i in range(6)]
     code = L.ttt_scan_bwd(ctypes.byref(c.c()), *args, None, P(0x40000), None, P(0x50000),

@@ -114,12 +114,12 @@ def test_bwd_key_output_matches_oracle(kind, d, chunk, T):
         assert rel_l2(a, b) <= TOL["f32"], ("dW0", i)
 
 
-def test_bwd_cfg1_fp32_full_T():
-    w = WORKLOADS[1]
+def test_bwd_mlp_fp32_d16_full_T():
+    w = WORKLOADS["ttt_mlp_fp32_d16"]
     inp = make_inputs(w, with_dz=True)
     dZ = inp.pop("dZ")
     cfg = ops.Config(kind="mlp", B=1, H=1, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk, io="f32")
-    note("bwd cfg1 full")
+    note("bwd mlp fp32 d16 full")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     ora = _oracle_grads(inp, dZ, None, "mlp", w.chunk, False)
     _compare(gpu, ora, TOL["f32"])
@@ -130,16 +130,16 @@ BWD_KERNELS = {"mfma": "ttt_bwd_mfma_d64", "generic": "ttt_bwd_generic"}
 
 @pytest.mark.parametrize("kernel", ["mfma", "generic"])
 @pytest.mark.parametrize("T", [64, 512])
-def test_bwd_cfg5_shape_bf16(T, kernel):
-    """Config-5 head shape (d=64, hidden=256, bf16 I/O) through the tuned forward and each
+def test_bwd_mlp_bf16_d64_shape(T, kernel):
+    """The d=64, hidden=256, bf16 I/O head shape through the tuned forward and each
     backward kernel, two heads of two sequences, against the oracle."""
-    w = WORKLOADS[5]
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     inp = make_inputs(w, batch_idx=[0, 3], head_idx=[2, 15], T=T, with_dz=True)
     dZ = inp.pop("dZ")
     cfg = ops.Config(kind="mlp", B=2, H=2, T=T, d=w.d, hidden=w.hidden, chunk=w.chunk, io="bf16",
                      force_generic=kernel == "generic")
     assert ops.bwd_kernel_name(cfg) == BWD_KERNELS[kernel]
-    note(f"bwd cfg5 shape T={T} fwd={ops.fwd_kernel_name(cfg)} bwd={ops.bwd_kernel_name(cfg)}")
+    note(f"bwd mlp bf16 d64 shape T={T} fwd={ops.fwd_kernel_name(cfg)} bwd={ops.bwd_kernel_name(cfg)}")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     ora = _oracle_grads(inp, dZ, None, "mlp", w.chunk, False)
     _compare(gpu, ora, TOL["bf16"])
@@ -168,16 +168,16 @@ def test_bwd_mfma_variants(T, per_seq, with_dwt, gelu, B, H):
     _compare(gpu, ora, TOL["bf16"])
 
 
-def test_bwd_cfg5_full_size_sampled_heads():
-    """Full config-5 launch (B=4, H=16, T=8192) of the tuned backward; the oracle checks the
+def test_bwd_mlp_bf16_d64_B4H16_sampled_heads():
+    """Full launch at B=4, H=16, T=8192 of the tuned backward; the oracle checks the
     per-token gradients (dQ, dK, dV, deta) of two heads at full length."""
-    w = WORKLOADS[5]
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     inp = make_inputs(w, with_dz=True)
     dZ = inp.pop("dZ")
     cfg = ops.Config(kind="mlp", B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
                      io="bf16")
     assert ops.bwd_kernel_name(cfg) == "ttt_bwd_mfma_d64"
-    note("bwd cfg5 full size, sampled heads")
+    note("bwd B=4 H=16 T=8192, sampled heads")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     torch.cuda.synchronize()
     for b, h in [(1, 4), (3, 13)]:
@@ -189,16 +189,16 @@ def test_bwd_cfg5_full_size_sampled_heads():
             assert e <= TOL["bf16"], (b, h, k, e)
 
 
-def test_bwd_cfg5_full_size_runs_and_is_finite():
-    """Full config-5 size (B=4, H=16, T=8192): the backward runs, its outputs are finite
+def test_bwd_mlp_bf16_d64_B4H16_runs_and_is_finite():
+    """Full size B=4, H=16, T=8192: the backward runs, its outputs are finite
     and the gradients are deterministic run to run."""
-    w = WORKLOADS[5]
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     inp = make_inputs(w, with_dz=True)
     dZ = inp.pop("dZ").cuda()
     cfg = ops.Config(kind="mlp", B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
                      io="bf16")
     d = to_dev(inp)
-    note("bwd cfg5 full size")
+    note("bwd B=4 H=16 T=8192")
     fwd, g1 = _gpu_grads(cfg, d, dZ, None)
     g2 = ops.scan_bwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["gamma"], d["beta"], fwd["saved"], dZ)
     torch.cuda.synchronize()
@@ -213,7 +213,7 @@ def test_bwd_cfg5_full_size_runs_and_is_finite():
 def test_saved_chunk_start_weights(variant):
     """The forward's saved buffer holds W0 at chunk 0 exactly and the carried weights at
     every later chunk start (W at chunk c equals W_T of a scan over the first c chunks)."""
-    w = WORKLOADS[5]
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     T = 64
     inp = make_inputs(w, batch_idx=[0, 1], head_idx=[3, 9], T=T)
     cfg = ops.Config(kind="mlp", B=2, H=2, T=T, d=w.d, hidden=w.hidden, chunk=w.chunk, io="bf16",

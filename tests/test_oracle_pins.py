@@ -266,8 +266,8 @@ def test_theorem1_random_and_online_breaks_it():
     lin = torch.einsum("ntd,nsd->nts", q, k).tril() @ v
     cfg = OracleConfig(kind="linear", chunk=T, layer_norm=False, residual=False)
     assert rel(scan(q, k, v, eta, W0, None, None, cfg)[0], lin) <= 1e-13
-    cfg1 = OracleConfig(kind="linear", chunk=1, layer_norm=False, residual=False)
-    assert rel(scan(q, k, v, eta, W0, None, None, cfg1)[0], lin) > 1e-3
+    online = OracleConfig(kind="linear", chunk=1, layer_norm=False, residual=False)
+    assert rel(scan(q, k, v, eta, W0, None, None, online)[0], lin) > 1e-3
 
 
 def test_golden_delta_rule():
@@ -468,7 +468,7 @@ def test_key_output_outer_grads_finite_differences():
 # ---------------------------------------------------------------------------
 
 def test_synth_is_deterministic_and_subset_consistent():
-    w = WORKLOADS[3].with_(T=64)
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"].with_(T=64)
     a = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 5])
     b = make_inputs(w, batch_idx=[1], head_idx=[5], T=32)
     c = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 5])
@@ -481,7 +481,7 @@ def test_synth_is_deterministic_and_subset_consistent():
 
 
 def test_synth_distributions():
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     inp = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=4096)
     q = inp["Q"].double()
     assert abs(q.var().item() * w.d - 1.0) < 0.02
@@ -490,7 +490,7 @@ def test_synth_distributions():
     assert abs(eta.mean().item() - 0.5 * w.eta_base) < 0.01 * w.eta_base
     assert abs(inp["W0"][0].double().std().item() - 0.02) < 0.001
     # AR(1) drift: lag-1 correlation close to rho, marginal variance kept at 1/d
-    w4 = WORKLOADS[4]
+    w4 = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     k = make_inputs(w4, batch_idx=[0], head_idx=[0], T=8192)["K"].double()[0, 0]
     corr = (k[1:] * k[:-1]).mean() / (k * k).mean()
     assert abs(corr.item() - 0.999) < 0.002
@@ -498,7 +498,7 @@ def test_synth_distributions():
 
 
 def test_flatten_heads_broadcasts_w0_over_batch():
-    w = WORKLOADS[2].with_(T=32)
+    w = WORKLOADS["ttt_linear_fp32_d64"].with_(T=32)
     inp = make_inputs(w, batch_idx=[0, 2], head_idx=[1, 3, 4])
     flat = flatten_heads(inp)
     assert flat["Q"].shape == (6, 32, 64)

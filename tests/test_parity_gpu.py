@@ -46,17 +46,17 @@ def _variant_config(w, kernel, **kw):
     return cfg
 
 
-def test_cfg1_mlp_fp32_full():
-    w = WORKLOADS[1]
-    note(f"cfg1 full {w}")
+def test_mlp_fp32_d16_full():
+    w = WORKLOADS["ttt_mlp_fp32_d16"]
+    note(f"mlp fp32 d16 full {w}")
     inp = make_inputs(w)
     res = _run(ops_config(w), to_dev(inp), want_loss=True)
     _check_heads(res, inp, [(0, 0)], w, TOL["f32"])
 
 
-def test_cfg2_linear_fp32_full():
-    w = WORKLOADS[2]
-    note(f"cfg2 full {w}")
+def test_linear_fp32_d64_full():
+    w = WORKLOADS["ttt_linear_fp32_d64"]
+    note(f"linear fp32 d64 full {w}")
     inp = make_inputs(w)
     res = _run(ops_config(w), to_dev(inp), want_loss=True)
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
@@ -64,11 +64,11 @@ def test_cfg2_linear_fp32_full():
 
 
 @pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
-def test_cfg3_full_size_sampled_heads(kernel):
-    """Full config-3 launch (B=8, H=12, T=8192); the oracle checks three heads at full T."""
-    w = WORKLOADS[3]
+def test_mlp_bf16_d64_T8k_sampled_heads(kernel):
+    """Full launch at B=8, H=12, T=8192; the oracle checks three heads at full T."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     cfg = _variant_config(w, kernel)
-    note(f"cfg3 full {kernel} -> {ops.fwd_kernel_name(cfg)}")
+    note(f"mlp bf16 d64 T8k full {kernel} -> {ops.fwd_kernel_name(cfg)}")
     inp = make_inputs(w)
     res = _run(cfg, to_dev(inp), want_loss=True)
     torch.cuda.synchronize()
@@ -76,45 +76,45 @@ def test_cfg3_full_size_sampled_heads(kernel):
 
 
 @pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
-def test_cfg3_all_heads_short(kernel):
-    w = WORKLOADS[3]
+def test_mlp_bf16_d64_all_heads_short(kernel):
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     cfg = _variant_config(w, kernel, T=256)
-    note(f"cfg3 T=256 all heads {kernel}")
+    note(f"mlp bf16 d64 T=256 all heads {kernel}")
     inp = make_inputs(w, T=256)
     res = _run(cfg, to_dev(inp), want_loss=True)
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     _check_heads(res, inp, pairs, w, TOL["bf16"])
 
 
-CFG4_KERNELS = {"split": ({}, "ttt_fwd_mfma_split_d128"),
+D128_KERNELS = {"split": ({}, "ttt_fwd_mfma_split_d128"),
                 "generic": (dict(force_generic=True), "ttt_fwd_generic")}
 
 
 @pytest.mark.parametrize("kernel", ["split", "generic"])
-def test_cfg4_d128_reduced_T(kernel):
-    """Config-4 head shape (d=128, hidden=512, AR(1) drifting inputs) on two heads, T=512,
+def test_mlp_bf16_d128_reduced_T(kernel):
+    """The d=128, hidden=512 head shape (AR(1) drifting inputs) on two heads, T=512,
     through the split kernel (four workgroups per head) and the portable one."""
-    w = WORKLOADS[4]
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     inp = make_inputs(w, head_idx=[0, 23], T=512)
-    flags, name = CFG4_KERNELS[kernel]
+    flags, name = D128_KERNELS[kernel]
     cfg = ops_config(w, T=512, H=2, **flags)
     assert ops.fwd_kernel_name(cfg) == name
-    note(f"cfg4 d=128 T=512 heads 0,23 {name}")
+    note(f"mlp bf16 d=128 T=512 heads 0,23 {name}")
     res = _run(cfg, to_dev(inp), want_loss=True)
     torch.cuda.synchronize()
     assert ops.read_status(res["workspace"]) == 0
     _check_heads(res, inp, [(0, 0), (0, 1)], w, TOL["bf16"])
 
 
-def test_cfg4_full_size_sampled_heads_prefix():
-    """Full config-4 launch (B=1, H=24, T=131072) of the split kernel: the end state of every
+def test_mlp_bf16_d128_T128k_sampled_heads_prefix():
+    """Full launch at B=1, H=24, T=131072 of the split kernel: the end state of every
     head is finite, and for two heads z and the per-token loss of the first 4096 tokens
     (which depend only on that prefix) match the oracle."""
-    w = WORKLOADS[4]
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     inp = make_inputs(w)
     cfg = ops_config(w)
     assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
-    note("cfg4 full size, split kernel")
+    note("mlp bf16 d128 T128k full size, split kernel")
     res = _run(cfg, to_dev(inp), want_loss=True)
     torch.cuda.synchronize()
     assert ops.read_status(res["workspace"]) == 0
@@ -155,7 +155,7 @@ def test_split_partial_group_tanh_per_seq():
 def test_split_more_heads_than_one_launch():
     """72 heads of the d=128 shape: more than one launch of the split kernel holds on a
     256-CU device (64 heads); heads from both launches against the oracle."""
-    w = WORKLOADS[4]
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     B, H, T = 9, 8, 32
     inp = make_inputs(w.with_(B=9, H=8), T=T)
     cfg = ops_config(w, T=T, B=B, H=H)
@@ -170,7 +170,7 @@ def test_split_more_heads_than_one_launch():
 def test_split_saved_chunk_start_weights():
     """The split kernel's saved buffer: W0 exactly at chunk 0, and at chunk 2 the W_T of a
     scan over the first two chunks."""
-    w = WORKLOADS[4]
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     T = 64
     inp = make_inputs(w, head_idx=[3, 4, 9], T=T)
     cfg = ops_config(w, T=T, H=3)
@@ -191,10 +191,10 @@ def test_split_saved_chunk_start_weights():
 
 
 @pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
-def test_cfg5_fwd_full_size_sampled_heads(kernel):
-    w = WORKLOADS[5]
+def test_mlp_bf16_d64_B4H16_fwd_sampled_heads(kernel):
+    w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     cfg = _variant_config(w, kernel)
-    note(f"cfg5 fwd full {kernel}")
+    note(f"mlp bf16 d64 B=4 H=16 fwd full {kernel}")
     inp = make_inputs(w)
     res = _run(cfg, to_dev(inp))
     _check_heads(res, inp, [(1, 2), (3, 15)], w, TOL["bf16"])
@@ -204,7 +204,7 @@ def test_cfg5_fwd_full_size_sampled_heads(kernel):
 def test_pair_partial_groups_all_heads(B, H, T):
     """Head counts that leave part of the last group of 8 pairs empty, single-chunk and
     few-chunk scans (fewer chunks than ring slots): every head against the oracle."""
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     cfg = _variant_config(w, "pair", B=B, H=H, T=T)
     note(f"pair partial groups B={B} H={H} T={T}")
     inp = make_inputs(w, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
@@ -216,7 +216,7 @@ def test_pair_partial_groups_all_heads(B, H, T):
 
 def test_pair_not_used_above_128_heads():
     """More than 128 (batch, head) pairs: the host picks one workgroup per head."""
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     cfg = ops_config(w, B=9, H=16, T=64)
     assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_d64"
     note("144 heads T=64")
@@ -299,7 +299,7 @@ def test_edge_shapes_fp32(kind, d, chunk, T, gelu, eta_scale, per_seq):
 
 
 def test_eta_zero_gives_initial_map():
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     inp = make_inputs(w, batch_idx=[0, 1], head_idx=[0, 1, 2], T=64)
     inp["eta"] = torch.zeros_like(inp["eta"])
     cfg = ops_config(w, T=64, B=2, H=3)
@@ -316,7 +316,7 @@ def test_eta_zero_gives_initial_map():
 
 
 def test_split_scan_equals_unsplit():
-    w = WORKLOADS[1]
+    w = WORKLOADS["ttt_mlp_fp32_d16"]
     inp = make_inputs(w)
     d = to_dev(inp)
     cfg = ops_config(w)
@@ -342,7 +342,7 @@ def _tok(x, t):
     return x[:, :, t].clone()
 
 
-@pytest.mark.parametrize("wid", [1, 2])
+@pytest.mark.parametrize("wid", ["ttt_mlp_fp32_d16", "ttt_linear_fp32_d64"])
 def test_decode_loop_equals_scan(wid):
     w = WORKLOADS[wid]
     T = 64
@@ -350,7 +350,7 @@ def test_decode_loop_equals_scan(wid):
     B, H = inp["Q"].shape[:2]
     cfg = ops_config(w, T=T, B=B, H=H)
     d = to_dev(inp)
-    note(f"decode loop cfg{wid}")
+    note(f"decode loop {wid}")
     scan_res = _run(cfg, d)
     Ws = tuple(x.unsqueeze(0).expand(B, *x.shape).contiguous().clone() for x in d["W0"])
     acc = tuple(torch.zeros_like(x) for x in Ws)
@@ -370,9 +370,9 @@ def test_decode_loop_equals_scan(wid):
 @pytest.mark.parametrize("io,gelu", [("bf16", "erf"), ("f32", "tanh")])
 def test_decode_stream_equals_oracle(io, gelu):
     """The tuned decode kernel (MLP, d=64) and the portable one: 48 decode steps (three
-    commits) over 2 x 3 heads of the config-3 distributions, against the oracle scan of the
+    commits) over 2 x 3 heads of the d = 64 bf16 MLP workload's distributions, against the oracle scan of the
     same tokens (z of every token, the committed weights)."""
-    w = WORKLOADS[3].with_(io=io)
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"].with_(io=io)
     T, bi, hi = 48, [0, 5], [1, 6, 11]
     inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
     B, H = len(bi), len(hi)
@@ -401,7 +401,8 @@ def test_decode_stream_equals_oracle(io, gelu):
             assert torch.count_nonzero(a).item() == 0
 
 
-@pytest.mark.parametrize("wid,kind", [(1, "mlp"), (2, "linear"), (3, "mlp")])
+@pytest.mark.parametrize("wid,kind", [("ttt_mlp_fp32_d16", "mlp"), ("ttt_linear_fp32_d64", "linear"),
+                                      ("ttt_mlp_bf16_d64_T8k", "mlp")])
 def test_key_output_forward_and_decode(wid, kind):
     """The Eq. 9 output rule (z_t = f(K_t; W at the chunk start)) through the portable forward
     and the portable decode, against the oracle with the same rule; the per-token loss equals
@@ -413,7 +414,7 @@ def test_key_output_forward_and_decode(wid, kind):
     B, H = len(bi), len(hi)
     cfg = ops_config(w, T=T, B=B, H=H, output_key=True)
     assert ops.fwd_kernel_name(cfg) == "ttt_fwd_generic"
-    note(f"key output cfg{wid}")
+    note(f"key output {wid}")
     d = to_dev(inp)
     res = _run(cfg, d, want_loss=True)
     torch.cuda.synchronize()
@@ -431,7 +432,7 @@ def test_key_output_forward_and_decode(wid, kind):
 
 def test_scan_then_decode_continues_the_sequence():
     """Prefill T0 tokens with the scan, decode the rest: equals the oracle on all T."""
-    w = WORKLOADS[1]
+    w = WORKLOADS["ttt_mlp_fp32_d16"]
     T0, T = 64, 96
     inp = make_inputs(w, T=T)
     d = to_dev(inp)
@@ -451,13 +452,13 @@ def test_scan_then_decode_continues_the_sequence():
         assert rel_l2(a[0], b) <= TOL["f32"]
 
 
-@pytest.mark.parametrize("wid", [1, 3])
+@pytest.mark.parametrize("wid", ["ttt_mlp_fp32_d16", "ttt_mlp_bf16_d64_T8k"])
 def test_runs_are_bitwise_deterministic(wid):
     w = WORKLOADS[wid]
     T = min(w.T, 512)
     inp = to_dev(make_inputs(w, T=T))
     cfg = ops_config(w, T=T)
-    note(f"determinism cfg{wid}")
+    note(f"determinism {wid}")
     a = _run(cfg, inp, want_loss=True)
     b = _run(cfg, inp, want_loss=True)
     assert torch.equal(a["Z"], b["Z"]) and torch.equal(a["loss"], b["loss"])
@@ -467,7 +468,7 @@ def test_runs_are_bitwise_deterministic(wid):
 
 @pytest.mark.parametrize("force_generic", [True, False])
 def test_nonfinite_input_sets_status(force_generic):
-    w = WORKLOADS[3]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
     inp = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
     inp["K"][0, 1, 37, 5] = float("nan")
     cfg = ops_config(w, T=64, B=1, H=2, force_generic=force_generic)
@@ -488,7 +489,7 @@ def test_device_scope_handoff(kernel):
     path (atomics and fences, as when the workgroups of a head sit on different XCDs): same
     kernel, status clean, every head against the oracle, and the same result as the default
     same-XCD path up to bf16 noise."""
-    w = WORKLOADS[3] if kernel == "pair" else WORKLOADS[4]
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"] if kernel == "pair" else WORKLOADS["ttt_mlp_bf16_d128_T128k"]
     B, H, T = (2, 5, 96) if kernel == "pair" else (1, 3, 64)
     inp = make_inputs(w, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
     cfg = ops_config(w, B=B, H=H, T=T, device_scope=True)
