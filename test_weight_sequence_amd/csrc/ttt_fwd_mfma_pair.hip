@@ -88,6 +88,7 @@ union SmemP {
 // (a plain or sc0 load may return a line the L1 still holds from an earlier read).
 constexpr int kLoadL2 = 16;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned long long u64;
 typedef u64 u64x2 __attribute__((ext_vector_type(2)));
 
@@ -295,6 +296,11 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     for (int i = tid; i < static_cast<int>(sizeof(S.E2)) / 16; i += NT) e4[i] = uint4{0u, 0u, 0u, 0u};
   }
   if (tid < 8) S.zeros[tid] = (__bf16)0.f;
+  // Streamed rows read for the last time (V, eta here; K and Q in the consumer) and the Z
+  // stores are non-temporal, so that they leave the L2 first and the ring lines stay: with
+  // plain accesses about a quarter of the ring's stores were evicted to HBM (333 MB written
+  // per launch at B=8, H=12, T=8192 against 142 MB with these hints). K stays a plain load:
+  // the consumer reads the same rows a few chunks later and finds them in the L2.
   // staging by waves 4..7: thread -> (token, 4 consecutive d). Every wave issues exactly
   // three loads (K, V, eta) per chunk (waves 0..3 load the same addresses as waves 4..7 and
   // drop the data), so the count of memory operations after the slot stores is fixed.
@@ -308,8 +314,9 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     Ld r;
     const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
     r.k = *reinterpret_cast<const uint2*>(Kg + off);
-    r.x = *reinterpret_cast<const uint2*>(Xg + off);
-    r.e = etag[chunk * BC + (lt & 15)];
+    const u32x2 xv = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(Xg + off));
+    r.x = uint2{xv[0], xv[1]};
+    r.e = __builtin_nontemporal_load(etag + chunk * BC + (lt & 15));
     return r;
   };
   auto stage_write = [&](int chunk, const Ld& r) {
@@ -543,8 +550,8 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
   auto gload = [&](int chunk) {
     Ld r;
     const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
-    r.k = *reinterpret_cast<const unsigned*>(Kg + off);
-    r.x = *reinterpret_cast<const unsigned*>(Xg + off);
+    r.k = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(Kg + off));
+    r.x = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(Xg + off));
     return r;
   };
   auto stage_write = [&](int slot, const Ld& r) {
@@ -574,7 +581,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       const int d = 16 * i + c16;
       const float o = bf(So.X[t * RS + d]) + gam[i] * (z[i] - ls.mu) * ls.rs + bet[i];
       chk += o;
-      Zg[static_cast<size_t>(cc * BC + t) * D + d] = (__bf16)o;
+      __builtin_nontemporal_store((__bf16)o, &Zg[static_cast<size_t>(cc * BC + t) * D + d]);
     }
     chk = sum16(chk);
     if (c16 == 0) flag_nonfinite(p.status, chk);
