@@ -41,6 +41,9 @@ KERNEL_SOURCES = {
     "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
     "ttt_decode_stream_d64": ("ttt_decode_stream.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_fwd_mfma_split_d128": ("ttt_fwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
+                                "ttt_gelu.hpp"),
+    "ttt_bwd_mfma_d64": ("ttt_bwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
 }
 
 
@@ -185,7 +188,7 @@ def bench_scan_fwd(args, wid: str) -> dict:
     out["roofline"] = {
         "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
         "unit": "TFLOP/s", "frac": achieved / peak,
-        "traffic": _traffic(kernel, units) if headline else None,
+        "traffic": _traffic(kernel, units) if kernel in KERNEL_SOURCES else None,
         "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
         "algorithmic_bytes_per_launch": units * bytes_per_token_head(
             w.d, io_bytes, 2 * w.d * w.hidden, w.T)}
@@ -241,7 +244,8 @@ def bench_scan_bwd(args) -> dict:
     saved_bytes = w.B * w.H * (w.T // w.chunk) * 2 * w.d * w.hidden * 4
     out["roofline"] = {
         "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
-        "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+        "unit": "TFLOP/s", "frac": achieved / peak,
+        "traffic": _traffic(kernel, units) if kernel in KERNEL_SOURCES else None,
         "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
         # Q, K, V, dZ in and dQ, dK, dV out (bf16), eta in and deta out, the saved weights
         "algorithmic_bytes_per_launch": units * (7 * w.d * 2 + 8) + saved_bytes}
