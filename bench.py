@@ -321,8 +321,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps (default 5; 1 for the d=128 workload)")
     ap.add_argument("--workload", default="scan_fwd",
-                    choices=["scan_fwd", "scan_fwd_d128", "scan_bwd", "decode"],
+                    choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode"],
                     help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
+                         "scan_fwd_b16: the same head shape at B=16 (192 heads, 131,072 tokens "
+                         "per batch); "
                          "scan_fwd_d128: B=1 H=24 T=131072 d=128 forward; "
                          "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
@@ -368,6 +370,8 @@ def main():
 
     if args.workload == "scan_fwd":
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k")
+    elif args.workload == "scan_fwd_b16":
+        out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k_B16")
     elif args.workload == "scan_fwd_d128":
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
     elif args.workload == "scan_bwd":

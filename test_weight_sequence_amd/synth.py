@@ -43,7 +43,7 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five seeded workloads of the scan, keyed by name (shapes, dtypes and value
+# The seeded workloads of the scan, keyed by name (shapes, dtypes and value
 # distributions).
 WORKLOADS = {
     "ttt_mlp_fp32_d16": Workload("ttt_mlp_fp32_d16", "mlp", 1, 1, 256, 16, 64, 16, "f32", 0.1, "normal", seed=1001),
@@ -55,6 +55,10 @@ WORKLOADS = {
                 "normal", drift=0.999, seed=1004),
     "ttt_mlp_bf16_d64_fwd_bwd": Workload("ttt_mlp_bf16_d64_fwd_bwd", "mlp", 4, 16, 8192, 64, 256, 16, "bf16", 0.1,
                 "normal", seed=1005),
+    # the d=64 T=8192 head shape at 131,072 tokens per batch (B=16, 192 heads): the same
+    # seed as the B=8 workload, so its first eight sequences are that workload's inputs
+    "ttt_mlp_bf16_d64_T8k_B16": Workload("ttt_mlp_bf16_d64_T8k_B16", "mlp", 16, 12, 8192, 64, 256, 16, "bf16", 0.1,
+                "normal", seed=1003),
 }
 
 

@@ -75,6 +75,19 @@ def test_mlp_bf16_d64_T8k_sampled_heads(kernel):
     _check_heads(res, inp, [(0, 0), (3, 7), (7, 11)], w, TOL["bf16"])
 
 
+def test_mlp_bf16_d64_T8k_B16_sampled_heads():
+    """Full launch at B=16, H=12, T=8192 (192 heads: one workgroup per head, the launch that
+    the wider-batch measurement times); the oracle checks three heads at full T."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k_B16"]
+    cfg = ops_config(w)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_d64"
+    note("mlp bf16 d64 T8k B=16 full")
+    inp = make_inputs(w)
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    _check_heads(res, inp, [(0, 5), (9, 2), (15, 11)], w, TOL["bf16"])
+
+
 @pytest.mark.parametrize("kernel", ["generic", "pair", "one_wg"])
 def test_mlp_bf16_d64_all_heads_short(kernel):
     w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
