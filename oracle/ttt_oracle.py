@@ -218,6 +218,44 @@ def scan(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig):
     return torch.stack(Z, dim=1), W, torch.stack(losses, dim=1)
 
 
+def scan_momentum(Q, K, V, theta, mom, alpha, W0: tuple, S0: tuple | None, gamma, beta,
+                  cfg: OracleConfig):
+    """Mini-batch scan with momentum and a forget gate, primal and token by token.
+
+    "Test-Time Training(TTT)과 LLM 메모리", section "Titans와 Miras", Eq. 14 and Eq. 13:
+      S_t = eta_t S_{t-1} - theta_t grad l(M_{t-1}; x_t)     (momentum; eta here is `mom`)
+      M_t = (1 - alpha_t) M_{t-1} + S_t                      (forget gate)
+    with the mini-batch rule of the base scan (E2E paper review, section 2.3, Eq. 5): inside a
+    chunk every gradient is taken at the memory the chunk started from, so for b = 1 this is
+    the per-token rule as written. The output is z_t = f(Q_t; M_t), after token t's update.
+    theta (the step size, times cfg.eta_scale), mom and alpha are [N, T]; S0 is the momentum
+    carried in (zeros when None). M and S are both carried across chunks. With mom = 0 and
+    alpha = 0 this is the base scan with eta = theta.
+    Returns Z [N, T, d], the final memory M_T and momentum S_T (tuples) and the loss [N, T].
+    """
+    N, T, d = Q.shape
+    b = cfg.chunk
+    if T % b != 0:
+        raise ValueError("T must be a multiple of the chunk size")
+    if cfg.output != "query":
+        raise ValueError("the momentum scan has the query output only")
+    M = tuple(w for w in W0)
+    S = tuple(torch.zeros_like(w) for w in W0) if S0 is None else tuple(s for s in S0)
+    Z, losses = [], []
+    for i in range(T // b):
+        M_start = M
+        for t in range(i * b, (i + 1) * b):
+            loss, grads = token_loss_and_grad(K[:, t], V[:, t], M_start, gamma, beta, cfg)
+            th = (cfg.eta_scale * theta[:, t]).reshape(N, 1, 1)
+            mo = mom[:, t].reshape(N, 1, 1)
+            keep = (1.0 - alpha[:, t]).reshape(N, 1, 1)
+            S = tuple(mo * sv - th * gw for sv, gw in zip(S, grads))
+            M = tuple(keep * m + sv for m, sv in zip(M, S))
+            Z.append(f_apply(Q[:, t], M, gamma, beta, cfg))
+            losses.append(loss)
+    return torch.stack(Z, dim=1), M, S, torch.stack(losses, dim=1)
+
+
 def scan_outer_grads(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig,
                      dZ, dW_T: tuple | None = None):
     """Outer-loop backward by automatic differentiation through the scan.

@@ -14,7 +14,8 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle import OracleConfig, gelu, gelu_prime, scan, scan_outer_grads, token_loss_and_grad
+from oracle import (OracleConfig, gelu, gelu_prime, scan, scan_momentum, scan_outer_grads,
+                    token_loss_and_grad)
 from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -504,3 +505,127 @@ def test_flatten_heads_broadcasts_w0_over_batch():
     assert flat["Q"].shape == (6, 32, 64)
     assert torch.equal(flat["W0"][0][0], flat["W0"][0][3])
     assert torch.equal(flat["Q"][4], inp["Q"][1, 1].double())
+
+
+# ---------------------------------------------------------------------------
+# Momentum and forget gate ("Titans와 Miras", Eq. 13/14) on the mini-batch scan
+# ---------------------------------------------------------------------------
+
+def _gates(N, T, seed, mom_hi=0.9, alpha_hi=0.3):
+    g = torch.Generator().manual_seed(seed)
+    mom = mom_hi * torch.rand(N, T, generator=g, dtype=DT)
+    alpha = alpha_hi * torch.rand(N, T, generator=g, dtype=DT)
+    return mom, alpha
+
+
+def _autograd_grads(K, V, W, gamma, beta, kind, eps, ts):
+    """Per-token gradients of ||f(K_t; W) - V_t||^2 at one fixed W (autograd), one head."""
+    Wg = [w.clone().requires_grad_(True) for w in W]
+    out = []
+    for t in ts:
+        pred = lib_f(K[t], Wg, gamma, beta, kind, eps)
+        out.append([x.detach() for x in torch.autograd.grad(((pred - V[t]) ** 2).sum(), Wg)])
+    return out
+
+
+def lib_scan_momentum(Q, K, V, theta, mom, alpha, W0, S0, gamma, beta, kind, b, eps):
+    """Eq. 14 then Eq. 13 per token with autograd gradients at the chunk-start memory."""
+    N, T, d = Q.shape
+    Zs, Ms, Ss = [], [], []
+    for n in range(N):
+        M = [w[n].clone() for w in W0]
+        S = [s[n].clone() for s in S0]
+        zs = []
+        for c0 in range(0, T, b):
+            grads = _autograd_grads(K[n], V[n], M, gamma[n], beta[n], kind, eps, range(c0, c0 + b))
+            for j, t in enumerate(range(c0, c0 + b)):
+                S = [mom[n, t] * s - theta[n, t] * gw for s, gw in zip(S, grads[j])]
+                M = [(1 - alpha[n, t]) * m + s for m, s in zip(M, S)]
+                zs.append(lib_f(Q[n, t], M, gamma[n], beta[n], kind, eps))
+        Zs.append(torch.stack(zs))
+        Ms.append(M)
+        Ss.append(S)
+    stack = lambda L: tuple(torch.stack([x[k] for x in L]) for k in range(len(W0)))
+    return torch.stack(Zs), stack(Ms), stack(Ss)
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_momentum_without_gates_is_the_plain_scan(kind):
+    """mom = 0 and alpha = 0: S_t = -theta_t grad, M_t = M_{t-1} + S_t, i.e. the base scan."""
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, 12, 4, 16, kind, seed=31)
+    cfg = OracleConfig(kind=kind, chunk=4)
+    zero = torch.zeros_like(eta)
+    Z, MT, ST, L = scan_momentum(Q, K, V, eta, zero, zero, W0, None, gamma, beta, cfg)
+    Zr, WTr, Lr = scan(Q, K, V, eta, W0, gamma, beta, cfg)
+    assert rel(Z, Zr) <= 1e-13 and rel(L, Lr) <= 1e-13
+    for a, b_ in zip(MT, WTr):
+        assert rel(a, b_) <= 1e-13
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+@pytest.mark.parametrize("b", [1, 4])
+def test_momentum_matches_autograd_loop(kind, b):
+    """Random momentum and forget gates, a nonzero carried-in momentum: the oracle's scan
+    against the per-token Eq. 14 / Eq. 13 loop with autograd gradients (b = 1: the rule as
+    written, gradient at M_{t-1})."""
+    N, T, d, h = 2, 12, 4, 16
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(N, T, d, h, kind, seed=32)
+    mom, alpha = _gates(N, T, seed=33)
+    g = torch.Generator().manual_seed(34)
+    S0 = tuple(0.05 * torch.randn(w.shape, generator=g, dtype=DT) for w in W0)
+    cfg = OracleConfig(kind=kind, chunk=b)
+    Z, MT, ST, _ = scan_momentum(Q, K, V, eta, mom, alpha, W0, S0, gamma, beta, cfg)
+    Zr, MTr, STr = lib_scan_momentum(Q, K, V, eta, mom, alpha, W0, S0, gamma, beta, kind, b, cfg.ln_eps)
+    assert rel(Z, Zr) <= 1e-12
+    for a, b_ in zip(MT + ST, MTr + STr):
+        assert rel(a, b_) <= 1e-12
+
+
+def test_momentum_full_forget_closed_form():
+    """alpha = 1, mom = 0, one chunk: M_t = S_t = -theta_t grad l_t(W0), so
+    z_t = f(Q_t; -theta_t grad l_t(W0))."""
+    N, T, d, h = 2, 8, 4, 16
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(N, T, d, h, "mlp", seed=35)
+    cfg = OracleConfig(kind="mlp", chunk=T)
+    Z = scan_momentum(Q, K, V, eta, torch.zeros_like(eta), torch.ones_like(eta), W0, None,
+                      gamma, beta, cfg)[0]
+    for n in range(N):
+        grads = _autograd_grads(K[n], V[n], [w[n] for w in W0], gamma[n], beta[n], "mlp",
+                                cfg.ln_eps, range(T))
+        for t in range(T):
+            zr = lib_f(Q[n, t], [-eta[n, t] * gw for gw in grads[t]], gamma[n], beta[n], "mlp", cfg.ln_eps)
+            assert rel(Z[n, t], zr) <= 1e-12
+
+
+def test_momentum_heavy_ball_closed_form():
+    """mom = 1, alpha = 0, zero momentum in, one chunk: S_u = -sum_{s<=u} theta_s g_s and
+    M_t = W0 + sum_{u<=t} S_u = W0 - sum_{s<=t} (t - s + 1) theta_s g_s."""
+    N, T, d, h = 2, 8, 4, 16
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(N, T, d, h, "linear", seed=36)
+    cfg = OracleConfig(kind="linear", chunk=T)
+    Z, MT, ST, _ = scan_momentum(Q, K, V, eta, torch.ones_like(eta), torch.zeros_like(eta), W0, None,
+                                 gamma, beta, cfg)
+    for n in range(N):
+        grads = _autograd_grads(K[n], V[n], [w[n] for w in W0], gamma[n], beta[n], "linear",
+                                cfg.ln_eps, range(T))
+        for t in range(T):
+            Mt = W0[0][n] - sum((t - s + 1) * eta[n, s] * grads[s][0] for s in range(t + 1))
+            assert rel(Z[n, t], lib_f(Q[n, t], [Mt], gamma[n], beta[n], "linear", cfg.ln_eps)) <= 1e-12
+        assert rel(ST[0][n], -sum(eta[n, s] * grads[s][0] for s in range(T))) <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["mlp", "linear"])
+def test_momentum_state_carries_across_a_split(kind):
+    """A scan of 2T tokens equals a scan of T then a scan of T started from (M_T, S_T)."""
+    Q, K, V, eta, W0, gamma, beta = _rand_inputs(2, 16, 4, 16, kind, seed=37)
+    mom, alpha = _gates(2, 16, seed=38)
+    cfg = OracleConfig(kind=kind, chunk=4)
+    Z, MT, ST, _ = scan_momentum(Q, K, V, eta, mom, alpha, W0, None, gamma, beta, cfg)
+    h = slice(0, 8), slice(8, 16)
+    Za, Ma, Sa, _ = scan_momentum(Q[:, h[0]], K[:, h[0]], V[:, h[0]], eta[:, h[0]], mom[:, h[0]],
+                                  alpha[:, h[0]], W0, None, gamma, beta, cfg)
+    Zb, Mb, Sb, _ = scan_momentum(Q[:, h[1]], K[:, h[1]], V[:, h[1]], eta[:, h[1]], mom[:, h[1]],
+                                  alpha[:, h[1]], Ma, Sa, gamma, beta, cfg)
+    assert torch.equal(torch.cat([Za, Zb], dim=1), Z)
+    for a, b_ in zip(Mb + Sb, MT + ST):
+        assert torch.equal(a, b_)
