@@ -200,6 +200,42 @@ def bench_scan_fwd(args, wid: str) -> dict:
     return out
 
 
+def bench_scan_fwd_momentum(args) -> dict:
+    """One step = one ttt_scan_fwd_momentum over the whole batch (the portable fp32 kernel),
+    d=64 T=8192 head shape at B=8, H=12, gates mom = 0.9 sigmoid(u), alpha = 0.01 sigmoid(u')."""
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS, momentum_gates
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk, io=w.io)
+    dev = torch.device("cuda:0")
+    d = _device_inputs(w, dev)
+    gates = {k: v.to(dev) for k, v in momentum_gates(w).items()}
+    ws = ops.new_workspace(cfg, ops.TTT_OP_FWD_MOMENTUM, dev)
+
+    def call(i):
+        ops.scan_fwd_momentum(cfg, d["Q"], d["K"], d["V"], d["eta"], gates["mom"], gates["alpha"],
+                              d["W0"], d["gamma"], d["beta"], workspace=ws)
+        return 0
+
+    ms_step, kms = _time_calls(call, args.steps, args.warmup)
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    k_avg = statistics.fmean(kms)
+    units = w.B * w.H * w.T
+    # the plain scan's products, plus Q S1 and A^Q S2 and the momentum's own update
+    flop = units * (flops_per_token_head(w.d, w.hidden, w.chunk) + 8 * w.d * w.hidden)
+    achieved = flop / (k_avg * 1e-3) / 1e12
+    out = _base_record(args, f"TTT-MLP momentum/forget-gate scan token*heads/s at d={w.d}, T={w.T}",
+                       units / (ms_step * 1e-3), ms_step, w, "ttt_fwd_generic (momentum)", "f32")
+    out["roofline"] = {
+        "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+        "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None, "kernel_ms": k_avg,
+        "kernel_ms_min": min(kms), "flop_per_launch": flop,
+        "algorithmic_bytes_per_launch": units * (bytes_per_token_head(w.d, 2, 2 * w.d * w.hidden, w.T) + 8)}
+    return out
+
+
 def bwd_flops_per_token_head(d: int, h: int, b: int) -> int:
     # The chunk's forward recomputed from its saved start weights (the five forward products:
     # K W1, A^K W2, E2 W2^T, Q W1, A^Q W2, and the four dual terms), then two adjoint
@@ -321,11 +357,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps (default 5; 1 for the d=128 workload)")
     ap.add_argument("--workload", default="scan_fwd",
-                    choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode"],
+                    choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode",
+                             "scan_fwd_momentum"],
                     help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
                          "scan_fwd_b16: the same head shape at B=16 (192 heads, 131,072 tokens "
                          "per batch); "
                          "scan_fwd_d128: B=1 H=24 T=131072 d=128 forward; "
+                         "scan_fwd_momentum: the B=8 forward with momentum and forget gate; "
                          "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -338,7 +376,7 @@ def main():
                     help="instead of the scan, time a plain device-to-device copy of MIB MiB "
                          "(the known-size reference for scaling the HBM byte counters)")
     args = ap.parse_args()
-    long_run = args.workload == "scan_fwd_d128"
+    long_run = args.workload in ("scan_fwd_d128", "scan_fwd_momentum")
     if args.steps is None:
         args.steps = 2 if long_run else 20
     if args.warmup is None:
@@ -376,6 +414,8 @@ def main():
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
     elif args.workload == "scan_bwd":
         out = bench_scan_bwd(args)
+    elif args.workload == "scan_fwd_momentum":
+        out = bench_scan_fwd_momentum(args)
     else:
         out = bench_decode(args)
     print(json.dumps(out), flush=True)

@@ -90,7 +90,7 @@ enum {
                                      they do not; the flag lets a test run it. */
 };
 /* op codes for ttt_workspace_size */
-enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2 };
+enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2, TTT_OP_FWD_MOMENTUM = 3 };
 
 typedef struct {
   int32_t kind;      /* TTT_LINEAR or TTT_MLP                                         */
@@ -116,7 +116,8 @@ typedef struct {
 /* Host-only check of a configuration (no HIP call). */
 ttt_status ttt_validate(const ttt_config* cfg);
 
-/* Bytes of workspace the op needs (TTT_OP_FWD / TTT_OP_BWD / TTT_OP_DECODE).
+/* Bytes of workspace the op needs (TTT_OP_FWD / TTT_OP_BWD / TTT_OP_DECODE /
+ * TTT_OP_FWD_MOMENTUM).
  * Host only. The first 256 bytes of every workspace hold the status word; the
  * caller zero-fills a new workspace once (or calls ttt_reset_status). */
 ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes);
@@ -137,6 +138,28 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
                         const float* eta, const float* ln_gamma, const float* ln_beta,
                         const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
                         void* saved, void* workspace, size_t ws_bytes, void* stream);
+
+/* Forward scan with momentum and a forget gate: the page "Test-Time Training(TTT)과 LLM
+ * 메모리", section "Titans와 Miras", Eq. 14 (S_t = mom_t S_{t-1} - theta_t grad l(M_{t-1}; x_t))
+ * and Eq. 13 (M_t = (1 - alpha_t) M_{t-1} + S_t), with the loss, f and output of
+ * ttt_scan_fwd and its mini-batch rule (inside a chunk every gradient is taken at the
+ * memory the chunk started from; chunk = 1 is the per-token rule as written).
+ *  theta [B,H,T] fp32: step size per token (times cfg->eta_scale); mom [B,H,T] fp32:
+ *  momentum decay; alpha [B,H,T] fp32: forget gate (0 keeps, 1 resets). Any real values
+ *  are accepted; the pages give (0, 1) for alpha.
+ *  W0: initial memory, shaped as for ttt_scan_fwd. S0 (nullable = zero): momentum carried
+ *  in, always per sequence [B,H,...]. W_T, S_T (nullable): final memory and momentum,
+ *  [B,H,...] (written). Z, loss: as for ttt_scan_fwd.
+ *  Runs the portable fp32 kernel for every supported shape and io dtype. TTT_OUTPUT_KEY is
+ *  rejected (TTT_ERR_UNSUPPORTED); there is no saved state and no backward for this
+ *  variant. Workspace: ttt_workspace_size(.., TTT_OP_FWD_MOMENTUM, ..) bytes (the fp32
+ *  memory and momentum of every head). Errors as for ttt_scan_fwd. */
+ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                                 const float* theta, const float* mom, const float* alpha,
+                                 const float* ln_gamma, const float* ln_beta, const ttt_weights* W0,
+                                 const ttt_weights* S0, void* Z, const ttt_weights* W_T,
+                                 const ttt_weights* S_T, float* loss, void* workspace,
+                                 size_t ws_bytes, void* stream);
 
 /* Outer-loop backward through the scan (gradients of gradients, the outer loop of
  * the E2E paper review, section 2.2): given dZ [B,H,T,d] (io dtype) and optionally

@@ -147,6 +147,10 @@ const char* ttt_status_str(ttt_status s) {
 
 ttt_status ttt_validate(const ttt_config* cfg) { return check_common(cfg, true); }
 
+size_t fwd_momentum_ws_bytes(const ttt_config* c) {
+  return kStatusBytes + static_cast<size_t>(c->B) * c->H * 2 * weights_per_head(c) * sizeof(float);
+}
+
 ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) {
   if (!bytes) return TTT_ERR_NULL;
   const bool need_T = op != TTT_OP_DECODE;
@@ -156,6 +160,11 @@ ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) 
     case TTT_OP_FWD: *bytes = fwd_ws_bytes(cfg); return TTT_OK;
     case TTT_OP_BWD: *bytes = bwd_ws_bytes(cfg); return TTT_OK;
     case TTT_OP_DECODE: *bytes = kStatusBytes; return TTT_OK;
+    case TTT_OP_FWD_MOMENTUM:
+      if (fwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk, true) > kMaxLds)
+        return TTT_ERR_UNSUPPORTED;
+      *bytes = fwd_momentum_ws_bytes(cfg);
+      return TTT_OK;
     default: return TTT_ERR_ARG;
   }
 }
@@ -226,6 +235,59 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
   if (use_split(cfg) && fwd_split_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_split(p, s));
   return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
+}
+
+ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                                 const float* theta, const float* mom, const float* alpha,
+                                 const float* ln_gamma, const float* ln_beta, const ttt_weights* W0,
+                                 const ttt_weights* S0, void* Z, const ttt_weights* W_T,
+                                 const ttt_weights* S_T, float* loss, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  ttt_status st = check_common(cfg, true);
+  if (st != TTT_OK) return st;
+  if (cfg->flags & TTT_OUTPUT_KEY) return TTT_ERR_UNSUPPORTED;
+  if (fwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk, true) > kMaxLds)
+    return TTT_ERR_UNSUPPORTED;
+  const bool mlp = cfg->kind == TTT_MLP;
+  if (!Q || !K || !V || !theta || !mom || !alpha || !ln_gamma || !ln_beta || !W0 || !W0->w1 || !Z)
+    return TTT_ERR_NULL;
+  if (mlp && !W0->w2) return TTT_ERR_NULL;
+  for (const ttt_weights* w : {S0, W_T, S_T})
+    if (w && (!w->w1 || (mlp && !w->w2))) return TTT_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, theta, mom, alpha, ln_gamma, ln_beta, W0->w1, Z};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+  if (mlp && !aligned16(W0->w2)) return TTT_ERR_ALIGN;
+  for (const ttt_weights* w : {S0, W_T, S_T})
+    if (w && (!aligned16(w->w1) || (mlp && !aligned16(w->w2)))) return TTT_ERR_ALIGN;
+  if (loss && !aligned16(loss)) return TTT_ERR_ALIGN;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < fwd_momentum_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
+
+  ScanParams p = scan_params(cfg);
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.eta = theta;
+  p.gamma = ln_gamma;
+  p.beta = ln_beta;
+  p.w0_1 = W0->w1;
+  p.w0_2 = mlp ? W0->w2 : nullptr;
+  p.Z = Z;
+  p.wt_1 = W_T ? W_T->w1 : nullptr;
+  p.wt_2 = (W_T && mlp) ? W_T->w2 : nullptr;
+  p.loss = loss;
+  p.saved = nullptr;
+  p.status = static_cast<unsigned*>(workspace);
+  p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
+  p.mom = mom;
+  p.alpha = alpha;
+  p.s0_1 = S0 ? S0->w1 : nullptr;
+  p.s0_2 = (S0 && mlp) ? S0->w2 : nullptr;
+  p.st_1 = S_T ? S_T->w1 : nullptr;
+  p.st_2 = (S_T && mlp) ? S_T->w2 : nullptr;
+  return map_hip(launch_fwd_generic(p, static_cast<hipStream_t>(stream)));
 }
 
 ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,

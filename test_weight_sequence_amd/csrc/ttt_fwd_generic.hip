@@ -19,6 +19,16 @@
 // With TTT_OUTPUT_KEY (the simplified output rule, E2E paper review section 2.4.2, Eq. 9)
 // the output is the key-side prediction at the chunk-start weights, z = K + LN(Z^K), and
 // the query side (H^Q, Z^Q) is skipped.
+//
+// With momentum and a forget gate (page "Test-Time Training(TTT)과 LLM 메모리", section
+// "Titans와 Miras", Eq. 14: S_t = m_t S_{t-1} - theta_t grad_t, Eq. 13: M_t = (1 - a_t) M_{t-1}
+// + S_t, gradients at the chunk-start memory) the two linear recurrences unroll, inside a
+// chunk, into M_t = A_t M + B_t S - sum_{s<=t} C_ts theta_s grad_s and S_t = P_t S -
+// sum_{s<=t} D_ts theta_s grad_s, with scalar coefficients of the chunk's gates:
+//   P_t = m_t P_{t-1}, D_ts = m_t D_{t-1,s} (D_tt = 1), A_t = (1 - a_t) A_{t-1},
+//   B_t = (1 - a_t) B_{t-1} + P_t, C_ts = (1 - a_t) C_{t-1,s} + D_ts  (A_0 = P_0 = 1, B_0 = 0).
+// The dual form then scales the chunk-start products per token (A_t Q W1 + B_t Q S1) and
+// weights the causal masks by C; the memory and the momentum are both carried.
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -29,9 +39,10 @@ constexpr int MAXB = kMaxChunk;
 
 struct Lds {
   float *K, *V, *Q, *E, *A, *G, *AQ, *Z, *ZQ, *S;
+  float *C, *Dl, *Av, *Bv;  // momentum coefficients: C [b x b], last row of D, A_t, B_t, P_b
 };
 
-__device__ __forceinline__ Lds carve(float* base, int kind, int b, int d, int h) {
+__device__ __forceinline__ Lds carve(float* base, int kind, int b, int d, int h, bool mom) {
   Lds s;
   float* p = base;
   s.K = p; p += b * d;
@@ -47,6 +58,14 @@ __device__ __forceinline__ Lds carve(float* base, int kind, int b, int d, int h)
     s.AQ = p; p += b * h;
   } else {
     s.A = s.G = s.AQ = nullptr;
+  }
+  if (mom) {
+    s.C = p; p += b * b;
+    s.Dl = p; p += b;
+    s.Av = p; p += b;
+    s.Bv = p; p += b + 1;
+  } else {
+    s.C = s.Dl = s.Av = s.Bv = nullptr;
   }
   return s;
 }
@@ -69,7 +88,7 @@ __device__ __forceinline__ RowLN ln_row(float z0, float z1, int lane, int d, flo
   return r;
 }
 
-template <typename IO, int KIND>
+template <typename IO, int KIND, bool MOM>
 __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
   extern __shared__ float lds_raw[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,15 +98,21 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
   const size_t nW1 = KIND == TTT_MLP ? static_cast<size_t>(d) * h : static_cast<size_t>(d) * d;
   const size_t nW2 = KIND == TTT_MLP ? static_cast<size_t>(h) * d : 0;
   const size_t nW = nW1 + nW2;
-  Lds s = carve(lds_raw, KIND, b, d, h);
+  Lds s = carve(lds_raw, KIND, b, d, h, MOM);
 
-  float* W1 = p.wbuf + static_cast<size_t>(bh) * nW;
+  float* W1 = p.wbuf + static_cast<size_t>(bh) * (MOM ? 2 * nW : nW);
   float* W2 = W1 + nW1;
+  float* S1 = W1 + nW;  // momentum (MOM only)
+  float* S2 = S1 + nW1;
   const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
   const bool key_out = (p.flags & TTT_OUTPUT_KEY) != 0;
   const size_t w0_head = per_seq ? static_cast<size_t>(bh) : static_cast<size_t>(hidx);
   for (size_t i = tid; i < nW1; i += NT) W1[i] = p.w0_1[w0_head * nW1 + i];
   for (size_t i = tid; i < nW2; i += NT) W2[i] = p.w0_2[w0_head * nW2 + i];
+  if (MOM) {
+    for (size_t i = tid; i < nW1; i += NT) S1[i] = p.s0_1 ? p.s0_1[static_cast<size_t>(bh) * nW1 + i] : 0.f;
+    for (size_t i = tid; i < nW2; i += NT) S2[i] = p.s0_2 ? p.s0_2[static_cast<size_t>(bh) * nW2 + i] : 0.f;
+  }
   const float* gam = p.gamma + static_cast<size_t>(hidx) * d;
   const float* bet = p.beta + static_cast<size_t>(hidx) * d;
   const float g0 = lane < d ? gam[lane] : 0.f, g1 = lane + 64 < d ? gam[lane + 64] : 0.f;
@@ -115,6 +140,32 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
       s.Q[i] = to_f32(Qg[static_cast<size_t>(t0) * d + i]);
     }
     if (tid < b) s.E[tid] = etag[t0 + tid] * p.eta_scale;
+    if (MOM && tid == 0) {
+      // the chunk's coefficients (header comment), token by token
+      const float* mg = p.mom + static_cast<size_t>(bh) * p.T + t0;
+      const float* ag = p.alpha + static_cast<size_t>(bh) * p.T + t0;
+      float D[MAXB], Cr[MAXB];
+#pragma unroll
+      for (int u = 0; u < MAXB; ++u) D[u] = Cr[u] = 0.f;
+      float A = 1.f, Bc = 0.f, P = 1.f;
+      for (int t = 0; t < b; ++t) {
+        const float m = mg[t], keep = 1.f - ag[t];
+        P *= m;
+        A *= keep;
+        Bc = keep * Bc + P;
+#pragma unroll
+        for (int u = 0; u < MAXB; ++u) {
+          if (u < t) D[u] *= m;
+          if (u == t) D[u] = 1.f;
+          if (u <= t) Cr[u] = keep * Cr[u] + D[u];
+        }
+        for (int u = 0; u < b; ++u) s.C[t * b + u] = u <= t ? Cr[u] : 0.f;
+        s.Av[t] = A;
+        s.Bv[t] = Bc;
+      }
+      for (int u = 0; u < b; ++u) s.Dl[u] = D[u];
+      s.Bv[b] = P;
+    }
     __syncthreads();
 
     // ---- K side forward: Z^K ----
@@ -211,7 +262,7 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
       float acc = 0.f;
       if (u <= t)
         for (int k = 0; k < d; ++k) acc = fmaf(s.Q[t * d + k], s.K[u * d + k], acc);
-      s.S[i] = acc;
+      s.S[i] = MOM ? acc * s.C[i] : acc;
     }
     __syncthreads();
 
@@ -248,6 +299,20 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
           for (int t = 0; t < MAXB; ++t)
             if (t < b) acc[t] = fmaf(s.Q[t * d + k], w, acc[t]);
         }
+        if (MOM) {
+          float am[MAXB];
+#pragma unroll
+          for (int t = 0; t < MAXB; ++t) am[t] = 0.f;
+          for (int k = 0; k < d; ++k) {
+            const float w = S1[static_cast<size_t>(k) * h + j];
+#pragma unroll
+            for (int t = 0; t < MAXB; ++t)
+              if (t < b) am[t] = fmaf(s.Q[t * d + k], w, am[t]);
+          }
+#pragma unroll
+          for (int t = 0; t < MAXB; ++t)
+            if (t < b) acc[t] = s.Av[t] * acc[t] + s.Bv[t] * am[t];
+        }
 #pragma unroll
         for (int u = 0; u < MAXB; ++u) {
           if (u < b) {
@@ -268,7 +333,7 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
         float acc = 0.f;
         if (u <= t)
           for (int j = 0; j < h; ++j) acc = fmaf(s.AQ[t * h + j], s.A[u * h + j], acc);
-        s.S[i] = acc;
+        s.S[i] = MOM ? acc * s.C[i] : acc;
       }
       __syncthreads();
       // ---- Z^Q = A^Q W2 - S2 E2 ----
@@ -282,6 +347,24 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
           for (int m = 0; m < MAXB; ++m) {
             const int t = grp + m * ngrp;
             if (t < b) acc[m] = fmaf(s.AQ[t * h + j], w, acc[m]);
+          }
+        }
+        if (MOM) {
+          float am[MAXB];
+#pragma unroll
+          for (int m = 0; m < MAXB; ++m) am[m] = 0.f;
+          for (int j = 0; j < h; ++j) {
+            const float w = S2[static_cast<size_t>(j) * d + col];
+#pragma unroll
+            for (int m = 0; m < MAXB; ++m) {
+              const int t = grp + m * ngrp;
+              if (t < b) am[m] = fmaf(s.AQ[t * h + j], w, am[m]);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MAXB; ++m) {
+            const int t = grp + m * ngrp;
+            if (t < b) acc[m] = s.Av[t] * acc[m] + s.Bv[t] * am[m];
           }
         }
 #pragma unroll
@@ -307,6 +390,24 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
           for (int m = 0; m < MAXB; ++m) {
             const int t = grp + m * ngrp;
             if (t < b) acc[m] = fmaf(s.Q[t * d + k], w, acc[m]);
+          }
+        }
+        if (MOM) {
+          float am[MAXB];
+#pragma unroll
+          for (int m = 0; m < MAXB; ++m) am[m] = 0.f;
+          for (int k = 0; k < d; ++k) {
+            const float w = S1[static_cast<size_t>(k) * d + col];
+#pragma unroll
+            for (int m = 0; m < MAXB; ++m) {
+              const int t = grp + m * ngrp;
+              if (t < b) am[m] = fmaf(s.Q[t * d + k], w, am[m]);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MAXB; ++m) {
+            const int t = grp + m * ngrp;
+            if (t < b) acc[m] = s.Av[t] * acc[m] + s.Bv[t] * am[m];
           }
         }
 #pragma unroll
@@ -340,7 +441,40 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
       if (lane == 0) flag_nonfinite(p.status, chk);
     }
     // ---- weight update (chunk end) ----
-    if (KIND == TTT_MLP) {
+    if (MOM) {
+      // M = A_b M + B_b S - K^T (C_b . E1) ..., S = P_b S - K^T (D_b . E1) ... (old S in both)
+      const float Ab = s.Av[b - 1], Bb = s.Bv[b - 1], Pb = s.Bv[b];
+      const float* Cb = s.C + (b - 1) * b;
+      const size_t n1 = KIND == TTT_MLP ? static_cast<size_t>(d) * h : static_cast<size_t>(d) * d;
+      const int w1c = KIND == TTT_MLP ? h : d;
+      const float* E1 = KIND == TTT_MLP ? s.G : s.Z;
+      for (size_t i = tid; i < n1; i += NT) {
+        const int k = static_cast<int>(i / w1c), j = static_cast<int>(i % w1c);
+        const float sv = S1[i];
+        float am = Ab * W1[i] + Bb * sv, as = Pb * sv;
+        for (int t = 0; t < b; ++t) {
+          const float ke = s.K[t * d + k] * E1[t * w1c + j];
+          am = fmaf(-Cb[t], ke, am);
+          as = fmaf(-s.Dl[t], ke, as);
+        }
+        W1[i] = am;
+        S1[i] = as;
+      }
+      if (KIND == TTT_MLP) {
+        for (int i = tid; i < h * d; i += NT) {
+          const int j = i / d, cc = i % d;
+          const float sv = S2[i];
+          float am = Ab * W2[i] + Bb * sv, as = Pb * sv;
+          for (int t = 0; t < b; ++t) {
+            const float ae = s.A[t * h + j] * s.Z[t * d + cc];
+            am = fmaf(-Cb[t], ae, am);
+            as = fmaf(-s.Dl[t], ae, as);
+          }
+          W2[i] = am;
+          S2[i] = as;
+        }
+      }
+    } else if (KIND == TTT_MLP) {
       for (int i = tid; i < d * h; i += NT) {
         const int k = i / h, j = i % h;
         float acc = W1[i];
@@ -372,6 +506,10 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
     float* o2 = p.wt_2 + static_cast<size_t>(bh) * nW2;
     for (size_t i = tid; i < nW2; i += NT) o2[i] = W2[i];
   }
+  if (MOM && p.st_1) {
+    for (size_t i = tid; i < nW1; i += NT) p.st_1[static_cast<size_t>(bh) * nW1 + i] = S1[i];
+    for (size_t i = tid; i < nW2; i += NT) p.st_2[static_cast<size_t>(bh) * nW2 + i] = S2[i];
+  }
 }
 
 __global__ void reset_status_kernel(unsigned* status) {
@@ -380,19 +518,21 @@ __global__ void reset_status_kernel(unsigned* status) {
 
 }  // namespace
 
-size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk) {
+size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk, bool momentum) {
   size_t f = 5 * static_cast<size_t>(chunk) * d + 16 + static_cast<size_t>(chunk) * chunk;
   if (kind == TTT_MLP) f += 3 * static_cast<size_t>(chunk) * hid;
+  if (momentum) f += static_cast<size_t>(chunk) * chunk + 3 * static_cast<size_t>(chunk) + 1;
   return f * sizeof(float);
 }
 
 hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t stream) {
-  const size_t lds = fwd_generic_lds_bytes(p.kind, p.d, p.hid, p.chunk);
+  const bool mom = p.mom != nullptr;
+  const size_t lds = fwd_generic_lds_bytes(p.kind, p.d, p.hid, p.chunk, mom);
   const dim3 grid(p.B * p.H), block(NT);
   hipError_t e;
 #define TTT_LAUNCH(IO, KIND)                                                              \
   do {                                                                                    \
-    auto fn = fwd_generic_kernel<IO, KIND>;                                               \
+    auto fn = mom ? fwd_generic_kernel<IO, KIND, true> : fwd_generic_kernel<IO, KIND, false>; \
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                            \
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
     if (e != hipSuccess) return e;                                                        \

@@ -33,8 +33,15 @@ struct ScanParams {
   float* wt_2;
   float* loss;
   float* saved;    // [B*H, T/chunk, nW] chunk-start weights, or null
-  float* wbuf;     // [B*H, nW] fp32 working weights (portable kernel)
+  float* wbuf;     // [B*H, nW] fp32 working weights (portable kernel); [B*H, 2 nW] with momentum
   unsigned* status;
+  // momentum / forget-gate variant (portable kernel only; null mom = the plain scan)
+  const float* mom;    // [B*H, T] momentum decay per token
+  const float* alpha;  // [B*H, T] forget gate per token
+  const float* s0_1;   // [B*H, ..] momentum carried in, or null (zero)
+  const float* s0_2;
+  float* st_1;         // [B*H, ..] momentum out, or null
+  float* st_2;
 };
 
 struct BwdParams {
@@ -86,7 +93,7 @@ __host__ __device__ inline size_t n_weights(int kind, int d, int hid) {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t s);
-size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
+size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk, bool momentum = false);
 bool fwd_mfma_supported(const ScanParams& p);
 hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t s);
 // Two-workgroup (producer/consumer) variant of the tuned forward: its workspace region

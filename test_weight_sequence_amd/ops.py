@@ -4,7 +4,7 @@ Every step of the scan runs in the HIP library; torch is used here only to alloc
 device memory and to obtain the current HIP stream. If libttt.so is missing or
 cannot be loaded, every entry point raises: there is no fallback path.
 
-Names mirror include/ttt.h: scan_fwd, scan_bwd, decode_step, validate,
+Names mirror include/ttt.h: scan_fwd, scan_fwd_momentum, scan_bwd, decode_step, validate,
 workspace_size, saved_size, read_status, reset_status, fwd_kernel_name, bwd_kernel_name,
 decode_kernel_name.
 """
@@ -23,14 +23,14 @@ TTT_F32, TTT_BF16 = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
 TTT_W0_PER_SEQ, TTT_FORCE_GENERIC, TTT_ONE_WG_PER_HEAD, TTT_OUTPUT_KEY = 1, 2, 4, 8
 TTT_FORCE_DEVICE_SCOPE = 16
-TTT_OP_FWD, TTT_OP_BWD, TTT_OP_DECODE = 0, 1, 2
+TTT_OP_FWD, TTT_OP_BWD, TTT_OP_DECODE, TTT_OP_FWD_MOMENTUM = 0, 1, 2, 3
 
 STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE",
           4: "TTT_ERR_UNSUPPORTED", 5: "TTT_ERR_ALIGN", 6: "TTT_ERR_WORKSPACE",
           7: "TTT_ERR_HIP", 8: "TTT_ERR_NONFINITE", 9: "TTT_ERR_ARG",
           10: "TTT_ERR_TIMEOUT"}
 
-EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
+EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd", "ttt_scan_fwd_momentum",
            "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
            "ttt_fwd_kernel_name", "ttt_bwd_kernel_name", "ttt_decode_kernel_name", "ttt_status_str",
            "ttt_abi_version")
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_workspace_size.argtypes = [cfgp, I32, ctypes.POINTER(S)]
         L.ttt_saved_size.argtypes = [cfgp, ctypes.POINTER(S)]
         L.ttt_scan_fwd.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, S, P]
+        L.ttt_scan_fwd_momentum.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, wp, P, wp, wp, P, P, S, P]
         L.ttt_scan_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, P, P, P, P, wp, P, P, P, S, P]
         L.ttt_decode_step.argtypes = [cfgp, P, P, P, P, P, P, wp, wp, I32, P, P, S, P]
         L.ttt_read_status.argtypes = [P, P]
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_status_str.argtypes = [I32]
         L.ttt_status_str.restype = ctypes.c_char_p
         for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
+                     "ttt_scan_fwd_momentum",
                      "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
                      "ttt_abi_version"):
             getattr(L, name).restype = I32
@@ -217,6 +219,26 @@ def scan_fwd(cfg: Config, Q, K, V, eta, W0, gamma, beta, *, want_wt=True, want_l
     _check(code, "ttt_scan_fwd")
     return {"Z": Z, "W_T": tuple(WT) if WT else None, "loss": loss, "saved": saved,
             "workspace": ws}
+
+
+def scan_fwd_momentum(cfg: Config, Q, K, V, theta, mom, alpha, W0, gamma, beta, S0=None, *,
+                      want_loss=False, workspace=None, stream=None) -> dict:
+    """Forward scan with momentum and a forget gate (ttt_scan_fwd_momentum). theta, mom,
+    alpha [B,H,T] fp32; S0 (optional) tuple of fp32 [B,H,...]. Returns Z, W_T, S_T (and
+    loss when asked)."""
+    dev = Q.device
+    lead = (cfg.B, cfg.H)
+    Z = torch.empty(*lead, cfg.T, cfg.d, dtype=cfg.io_dtype, device=dev)
+    WT = [torch.empty(s, dtype=torch.float32, device=dev) for s in cfg.weight_shapes(lead)]
+    ST = [torch.empty(s, dtype=torch.float32, device=dev) for s in cfg.weight_shapes(lead)]
+    loss = torch.empty(*lead, cfg.T, dtype=torch.float32, device=dev) if want_loss else None
+    ws = workspace if workspace is not None else new_workspace(cfg, TTT_OP_FWD_MOMENTUM, dev)
+    code = lib().ttt_scan_fwd_momentum(
+        ctypes.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta), _ptr(mom), _ptr(alpha),
+        _ptr(gamma), _ptr(beta), _weights(W0), _weights(S0), _ptr(Z), _weights(WT), _weights(ST),
+        _ptr(loss), _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "ttt_scan_fwd_momentum")
+    return {"Z": Z, "W_T": tuple(WT), "S_T": tuple(ST), "loss": loss, "workspace": ws}
 
 
 def scan_bwd(cfg: Config, Q, K, V, eta, gamma, beta, saved, dZ, dW_T=None, *,

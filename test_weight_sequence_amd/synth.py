@@ -16,7 +16,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-_TENSOR_CODE = {"Q": 0, "K": 1, "V": 2, "u": 3, "W0": 4, "dZ": 5}
+_TENSOR_CODE = {"Q": 0, "K": 1, "V": 2, "u": 3, "W0": 4, "dZ": 5, "u_mom": 6, "u_alpha": 7}
 
 
 @dataclass(frozen=True)
@@ -154,4 +154,25 @@ def flatten_heads(inp: dict) -> dict:
     for name in ("gamma", "beta"):
         g = inp[name].to(torch.float64)
         out[name] = g.unsqueeze(0).expand(nb, *g.shape).reshape(nb * nh, -1).clone()
+    return out
+
+
+def momentum_gates(w: Workload, batch_idx=None, head_idx=None, T: int | None = None,
+                   mom_max: float = 0.9, alpha_max: float = 0.01) -> dict:
+    """Per-token gates for the momentum / forget-gate scan, fp32 [nb, nh, T]:
+    mom_t = mom_max * sigmoid(u_t), alpha_t = alpha_max * sigmoid(u'_t), u, u' ~ N(0, 1),
+    keyed like the other streams (a slice is generated exactly as the full workload).
+    The forget gate stays small: with alpha up to 0.1 the memory of the d=64 MLP decays into
+    the LayerNorm's eps regime and the scan's output moves by O(1) under 1e-7 input noise."""
+    bi = list(range(w.B)) if batch_idx is None else list(batch_idx)
+    hi = list(range(w.H)) if head_idx is None else list(head_idx)
+    T = w.T if T is None else T
+    out = {}
+    for name, code, top in (("mom", "u_mom", mom_max), ("alpha", "u_alpha", alpha_max)):
+        arr = np.empty((len(bi), len(hi), T))
+        for i, b in enumerate(bi):
+            for j, h in enumerate(hi):
+                u = _rng(w.seed, code, b, h).standard_normal(w.T)[:T]
+                arr[i, j] = top / (1.0 + np.exp(-u))
+        out[name] = torch.from_numpy(arr).to(torch.float32)
     return out

@@ -173,3 +173,25 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(ops, "_LIB_PATH", "/nonexistent/libttt.so")
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def test_momentum_fwd_checks_before_launch():
+    """ttt_scan_fwd_momentum: null, alignment, workspace and unsupported-flag errors are
+    reported on the host, before anything is enqueued (fake device addresses, no GPU)."""
+    L = ops.lib()
+    P = ctypes.c_void_p
+    c = mlp_d64()
+    need = ops.workspace_size(c, ops.TTT_OP_FWD_MOMENTUM)
+    assert need == 256 + c.B * c.H * 2 * 2 * c.d * c.hidden * 4
+    w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
+
+    def call(cfg, first=0x1000, ws=need, ws_ptr=0x90000):
+        args = [P(first)] + [P(0x1000 * (i + 2)) for i in range(7)]  # Q K V theta mom alpha gamma beta
+        return L.ttt_scan_fwd_momentum(ctypes.byref(cfg.c()), *args, w, None, P(0x70000), w, w, None,
+                                       P(ws_ptr), ws, None)
+    assert call(c, first=0) == 1                    # TTT_ERR_NULL
+    assert call(c, first=0x1008) == 5               # TTT_ERR_ALIGN
+    assert call(c, ws=need - 16) == 6               # TTT_ERR_WORKSPACE
+    assert call(c, ws_ptr=0) == 6
+    assert call(mlp_d64(T=17)) == 2                 # TTT_ERR_SHAPE
+    assert call(mlp_d64(output_key=True)) == 4      # TTT_ERR_UNSUPPORTED

@@ -1,0 +1,99 @@
+"""GPU parity of ttt_scan_fwd_momentum (momentum and forget gate, "Titans와 Miras" Eq. 13/14
+of the TTT-memory page, on the mini-batch scan) against the fp64 oracle's primal scan."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from helpers import TOL, note, ops_config, rel_l2, to_dev
+from oracle import OracleConfig, scan_momentum
+from test_weight_sequence_amd import ops
+from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs, momentum_gates
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(wid, B, H, T, seed_s0=None, mom_max=0.9, alpha_max=0.01):
+    w = WORKLOADS[wid]
+    inp = make_inputs(w, batch_idx=range(B), head_idx=range(H), T=T)
+    inp.update(momentum_gates(w, batch_idx=range(B), head_idx=range(H), T=T, mom_max=mom_max,
+                              alpha_max=alpha_max))
+    cfg = ops_config(w, B=B, H=H, T=T)
+    S0 = None
+    if seed_s0 is not None:
+        g = torch.Generator().manual_seed(seed_s0)
+        S0 = tuple(1e-3 * torch.randn((B, H) + s[2:], generator=g) for s in cfg.weight_shapes((B, H)))
+    return w, cfg, inp, S0
+
+
+def _oracle(w, cfg, inp, S0):
+    flat = flatten_heads(inp)
+    n = cfg.B * cfg.H
+    mom = inp["mom"].to(torch.float64).reshape(n, -1)
+    alpha = inp["alpha"].to(torch.float64).reshape(n, -1)
+    s0 = None if S0 is None else tuple(s.to(torch.float64).reshape(n, *s.shape[2:]) for s in S0)
+    ocfg = OracleConfig(kind=w.kind, chunk=w.chunk)
+    return scan_momentum(flat["Q"], flat["K"], flat["V"], flat["eta"], mom, alpha, flat["W0"], s0,
+                         flat["gamma"], flat["beta"], ocfg)
+
+
+def _run(cfg, inp, S0):
+    d = to_dev(inp)
+    s0 = None if S0 is None else tuple(s.cuda().contiguous() for s in S0)
+    res = ops.scan_fwd_momentum(cfg, d["Q"], d["K"], d["V"], d["eta"], d["mom"], d["alpha"], d["W0"],
+                                d["gamma"], d["beta"], S0=s0, want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    return res
+
+
+@pytest.mark.parametrize("wid,B,H,T,s0", [
+    ("ttt_mlp_fp32_d16", 1, 1, 256, None),
+    ("ttt_mlp_fp32_d16", 1, 1, 256, 5),
+    ("ttt_linear_fp32_d64", 2, 3, 512, 6),
+    ("ttt_mlp_bf16_d64_T8k", 1, 3, 1024, 7),
+    ("ttt_mlp_bf16_d128_T128k", 1, 2, 256, None),
+])
+def test_momentum_scan_matches_oracle(wid, B, H, T, s0):
+    w, cfg, inp, S0 = _case(wid, B, H, T, seed_s0=s0)
+    note(f"momentum {wid} B={B} H={H} T={T} s0={s0}")
+    res = _run(cfg, inp, S0)
+    Z, MT, ST, L = _oracle(w, cfg, inp, S0)
+    tol = TOL["bf16" if w.io == "bf16" else "f32"]
+    n = cfg.B * cfg.H
+    assert rel_l2(res["Z"].reshape(n, T, -1), Z) <= tol
+    assert rel_l2(res["loss"].reshape(n, T), L) <= tol
+    for g, o in zip(res["W_T"] + res["S_T"], MT + ST):
+        assert rel_l2(g.reshape(o.shape), o) <= tol
+
+
+def test_momentum_without_gates_equals_plain_scan():
+    """mom = 0 and alpha = 0 reduce the variant to ttt_scan_fwd (portable kernel, same inputs)."""
+    w, cfg, inp, _ = _case("ttt_mlp_fp32_d16", 1, 1, 256, mom_max=0.0, alpha_max=0.0)
+    note("momentum gates off vs plain scan")
+    res = _run(cfg, inp, None)
+    d = to_dev(inp)
+    gcfg = ops_config(w, B=1, H=1, T=256, force_generic=True)
+    ref = ops.scan_fwd(gcfg, d["Q"], d["K"], d["V"], d["eta"], d["W0"], d["gamma"], d["beta"])
+    torch.cuda.synchronize()
+    assert rel_l2(res["Z"], ref["Z"]) <= 1e-6
+    for a, b in zip(res["W_T"], ref["W_T"]):
+        assert rel_l2(a, b) <= 1e-6
+
+
+def test_momentum_state_carries_across_calls():
+    """Two calls of T/2 tokens, the second started from the first's (W_T, S_T), equal one call."""
+    w, cfg, inp, _ = _case("ttt_linear_fp32_d64", 1, 2, 256)
+    note("momentum carry across calls")
+    full = _run(cfg, inp, None)
+    half = ops_config(w, B=1, H=2, T=128, w0_per_seq=True)
+    cut = lambda x, sl: x[:, :, sl].contiguous() if x.dim() >= 3 else x
+    a_inp = {k: (cut(v, slice(0, 128)) if k in ("Q", "K", "V", "eta", "mom", "alpha") else v) for k, v in inp.items()}
+    a_inp["W0"] = tuple(x.unsqueeze(0).expand(1, *x.shape).contiguous() for x in inp["W0"])
+    a = _run(half, a_inp, None)
+    b_inp = {k: (cut(v, slice(128, 256)) if k in ("Q", "K", "V", "eta", "mom", "alpha") else v) for k, v in inp.items()}
+    b_inp["W0"] = tuple(x.cpu() for x in a["W_T"])
+    b = _run(half, b_inp, tuple(x.cpu() for x in a["S_T"]))
+    assert rel_l2(torch.cat([a["Z"], b["Z"]], dim=2), full["Z"]) <= 1e-6
+    for x, y in zip(b["W_T"] + b["S_T"], full["W_T"] + full["S_T"]):
+        assert rel_l2(x, y) <= 1e-6
