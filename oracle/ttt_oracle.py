@@ -281,3 +281,86 @@ def scan_outer_grads(Q, K, V, eta, W0: tuple, gamma, beta, cfg: OracleConfig,
         "dQ": grads[0], "dK": grads[1], "dV": grads[2], "deta": grads[3],
         "dgamma": grads[4], "dbeta": grads[5], "dW0": tuple(grads[6:]),
     }
+
+
+# ----------------------------------------------------------------------------
+# Large-chunk TTT with SwiGLU fast weights and L2-normalised weights (LaCT)
+# ----------------------------------------------------------------------------
+
+def silu(x: torch.Tensor) -> torch.Tensor:
+    """SiLU(x) = x * sigmoid(x)."""
+    return x * torch.sigmoid(x)
+
+
+def silu_prime(x: torch.Tensor) -> torch.Tensor:
+    """d SiLU / dx = sigmoid(x) * (1 + x * (1 - sigmoid(x)))."""
+    s = torch.sigmoid(x)
+    return s * (1.0 + x * (1.0 - s))
+
+
+def lact_apply(x: torch.Tensor, W: tuple) -> torch.Tensor:
+    """f_W(x) = (SiLU(x W1) * (x W3)) W2 for row vectors x [N, d] (or [N, n, d]):
+    "Test-Time Training(TTT)과 LLM 메모리", section "LaCT", Eq. 6, f_W(x) = W2[SiLU(W1 x) o (W3 x)],
+    with the page's column-vector weights stored transposed: W1, W3 [N, d, h], W2 [N, h, d]."""
+    W1, W2, W3 = W
+    if x.dim() == 2:
+        a = torch.einsum("nd,ndh->nh", x, W1)
+        c = torch.einsum("nd,ndh->nh", x, W3)
+        return torch.einsum("nh,nhd->nd", silu(a) * c, W2)
+    a = torch.einsum("ntd,ndh->nth", x, W1)
+    c = torch.einsum("ntd,ndh->nth", x, W3)
+    return torch.einsum("nth,nhd->ntd", silu(a) * c, W2)
+
+
+def lact_token_grad(k: torch.Tensor, v: torch.Tensor, W: tuple):
+    """Gradient of the token loss l = -f_W(k) . v (same page and section, Eq. 7) with respect to
+    (W1, W2, W3), for row vectors k, v [N, d]. Hand derivation:
+      a = k W1, c = k W3, s = SiLU(a), u = s * c, f = u W2, l = -f . v
+      dl/dW2 = -u^T v;  gu = dl/du = -v W2^T
+      dl/dW3 = k^T (gu * s);  dl/dW1 = k^T (gu * c * SiLU'(a))."""
+    W1, W2, W3 = W
+    a = torch.einsum("nd,ndh->nh", k, W1)
+    c = torch.einsum("nd,ndh->nh", k, W3)
+    s = silu(a)
+    u = s * c
+    gW2 = -torch.einsum("nh,nd->nhd", u, v)
+    gu = -torch.einsum("nd,nhd->nh", v, W2)
+    gW3 = torch.einsum("nd,nh->ndh", k, gu * s)
+    gW1 = torch.einsum("nd,nh->ndh", k, gu * c * silu_prime(a))
+    return gW1, gW2, gW3
+
+
+def l2_normalize_units(W: torch.Tensor) -> torch.Tensor:
+    """Each output unit's weight vector scaled to unit L2 norm. With the row-vector storage
+    [N, inputs, outputs] that is every column (a row of the page's column-vector matrix)."""
+    return W / W.norm(dim=-2, keepdim=True)
+
+
+def scan_lact(Q, K, V, eta, W0: tuple, chunk: int, eta_scale: float = 1.0, apply: str = "after"):
+    """Large-chunk TTT layer of "Test-Time Training(TTT)과 LLM 메모리", section "LaCT": per chunk of
+    b tokens, the gradient g = grad_W sum_i eta_i l(f_W(k_i), v_i) of the chunk's summed loss at
+    the chunk-start weights (Eq. 4 with the loss of Eq. 7), the update W <- L2-Normalize(W - g)
+    (Eq. 8, each weight matrix per output unit), and the output o = f_W(q) (Eq. 2).
+
+    apply = "after": a chunk's tokens are read out with the weights after that chunk's update
+    (the order the section lists the steps in); "before": with the weights the chunk started from.
+    Q, K, V [N, T, d], eta [N, T]; W0 = (W1 [N, d, h], W2 [N, h, d], W3 [N, d, h]).
+    Returns Z [N, T, d] and the final weights."""
+    N, T, d = Q.shape
+    if T % chunk != 0:
+        raise ValueError("T must be a multiple of the chunk size")
+    if apply not in ("after", "before"):
+        raise ValueError(apply)
+    W = tuple(w for w in W0)
+    Z = []
+    for i in range(T // chunk):
+        sl = slice(i * chunk, (i + 1) * chunk)
+        G = tuple(torch.zeros_like(w) for w in W)
+        for t in range(i * chunk, (i + 1) * chunk):
+            g = lact_token_grad(K[:, t], V[:, t], W)
+            step = eta_scale * eta[:, t].reshape(N, 1, 1)
+            G = tuple(acc + step * gw for acc, gw in zip(G, g))
+        W_new = tuple(l2_normalize_units(w - gw) for w, gw in zip(W, G))
+        Z.append(lact_apply(Q[:, sl], W_new if apply == "after" else W))
+        W = W_new
+    return torch.cat(Z, dim=1), W
