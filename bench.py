@@ -68,6 +68,18 @@ def _traffic(kernel: str, n_launch_units: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "" where it cannot be read."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool = False) -> dict:
     """The fp64 oracle on the first n_seq sequences (the first n_heads heads of each, default
     all), first T tokens; with grads, the oracle's outer-loop gradients (autograd through
@@ -91,6 +103,7 @@ def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool 
     dt = time.perf_counter() - t0
     what = "outer-loop gradients (autograd through the primal scan)" if grads else "forward scan"
     return {"value": pairs * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"fp64 oracle {what} on sequences 0..{n_seq - 1} x heads 0..{nh - 1} "
                       f"({pairs} (batch, head) pairs) x first T={T} tokens of the same workload "
                       f"({dt:.1f} s wall, torch intra-op threads={cores})"}

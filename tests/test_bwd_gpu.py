@@ -5,7 +5,7 @@ import math
 import pytest
 import torch
 
-from helpers import TOL, note, rel_l2, to_dev
+from helpers import TOL, assert_parity, note, rel_l2, to_dev
 from oracle import OracleConfig, scan_outer_grads
 from test_weight_sequence_amd import ops
 from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs
@@ -40,13 +40,26 @@ def _oracle_grads(inp, dZ, dWT, kind, chunk, per_seq, **kw):
     return out
 
 
-def _compare(gpu, ora, tol):
-    for k in ("dQ", "dK", "dV", "deta", "dgamma", "dbeta"):
-        e = rel_l2(gpu[k], ora[k])
-        assert e <= tol, (k, e)
-    for i, (a, b) in enumerate(zip(gpu["dW0"], ora["dW0"])):
-        e = rel_l2(a, b)
-        assert e <= tol, ("dW0", i, e)
+def _heads(x):
+    """[B, H, ...] -> [B*H, ...] (per-head leading axis for assert_parity)."""
+    return x.reshape(x.shape[0] * x.shape[1], *x.shape[2:])
+
+
+def _compare(gpu, ora, tol, keys=("dQ", "dK", "dV", "deta", "dgamma", "dbeta", "dW0")):
+    """Whole-tensor and per-head relative L2 of every gradient, and per 16-token chunk (and
+    per token for dQ, dK, dV) where the gradient has a token axis."""
+    for k in ("dQ", "dK", "dV"):
+        if k in keys:
+            assert_parity(_heads(gpu[k]), _heads(ora[k]), tol, k)
+    if "deta" in keys:
+        assert_parity(_heads(gpu["deta"]), _heads(ora["deta"]), tol, "deta", per_token=False)
+    for k in ("dgamma", "dbeta"):
+        if k in keys:
+            assert_parity(gpu[k], ora[k], tol, k, time_axis=False)
+    if "dW0" in keys:
+        for i, (a, b) in enumerate(zip(gpu["dW0"], ora["dW0"])):
+            lead = a.reshape(-1, *a.shape[-2:]) if a.dim() > 3 else a
+            assert_parity(lead, b.reshape(lead.shape), tol, f"dW0[{i}]", time_axis=False)
 
 
 def _rand_case(kind, B, H, T, d, io, seed, per_seq, w_scale=0.2):
@@ -107,11 +120,7 @@ def test_bwd_key_output_matches_oracle(kind, d, chunk, T):
     assert torch.count_nonzero(gpu["dQ"]).item() == 0
     ora = _oracle_grads(inp, dZ, dWT, kind, chunk, False, eta_scale=0.5, output="key")
     assert torch.count_nonzero(ora["dQ"]).item() == 0
-    for k in ("dK", "dV", "deta", "dgamma", "dbeta"):
-        e = rel_l2(gpu[k], ora[k])
-        assert e <= TOL["f32"], (k, e)
-    for i, (a, b) in enumerate(zip(gpu["dW0"], ora["dW0"])):
-        assert rel_l2(a, b) <= TOL["f32"], ("dW0", i)
+    _compare(gpu, ora, TOL["f32"], keys=("dK", "dV", "deta", "dgamma", "dbeta", "dW0"))
 
 
 def test_bwd_mlp_fp32_d16_full_T():
@@ -184,9 +193,8 @@ def test_bwd_mlp_bf16_d64_B4H16_sampled_heads():
         sub = make_inputs(w, batch_idx=[b], head_idx=[h], with_dz=True)
         sdz = sub.pop("dZ")
         ora = _oracle_grads(sub, sdz, None, "mlp", w.chunk, False)
-        for k in ("dQ", "dK", "dV", "deta"):
-            e = rel_l2(gpu[k][b:b + 1, h:h + 1], ora[k])
-            assert e <= TOL["bf16"], (b, h, k, e)
+        one = {k: gpu[k][b:b + 1, h:h + 1] for k in ("dQ", "dK", "dV", "deta")}
+        _compare(one, ora, TOL["bf16"], keys=("dQ", "dK", "dV", "deta"))
 
 
 def test_bwd_mlp_bf16_d64_B4H16_runs_and_is_finite():

@@ -1,12 +1,14 @@
 """GPU parity: the HIP scan (through the C ABI) against the fp64 CPU oracle on the
-same seeded inputs. Tolerances (relative L2 over the whole tensor): 1e-4 for fp32
-I/O, 2e-2 for bf16 I/O (fp32 state in both)."""
+same seeded inputs. Tolerances (relative L2): 1e-4 for fp32 I/O, 2e-2 for bf16 I/O (fp32
+state in both), over the whole tensor and over each head; outputs with a token axis are also
+bounded per 16-token chunk and per token (helpers.assert_parity)."""
 import math
 
 import pytest
 import torch
 
-from helpers import TOL, note, oracle_heads, ops_config, rel_l2, to_dev
+from helpers import (TOL, assert_parity, note, oracle_heads, oracle_perturbed, ops_config, rel_l2,
+                     to_dev)
 from oracle import OracleConfig, f_apply
 from test_weight_sequence_amd import ops
 from test_weight_sequence_amd.synth import WORKLOADS, flatten_heads, make_inputs
@@ -19,17 +21,27 @@ def _run(cfg, d, **kw):
                         **kw)
 
 
+def _sensitive(w) -> bool:
+    """The d = 128 head shape (drifting inputs in its workload): a few tokens are far more
+    sensitive to rounding than the average, so its chunk and token bounds take the oracle's
+    own response to bf16-scale perturbations into account."""
+    return w.d >= 128 or w.drift > 0
+
+
 def _check_heads(res, inp, pairs, w, tol, cfg_kw=None, B_axis=True):
-    Z, WT, L = oracle_heads(inp, pairs, w.kind, w.chunk, **(cfg_kw or {}))
+    out = oracle_heads(inp, pairs, w.kind, w.chunk, perturbed=_sensitive(w), **(cfg_kw or {}))
+    Z, WT, L = out[:3]
+    pz = [p[0] for p in out[3]] if len(out) > 3 else None
+    pl = [p[2] for p in out[3]] if len(out) > 3 else None
     gz = torch.stack([res["Z"][b, h] for b, h in pairs]).cpu()
-    assert rel_l2(gz, Z) <= tol, rel_l2(gz, Z)
+    err = assert_parity(gz, Z, tol, "Z", perturbed=pz)
     for k, wt in enumerate(WT):
         g = torch.stack([res["W_T"][k][b, h] for b, h in pairs]).cpu()
-        assert rel_l2(g, wt) <= tol, (k, rel_l2(g, wt))
+        assert_parity(g, wt, tol, f"W_T[{k}]", time_axis=False)
     if res.get("loss") is not None:
         gl = torch.stack([res["loss"][b, h] for b, h in pairs]).cpu()
-        assert rel_l2(gl, L) <= tol, rel_l2(gl, L)
-    return rel_l2(gz, Z)
+        assert_parity(gl, L, tol, "loss", per_token=False, perturbed=pl)
+    return err
 
 
 # forward variants: the portable kernel, the tuned kernel with a producer/consumer pair of
@@ -136,11 +148,46 @@ def test_mlp_bf16_d128_T128k_sampled_heads_prefix():
     Tp = 4096
     pairs = [(0, 5), (0, 17)]
     pre = {k: (v[:, :, :Tp] if k in ("Q", "K", "V", "eta") else v) for k, v in inp.items()}
-    Z, _, L = oracle_heads(pre, pairs, w.kind, w.chunk)
+    Z, _, L, P = oracle_heads(pre, pairs, w.kind, w.chunk, perturbed=True)
     gz = torch.stack([res["Z"][b, h, :Tp] for b, h in pairs]).cpu()
     gl = torch.stack([res["loss"][b, h, :Tp] for b, h in pairs]).cpu()
-    assert rel_l2(gz, Z) <= TOL["bf16"], rel_l2(gz, Z)
-    assert rel_l2(gl, L) <= TOL["bf16"], rel_l2(gl, L)
+    assert_parity(gz, Z, TOL["bf16"], "Z prefix", perturbed=[p[0] for p in P])
+    assert_parity(gl, L, TOL["bf16"], "loss prefix", per_token=False, perturbed=[p[2] for p in P])
+
+
+def test_mlp_bf16_d128_late_window():
+    """The last 4096 tokens of the 131072-token d=128 workload on two heads, started from the
+    fp64 oracle's weights after token 126976 (rounded to fp32, tests/golden/d128_late_state.npz,
+    written by make_d128_late_state.py from the oracle alone). Both the split kernel (per-
+    sequence W0) and the oracle start from that state, so the check covers the regime where the
+    weights have grown over 7936 chunks, which the prefix check does not reach."""
+    import os
+    import numpy as np
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"]
+    st = np.load(os.path.join(os.path.dirname(__file__), "golden", "d128_late_state.npz"))
+    heads = [int(h) for h in st["heads"]]
+    t0 = int(st["t_start"])
+    Tw = w.T - t0
+    full = make_inputs(w, head_idx=heads)
+    inp = {k: (v[:, :, t0:].contiguous() if k in ("Q", "K", "V", "eta") else v) for k, v in full.items()}
+    inp["W0"] = (torch.from_numpy(st["w1"]).unsqueeze(0), torch.from_numpy(st["w2"]).unsqueeze(0))
+    cfg = ops_config(w, T=Tw, H=2, w0_per_seq=True)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    note(f"mlp bf16 d128 late window heads {heads} tokens {t0}..{w.T}")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    flat, ocfg = _oracle_all(inp, "mlp", w.chunk, per_seq=True)
+    from oracle import scan as oracle_scan
+    Z, WT, L = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
+                           flat["gamma"], flat["beta"], ocfg)
+    P = oracle_perturbed(flat, ocfg)
+    assert_parity(res["Z"].reshape(2, Tw, 128), Z, TOL["bf16"], "Z late window",
+                  perturbed=[p[0] for p in P])
+    assert_parity(res["loss"].reshape(2, Tw), L, TOL["bf16"], "loss late window", per_token=False,
+                  perturbed=[p[2] for p in P])
+    for g, o in zip(res["W_T"], WT):
+        assert_parity(g.reshape(o.shape), o, TOL["bf16"], "W_T late window", time_axis=False)
 
 
 def test_split_partial_group_tanh_per_seq():
@@ -159,10 +206,12 @@ def test_split_partial_group_tanh_per_seq():
     from oracle import scan as oracle_scan
     Z, WT, L = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
                            flat["gamma"], flat["beta"], ocfg)
-    assert rel_l2(res["Z"].reshape(B * H, T, 128), Z) <= TOL["bf16"]
-    assert rel_l2(res["loss"].reshape(B * H, T), L) <= TOL["bf16"]
+    P = oracle_perturbed(flat, ocfg)
+    assert_parity(res["Z"].reshape(B * H, T, 128), Z, TOL["bf16"], "Z", perturbed=[p[0] for p in P])
+    assert_parity(res["loss"].reshape(B * H, T), L, TOL["bf16"], "loss", per_token=False,
+                  perturbed=[p[2] for p in P])
     for g, o in zip(res["W_T"], WT):
-        assert rel_l2(g.reshape(o.shape), o) <= TOL["bf16"]
+        assert_parity(g.reshape(o.shape), o, TOL["bf16"], "W_T", time_axis=False)
 
 
 def test_split_more_heads_than_one_launch():
@@ -251,9 +300,9 @@ def test_pair_tanh_per_seq():
     from oracle import scan as oracle_scan
     Z, WT, _ = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
                            flat["gamma"], flat["beta"], ocfg)
-    assert rel_l2(res["Z"].reshape(B * H, T, 64), Z) <= TOL["bf16"]
+    assert_parity(res["Z"].reshape(B * H, T, 64), Z, TOL["bf16"], "Z")
     for g, o in zip(res["W_T"], WT):
-        assert rel_l2(g.reshape(o.shape), o) <= TOL["bf16"]
+        assert_parity(g.reshape(o.shape), o, TOL["bf16"], "W_T", time_axis=False)
 
 
 def _rand_case(kind, B, H, T, d, chunk, io, seed, per_seq=False):
@@ -305,10 +354,10 @@ def test_edge_shapes_fp32(kind, d, chunk, T, gelu, eta_scale, per_seq):
     from oracle import scan
     Z, WT, L = scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"], flat["gamma"],
                     flat["beta"], ocfg)
-    assert rel_l2(res["Z"].reshape(B * H, T, d), Z) <= TOL["f32"]
-    assert rel_l2(res["loss"].reshape(B * H, T), L) <= TOL["f32"]
+    assert_parity(res["Z"].reshape(B * H, T, d), Z, TOL["f32"], "Z")
+    assert_parity(res["loss"].reshape(B * H, T), L, TOL["f32"], "loss", per_token=False)
     for g, o in zip(res["W_T"], WT):
-        assert rel_l2(g.reshape(o.shape), o) <= TOL["f32"]
+        assert_parity(g.reshape(o.shape), o, TOL["f32"], "W_T", time_axis=False)
 
 
 def test_eta_zero_gives_initial_map():
@@ -323,7 +372,7 @@ def test_eta_zero_gives_initial_map():
                                                    for x in flat["W0"]),
                                flat["gamma"][n], flat["beta"][n], OracleConfig())
                        for n in range(6)])
-    assert rel_l2(res["Z"].reshape(6, 64, 64), ref) <= TOL["bf16"]
+    assert_parity(res["Z"].reshape(6, 64, 64), ref, TOL["bf16"], "Z")
     for g, w0 in zip(res["W_T"], inp["W0"]):
         assert torch.equal(g.cpu(), w0.unsqueeze(0).expand(2, *w0.shape))
 
@@ -373,7 +422,8 @@ def test_decode_loop_equals_scan(wid):
                                   _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc,
                                   t % w.chunk))
     Zd = torch.stack(zs, dim=2)
-    assert rel_l2(Zd, scan_res["Z"]) <= TOL[w.io]
+    assert_parity(Zd.reshape(B * H, T, -1), scan_res["Z"].reshape(B * H, T, -1), TOL[w.io],
+                  "decode loop vs scan")
     for a, b in zip(Ws, scan_res["W_T"]):
         assert rel_l2(a, b) <= TOL[w.io]
     for a in acc:
@@ -407,7 +457,7 @@ def test_decode_stream_equals_oracle(io, gelu):
               for t in range(T)]
         Z = torch.stack(zs, dim=2).cpu().reshape(B * H, T, 64)
         tol = TOL[io]
-        assert rel_l2(Z, Zo) <= tol, (generic, rel_l2(Z, Zo))
+        assert_parity(Z, Zo, tol, f"decode Z generic={generic}")
         for a, b in zip(Ws, WTo):
             assert rel_l2(a.cpu().reshape(b.shape), b) <= TOL["f32"], generic
         for a in acc:
@@ -438,7 +488,8 @@ def test_key_output_forward_and_decode(wid, kind):
     zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
                           _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t % w.chunk)
           for t in range(T)]
-    assert rel_l2(torch.stack(zs, dim=2), res["Z"]) <= TOL[w.io]
+    assert_parity(torch.stack(zs, dim=2).reshape(B * H, T, -1), res["Z"].reshape(B * H, T, -1),
+                  TOL[w.io], "key-output decode vs scan")
     for a, b in zip(Ws, res["W_T"]):
         assert rel_l2(a, b) <= TOL["f32"]
 
@@ -460,7 +511,7 @@ def test_scan_then_decode_continues_the_sequence():
           for t in range(T0, T)]
     Z = torch.cat([pre["Z"], torch.stack(zs, dim=2)], dim=2)
     Zo, WTo, _ = oracle_heads(inp, [(0, 0)], w.kind, w.chunk)
-    assert rel_l2(Z[0], Zo) <= TOL["f32"]
+    assert_parity(Z[0], Zo, TOL["f32"], "scan+decode Z")
     for a, b in zip(Ws, WTo):
         assert rel_l2(a[0], b) <= TOL["f32"]
 
