@@ -189,13 +189,17 @@ def bench_scan_fwd(args, wid: str) -> dict:
         raise RuntimeError("kernel reported non-finite values")
     k_avg = statistics.fmean(kms)
     units = w.B * w.H * w.T
-    flop = units * flops_per_token_head(w.d, w.hidden, w.chunk)
+    # A mini-batch larger than 16 tokens is evaluated in 16-token blocks (the dual-form tril
+    # products inside a block, the earlier blocks through the running weights), so the work per
+    # token is that of b = 16 however large the mini-batch is.
+    flop = units * flops_per_token_head(w.d, w.hidden, min(w.chunk, 16))
     achieved = flop / (k_avg * 1e-3) / 1e12
     mfma = kernel != "ttt_fwd_generic"
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
     io_bytes = 2 if w.io == "bf16" else 4
     metric = ("TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)"
-              if headline else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}")
+              if headline else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}" +
+              (f", mini-batch {w.chunk}" if w.chunk != 16 else ""))
     out = _base_record(args, metric, units / (ms_step * 1e-3), ms_step, w, kernel,
                        "bf16" if mfma else "f32")
     out["roofline"] = {
@@ -371,14 +375,18 @@ def main():
                     help="untimed steps (default 5; 1 for the d=128 workload)")
     ap.add_argument("--workload", default="scan_fwd",
                     choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode",
-                             "scan_fwd_momentum"],
+                             "scan_fwd_momentum", "scan_fwd_bigchunk"],
                     help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
                          "scan_fwd_b16: the same head shape at B=16 (192 heads, 131,072 tokens "
                          "per batch); "
                          "scan_fwd_d128: B=1 H=24 T=131072 d=128 forward; "
                          "scan_fwd_momentum: the B=8 forward with momentum and forget gate; "
+                         "scan_fwd_bigchunk: the B=8 forward with mini-batches of --chunk "
+                         "tokens (256 or 1024); "
                          "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
+    ap.add_argument("--chunk", type=int, default=256, choices=[256, 1024],
+                    help="mini-batch size of the scan_fwd_bigchunk workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-T", type=int, default=8192)
@@ -425,6 +433,8 @@ def main():
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k_B16")
     elif args.workload == "scan_fwd_d128":
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
+    elif args.workload == "scan_fwd_bigchunk":
+        out = bench_scan_fwd(args, f"ttt_mlp_bf16_d64_T8k_b{args.chunk}")
     elif args.workload == "scan_bwd":
         out = bench_scan_bwd(args)
     elif args.workload == "scan_fwd_momentum":

@@ -31,9 +31,9 @@ VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 NO_VGPR_FORM = {"ttt_bwd_mfma.hip"}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    flags = COMMON + ([] if os.path.basename(src) in NO_VGPR_FORM else VGPR_FORM)
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    flags = COMMON + list(extra) + ([] if os.path.basename(src) in NO_VGPR_FORM else VGPR_FORM)
     cmd = [HIPCC, *flags, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *flags, "-x", "hip", "-c", src, "-o", obj]
@@ -43,20 +43,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, lib: str = LIB, build_dir: str = BUILD, extra=()) -> str:
+    """Compile every source under csrc/ (with the extra compiler flags) and link `lib`."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 if __name__ == "__main__":

@@ -18,6 +18,16 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Mini-batches above kMaxChunk tokens run on the paired d = 64 kernel only (forward scan and
+// decode): MLP, d = 64, hidden = 256, bf16 I/O, a multiple of 16 up to kMaxPairChunk tokens,
+// at most kPairMaxHeads (batch, head) pairs, and none of the flags that select another kernel.
+bool large_chunk_ok(const ttt_config* c) {
+  return c->kind == TTT_MLP && c->d == 64 && c->hidden == 256 && c->io_dtype == TTT_BF16 &&
+         c->chunk % 16 == 0 && c->chunk <= kMaxPairChunk &&
+         !(c->flags & (TTT_FORCE_GENERIC | TTT_OUTPUT_KEY | TTT_ONE_WG_PER_HEAD)) &&
+         static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
+}
+
 ttt_status check_common(const ttt_config* c, bool need_T) {
   if (!c) return TTT_ERR_NULL;
   if (c->kind != TTT_LINEAR && c->kind != TTT_MLP) return TTT_ERR_UNSUPPORTED;
@@ -30,7 +40,7 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   if (need_T && c->T < 1) return TTT_ERR_SHAPE;
   if (c->d < 16 || c->d > 128 || c->d % 16 != 0) return TTT_ERR_UNSUPPORTED;
   if (c->kind == TTT_MLP && c->hidden != 4 * c->d) return TTT_ERR_UNSUPPORTED;
-  if (c->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;
+  if (c->chunk > kMaxChunk && !large_chunk_ok(c)) return TTT_ERR_UNSUPPORTED;
   if (need_T && c->T % c->chunk != 0) return TTT_ERR_SHAPE;
   if (!std::isfinite(c->ln_eps) || c->ln_eps < 0.f) return TTT_ERR_ARG;
   if (!std::isfinite(c->eta_scale)) return TTT_ERR_ARG;
@@ -38,7 +48,8 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   const double elems = static_cast<double>(c->B) * c->H * (need_T ? c->T : 1) * c->d;
   if (static_cast<double>(c->B) * c->H > 2147483647.0 || elems > 9.0e15) return TTT_ERR_SHAPE;
   const int hid = c->kind == TTT_MLP ? c->hidden : c->d;
-  if (fwd_generic_lds_bytes(c->kind, c->d, hid, c->chunk) > kMaxLds) return TTT_ERR_UNSUPPORTED;
+  if (c->chunk <= kMaxChunk && fwd_generic_lds_bytes(c->kind, c->d, hid, c->chunk) > kMaxLds)
+    return TTT_ERR_UNSUPPORTED;
   return TTT_OK;
 }
 
@@ -74,8 +85,9 @@ bool use_mfma(const ttt_config* c) {
 }
 
 bool use_pair(const ttt_config* c) {
-  return use_mfma(c) && !(c->flags & TTT_ONE_WG_PER_HEAD) &&
-         static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
+  if (!tuned_allowed(c) || (c->flags & TTT_ONE_WG_PER_HEAD)) return false;
+  ScanParams p = scan_params(c);
+  return fwd_pair_supported(p) && static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
 }
 
 bool use_split(const ttt_config* c) {
@@ -158,7 +170,10 @@ ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) 
   if (st != TTT_OK) return st;
   switch (op) {
     case TTT_OP_FWD: *bytes = fwd_ws_bytes(cfg); return TTT_OK;
-    case TTT_OP_BWD: *bytes = bwd_ws_bytes(cfg); return TTT_OK;
+    case TTT_OP_BWD:
+      if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // no backward for these
+      *bytes = bwd_ws_bytes(cfg);
+      return TTT_OK;
     case TTT_OP_DECODE: *bytes = kStatusBytes; return TTT_OK;
     case TTT_OP_FWD_MOMENTUM:
       if (fwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk, true) > kMaxLds)
@@ -186,7 +201,7 @@ const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
 }
 
 const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
-  if (check_common(cfg, true) != TTT_OK) return "";
+  if (check_common(cfg, true) != TTT_OK || cfg->chunk > kMaxChunk) return "";
   return use_bwd_mfma(cfg) ? "ttt_bwd_mfma_d64" : "ttt_bwd_generic";
 }
 
@@ -233,6 +248,7 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
+  if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // only the paired kernel takes these
   if (use_split(cfg) && fwd_split_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_split(p, s));
   return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
 }
@@ -297,6 +313,7 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
                         float* dbeta, void* workspace, size_t ws_bytes, void* stream) {
   ttt_status st = check_common(cfg, true);
   if (st != TTT_OK) return st;
+  if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // no backward for these
   const bool mlp = cfg->kind == TTT_MLP;
   if (!Q || !K || !V || !eta || !ln_gamma || !ln_beta || !saved || !dZ || !dQ || !dK || !dV ||
       !deta || !dW0 || !dW0->w1)
@@ -364,6 +381,7 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
                            void* stream) {
   ttt_status st = check_common(cfg, false);
   if (st != TTT_OK) return st;
+  if (cfg->chunk > kMaxChunk && !use_decode_stream(cfg)) return TTT_ERR_UNSUPPORTED;
   const bool mlp = cfg->kind == TTT_MLP;
   if (!q || !k || !v || !eta || !ln_gamma || !ln_beta || !W_start || !acc || !z ||
       !W_start->w1 || !acc->w1)

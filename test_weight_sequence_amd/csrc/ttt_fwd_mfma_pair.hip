@@ -34,9 +34,36 @@
 // Every wait is bounded. On expiry the status word gets kStatusTimeout, later waits return
 // at once, and the kernel runs to completion with meaningless outputs. The launch is
 // cooperative, so the two workgroups of a pair are always co-resident.
+//
+// Mini-batches larger than 16 tokens (b = 16 m, up to 1024): the kernel still walks the
+// sequence in 16-token sub-tiles, and the consumer is unchanged (its running weights are the
+// mini-batch start plus the updates of the sub-tiles before, so its query side is the dual
+// form of the whole mini-batch evaluated block by block: the tril products inside a sub-tile,
+// the earlier sub-tiles through the running weights). The producer takes every gradient of
+// the mini-batch at the weights the mini-batch started from, so its bf16 weight copies, their
+// transposes and the look-ahead correction are made once per mini-batch instead of once per
+// sub-tile; the fp32 weights still take each sub-tile's update in order, bit for bit as in
+// the consumer.
 #include "ttt_mfma_common.hpp"
 
 namespace ttt {
+
+#ifdef TTT_PHASE_CLOCKS
+// Opt-in timing build (test_weight_sequence_amd/phase_clocks.py builds it into a separate
+// library; the product library is compiled without it): shader-clock stamps at the phase
+// boundaries of each chunk of head 0, summed per wave over chunks 16 .. end.
+// [side: producer, consumer][wave][slot]: slots 0..7 phase sums, 8 chunk count, 9 last stamp,
+// 10 first counted stamp.
+__device__ unsigned long long g_phase_clocks[2][8][16];
+#define TTT_STAMP(var)        \
+  unsigned long long var;     \
+  asm volatile("s_memtime %0\n s_waitcnt lgkmcnt(0)" : "=s"(var)::"memory")
+#define TTT_DEP(x) asm volatile("" ::"v"(x))
+#else
+#define TTT_STAMP(var)
+#define TTT_DEP(x)
+#endif
+
 namespace {
 
 using namespace mfma;
@@ -233,6 +260,13 @@ __device__ __forceinline__ void cvt_w(const f4 (&W1c)[NDT][NHT], const f4 (&W2c)
     W2b8[dt] = cat(cvt4(W2c[0][dt]), cvt4(W2c[1][dt]));
   }
 }
+// bf16 operand copy of the fp32 W1 tiles alone.
+__device__ __forceinline__ void cvt_w1(const f4 (&W1c)[NDT][NHT], bf16x4 (&W1b)[NDT][NHT]) {
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) W1b[dt][ht] = cvt4(W1c[dt][ht]);
+}
 // X W1 for this wave's h tiles (X as row operands).
 __device__ __forceinline__ void xw1(const bf16x8 (&a)[2], const bf16x4 (&W1b)[NDT][NHT], f4 (&out)[NHT]) {
 #pragma unroll
@@ -247,6 +281,7 @@ __device__ __forceinline__ void xw1(const bf16x8 (&a)[2], const bf16x4 (&W1b)[ND
 // Per-workgroup view of one (batch, head).
 struct Ctx {
   int tid, lane, w, g, c16, head, hidx, hs, T, nchunks;
+  int m;            // 16-token sub-tiles per mini-batch (chunk / 16)
   unsigned* flags;  // counter words of this head
   char* ring;       // ring of this head
   const __bf16* Kg;
@@ -272,7 +307,7 @@ __device__ __forceinline__ void head_init(const ScanParams& p, const Ctx& x, Hea
   }
 }
 
-template <int GELU_KIND, bool LOCAL>
+template <int GELU_KIND, bool LOCAL, bool LARGE>
 __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x, ProdSmem& S) {
   const int tid = x.tid, lane = x.lane, w = x.w, g = x.g, c16 = x.c16, head = x.head, hs = x.hs;
   const int T = x.T, nchunks = x.nchunks;
@@ -332,25 +367,54 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   __syncthreads();
   const bf16x4 zz = lds4(S.zeros);
 
+  // bf16 operand copies of the weights the current mini-batch's gradients are taken at (the
+  // mini-batch start): made once per mini-batch. With 16-token mini-batches that is every
+  // sub-tile; with larger ones every sub-tile of the mini-batch reuses them.
+  // (kept across sub-tiles only for mini-batches above 16 tokens; with 16-token mini-batches
+  // each step makes its own, which keeps them out of the registers live across the loop)
+  struct WCopies {
+    bf16x4 W1b[NDT][NHT];
+    bf16x8 W2b8[NDT];
+    bf16x4 W2Tb[NDT][NHT];
+  };
+  WCopies keep;
+  const int m = LARGE ? x.m : 1;
   // chunk 0 enters with P = K(0) W0, and zero look-ahead terms
   Carry ca{}, cb{};
   {
-    bf16x4 W1b[NDT][NHT];
-    bf16x8 W2b8[NDT];
-    cvt_w(W1c, W2c, W1b, W2b8);
+    cvt_w(W1c, W2c, keep.W1b, keep.W2b8);
     bf16x8 aK[2];
     rows(S.st[0].K, g, c16, aK);
-    xw1(aK, W1b, ca.P);
+    xw1(aK, keep.W1b, ca.P);
   }
 
+#ifdef TTT_PHASE_CLOCKS
+  unsigned long long pacc[11] = {};
+#endif
   auto step = [&](const int c, const Carry& in, Carry& out) {
+    TTT_STAMP(s0);
     const PStage& st = S.st[c & 3];
     const int t0 = c * BC;
     const Ld ld = gload(min(c + 2, nchunks - 1));
-    // H^K(c) = K(c) W1(c-1) + (K(c) K(c-1)^T) E1n(c-1)
+    // sub-tile c of a mini-batch of m sub-tiles: the first one starts from the weights after
+    // every update so far, the others take their gradients at those same weights
+    const int sub = LARGE ? c % m : 0;
+    const bool first = sub == 0, last = sub == m - 1;
+    WCopies local;
+    WCopies& wc = LARGE ? keep : local;
+    auto& W1b = wc.W1b;
+    auto& W2b8 = wc.W2b8;
+    auto& W2Tb = wc.W2Tb;
+    // first: H^K(c) = K(c) W1(c-1) + (K(c) K(c-1)^T) E1n(c-1) (the look-ahead plus the update
+    // of the sub-tile before); otherwise H^K(c) = K(c) W1(start), computed one step ahead
     f4 hk[NHT];
-    hk[0] = mfma32(cat(in.sA, zz), in.e1, in.P[0]);
-    hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
+    if (first) {
+      hk[0] = mfma32(cat(in.sA, zz), in.e1, in.P[0]);
+      hk[1] = mfma32(cat(zz, in.sA), in.e1, in.P[1]);
+    } else {
+      hk[0] = in.P[0];
+      hk[1] = in.P[1];
+    }
     // the update of chunk c - 1 (W(c) = W(c-1) + ...), next to the GELU work
     // (at chunk 0 the carry is zero and the operands are zero-filled: an exact no-op)
     chunk_update(W1c, W2c, S.st[(c - 1) & 3].K, S.E2, in.e1, in.ak, g, c16, zz);
@@ -371,6 +435,9 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       akR[ht] = cvt4(a);
     }
     out.ak = cat(akR[0], akR[1]);
+    TTT_DEP(out.ak[0]);
+    TTT_DEP(gk[0][0]);
+    TTT_STAMP(s1);
     // scheduling hint: issue the 16 update MFMAs one at a time between runs of 4 VALU
     // instructions of the GELU above, so the matrix unit works while the VALU does
     // (runs of 2, 3, 5, 6 or 8 measured slower)
@@ -379,19 +446,24 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    bf16x4 W1b[NDT][NHT];
-    bf16x8 W2b8[NDT];
-    cvt_w(W1c, W2c, W1b, W2b8);
-    // look-ahead for chunk c + 1: K(c+1) W1(c) and K(c+1) K(c)^T (after the last chunk the
-    // slot holds other data and the result is not used)
+    if (first)
+      cvt_w(W1c, W2c, W1b, W2b8);  // the new mini-batch's start weights
+    else if (last)
+      cvt_w1(W1c, W1b);  // W1 with every update but this sub-tile's, for the next look-ahead
+    // look-ahead for sub-tile c + 1: K(c+1) W1 and, when c + 1 starts a mini-batch,
+    // K(c+1) K(c)^T for the update of sub-tile c (after the last sub-tile the slot holds
+    // other data and the result is not used)
     {
-      bf16x8 aK[2], aK1[2];
-      rows(st.K, g, c16, aK);
+      bf16x8 aK1[2];
       rows(S.st[(c + 1) & 3].K, g, c16, aK1);
       xw1(aK1, W1b, out.P);
-      f4 sT = mfma32(aK[0], aK1[0], zero4());  // C[t][t'] = K(c)_t . K(c+1)_t'
-      sT = mfma32(aK[1], aK1[1], sT);
-      out.sA = cvt4(sT);
+      if (last) {
+        bf16x8 aK[2];
+        rows(st.K, g, c16, aK);
+        f4 sT = mfma32(aK[0], aK1[0], zero4());  // C[t][t'] = K(c)_t . K(c+1)_t'
+        sT = mfma32(aK[1], aK1[1], sT);
+        out.sA = cvt4(sT);
+      }
     }
     // Z^K partial over this wave's h slice
     const bf16x8 akT8 = cat(cvt4(mfma32(out.ak, id.ilo, zero4())), cvt4(mfma32(out.ak, id.ihi, zero4())));
@@ -401,8 +473,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.red[w][dt][r][lane] = acc[r];
     }
-    // W2(c)^T tiles for E1n: waves 0..3 now, waves 4..7 during the LayerNorm
-    bf16x4 W2Tb[NDT][NHT];
+    TTT_STAMP(s2);
+    // W2^T tiles for E1n (once per mini-batch): waves 0..3 now, waves 4..7 during the LayerNorm
     auto w2t = [&]() {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -414,7 +486,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     // the barrier: K + beta - V and -eta for token 4w + lane/16
     float kvb[NDT] = {0.f, 0.f, 0.f, 0.f}, neta = 0.f;
     if (w < 4) {
-      w2t();
+      if (first) w2t();
       const int t = 4 * w + g;
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
@@ -432,11 +504,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     }
     // chunks the consumer is done reading (checked after the barriers)
     const unsigned cons = ho.ld(16);
-    if (p.saved) {
-      float* sv = p.saved + (static_cast<size_t>(head) * nchunks + c) * (2 * D * HID);
+    if (p.saved && first) {
+      float* sv = p.saved + (static_cast<size_t>(head) * (nchunks / m) + c / m) * (2 * D * HID);
       wtiles_store(sv, sv + D * HID, g, c16, hs, W1c, W2c);
     }
+    TTT_STAMP(s3);
     __syncthreads();
+    TTT_STAMP(s4);
 
     if (w < 4) {
       // LayerNorm forward/backward of Z^K: token 4w + lane/16, 16 lanes each
@@ -476,10 +550,12 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       // mean(g) is non-finite whenever any residual (inputs, Z^K) is
       if (c16 == 0) flag_nonfinite(p.status, mg);
     } else {
-      w2t();
+      if (first) w2t();
       if (c + 2 < nchunks) stage_write(c + 2, ld);
     }
+    TTT_STAMP(s5);
     __syncthreads();
+    TTT_STAMP(s6);
 
     // E1n(c) = (En2 W2^T) (.) G
     bf16x8 aE[2];
@@ -493,6 +569,8 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       e1[ht] = cvt4(acc * gk[ht]);
     }
     out.e1 = cat(e1[0], e1[1]);
+    TTT_DEP(out.e1[0]);
+    TTT_STAMP(s7);
 
     // hand chunk c to the consumer: slot c % RING must have been read (chunk c - RING)
     const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
@@ -506,6 +584,16 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
       ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, RS, 2, g, c16), tgroup(S.E2, RS, 3, g, c16)));
     }
     compiler_fence();
+#ifdef TTT_PHASE_CLOCKS
+    TTT_STAMP(s8);
+    if (c >= 16) {
+      const unsigned long long ph[8] = {s1 - s0, s2 - s1, s3 - s2, s4 - s3, s5 - s4, s6 - s5, s7 - s6, s8 - s7};
+      for (int k = 0; k < 8; ++k) pacc[k] += ph[k];
+      pacc[8] += 1;
+      pacc[9] = s8;
+    }
+    if (c == 16) pacc[10] = s0;
+#endif
   };
 
   // two chunks per trip, so the carried registers alternate without copies
@@ -523,6 +611,10 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   if (p.wt_1)
     wtiles_store(p.wt_1 + static_cast<size_t>(head) * D * HID, p.wt_2 + static_cast<size_t>(head) * HID * D,
                  g, c16, hs, W1c, W2c);
+#ifdef TTT_PHASE_CLOCKS
+  if (head == 0 && lane == 0)
+    for (int k = 0; k < 11; ++k) g_phase_clocks[0][w][k] = pacc[k];
+#endif
   return;
 }
 
@@ -587,7 +679,11 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     if (c16 == 0) flag_nonfinite(p.status, chk);
   };
 
+#ifdef TTT_PHASE_CLOCKS
+  unsigned long long cacc[11] = {};
+#endif
   auto step = [&](const int c, const Slot& cur, Slot& nxt) {
+    TTT_STAMP(s0);
     const int sl = c % 3;
     const PStage& st = S.st[sl];
     const bool has_next = c + 1 < nchunks;
@@ -622,6 +718,8 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       aqR[ht] = cvt4(a);
     }
     const bf16x8 aqR8 = cat(aqR[0], aqR[1]);
+    TTT_DEP(aqR8[0]);
+    TTT_STAMP(s1);
     const bf16x8 aqT8 = cat(cvt4(mfma32(aqR8, id.ilo, zero4())), cvt4(mfma32(aqR8, id.ihi, zero4())));
     const bf16x8 akT8 = cat(cvt4(mfma32(cur.ak, id.ilo, zero4())), cvt4(mfma32(cur.ak, id.ihi, zero4())));
     // Z^Q partial = A^Q W2 + tril(A^Q A^K^T) En2 over this wave's h slice
@@ -638,6 +736,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
 #pragma unroll
       for (int r = 0; r < 4; ++r) S.red[c & 1][w][dt][r][lane] = acc[r];
     }
+    TTT_STAMP(s2);
     // the producer's chunk-end update, from the same operands
     update_mfmas(W1c, W2c, cat(tgroup(st.K, RS, 0, g, c16), tgroup(st.K, RS, 1, g, c16)),
                  cat(tgroup(st.K, RS, 2, g, c16), tgroup(st.K, RS, 3, g, c16)), cur.e2[0], cur.e2[1], cur.e1,
@@ -649,6 +748,7 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       asm volatile("" ::"v"(dep) : "memory");
       compiler_fence();
     }
+    TTT_STAMP(s3);
     if (has_next) {
       const unsigned need = static_cast<unsigned>(c + 2);
       if (min(rdy_own, rdy_0) < need) {
@@ -659,9 +759,21 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
       slot_load(ho, nxt, c + 1, w, lane);
       stage_write((c + 1) % 3, ld);
     }
+    TTT_STAMP(s4);
     __syncthreads();
+    TTT_STAMP(s5);
     if (w == 0 && lane == 0) ho.st(16, static_cast<unsigned>(c + 1));
     if (w < 4) ln_out(c);
+#ifdef TTT_PHASE_CLOCKS
+    TTT_STAMP(s6);
+    if (c >= 16) {
+      const unsigned long long ph[6] = {s1 - s0, s2 - s1, s3 - s2, s4 - s3, s5 - s4, s6 - s5};
+      for (int k = 0; k < 6; ++k) cacc[k] += ph[k];
+      cacc[8] += 1;
+      cacc[9] = s6;
+    }
+    if (c == 16) cacc[10] = s0;
+#endif
   };
 
   spin_geq(ho, w, 1u, p.status);
@@ -675,9 +787,13 @@ __device__ __forceinline__ void consumer_body(const ScanParams& p, const Ctx& x,
     step(c + 1, sb, sa);
   }
   if (c < nchunks) step(c, sa, sb);
+#ifdef TTT_PHASE_CLOCKS
+  if (x.head == 0 && lane == 0)
+    for (int k = 0; k < 11; ++k) g_phase_clocks[1][w][k] = cacc[k];
+#endif
 }
 
-template <int GELU_KIND>
+template <int GELU_KIND, bool LARGE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_pair_kernel(ScanParams p, Pair q) {
   __shared__ SmemP sm;
@@ -695,6 +811,7 @@ fwd_mfma_pair_kernel(ScanParams p, Pair q) {
   x.hs = x.w * HS;
   x.T = p.T;
   x.nchunks = p.T / BC;
+  x.m = p.chunk / BC;
   x.flags = q.flags + static_cast<size_t>(x.head) * FLAG_WORDS;
   x.ring = q.ring + static_cast<size_t>(x.head) * RING * SLOT_BYTES;
   const size_t io_off = static_cast<size_t>(x.head) * p.T * D;
@@ -717,9 +834,9 @@ fwd_mfma_pair_kernel(ScanParams p, Pair q) {
   const bool local = other == xcc + 1 && !(p.flags & TTT_FORCE_DEVICE_SCOPE);
   if (producer) {
     if (local)
-      producer_body<GELU_KIND, true>(p, x, sm.p);
+      producer_body<GELU_KIND, true, LARGE>(p, x, sm.p);
     else
-      producer_body<GELU_KIND, false>(p, x, sm.p);
+      producer_body<GELU_KIND, false, LARGE>(p, x, sm.p);
   } else {
     if (local)
       consumer_body<GELU_KIND, true>(p, x, sm.c);
@@ -737,6 +854,11 @@ size_t flag_bytes(int nheads) {
 }
 
 }  // namespace
+
+bool fwd_pair_supported(const ScanParams& p) {
+  return p.kind == TTT_MLP && p.d == D && p.hid == HID && p.io == TTT_BF16 && p.chunk >= BC &&
+         p.chunk % BC == 0 && p.chunk <= kMaxPairChunk;
+}
 
 size_t fwd_pair_workspace_bytes(int nheads) {
   return flag_bytes(nheads) + static_cast<size_t>(nheads) * RING * SLOT_BYTES;
@@ -758,7 +880,7 @@ bool fwd_pair_fits(int nheads) {
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF>), NT, 0) == hipSuccess;
+            &per_cu, reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF, true>), NT, 0) == hipSuccess;
     cap[dev] = 1 + ((ok && coop) ? ncu * per_cu : 0);
   }
   return fwd_pair_blocks(nheads) <= cap[dev] - 1;
@@ -776,9 +898,21 @@ hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   ScanParams pc = p;
   void* args[] = {&pc, &q};
-  const void* fn = p.gelu == TTT_GELU_TANH ? reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_TANH>)
-                                           : reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF>);
+  // one kernel per mini-batch regime, so that the 16-token one keeps its own register allocation
+  const bool large = p.chunk > BC;
+  const void* fn = p.gelu == TTT_GELU_TANH
+                       ? (large ? reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_TANH, true>)
+                                : reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_TANH, false>))
+                       : (large ? reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF, true>)
+                                : reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF, false>));
   return hipLaunchCooperativeKernel(fn, dim3(fwd_pair_blocks(nheads)), dim3(NT), args, 0, stream);
 }
 
 }  // namespace ttt
+
+#ifdef TTT_PHASE_CLOCKS
+// Copies the per-phase clock sums of the last launch to host memory (2 * 8 * 16 values).
+extern "C" int ttt_phase_clocks_read(unsigned long long* host) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(ttt::g_phase_clocks), sizeof(ttt::g_phase_clocks)) == hipSuccess ? 0 : 1;
+}
+#endif

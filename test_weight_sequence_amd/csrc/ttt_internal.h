@@ -100,6 +100,10 @@ hipError_t launch_fwd_mfma(const ScanParams& p, hipStream_t s);
 // (after the status word), its grid size, whether the current device can co-schedule that
 // grid, and its launcher (wbuf points at the region).
 constexpr int kPairMaxHeads = 128;
+// Largest mini-batch of the paired kernel (a multiple of 16 tokens); every other kernel takes
+// mini-batches of at most kMaxChunk tokens.
+constexpr int kMaxPairChunk = 1024;
+bool fwd_pair_supported(const ScanParams& p);
 size_t fwd_pair_workspace_bytes(int nheads);
 int fwd_pair_blocks(int nheads);
 bool fwd_pair_fits(int nheads);

@@ -59,6 +59,11 @@ WORKLOADS = {
     # seed as the B=8 workload, so its first eight sequences are that workload's inputs
     "ttt_mlp_bf16_d64_T8k_B16": Workload("ttt_mlp_bf16_d64_T8k_B16", "mlp", 16, 12, 8192, 64, 256, 16, "bf16", 0.1,
                 "normal", seed=1003),
+    # the B=8 d=64 T=8192 inputs (same seed) with large mini-batches of 256 and 1024 tokens
+    "ttt_mlp_bf16_d64_T8k_b256": Workload("ttt_mlp_bf16_d64_T8k_b256", "mlp", 8, 12, 8192, 64, 256, 256, "bf16", 0.1,
+                "normal", seed=1003),
+    "ttt_mlp_bf16_d64_T8k_b1024": Workload("ttt_mlp_bf16_d64_T8k_b1024", "mlp", 8, 12, 8192, 64, 256, 1024, "bf16",
+                0.1, "normal", seed=1003),
 }
 
 

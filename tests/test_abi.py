@@ -54,7 +54,14 @@ def mlp_d64(**kw):
     (dict(d=8, hidden=32), 4),
     (dict(d=144, hidden=576), 4),
     (dict(d=40, hidden=160), 4),     # not a multiple of 16
-    (dict(chunk=32), 4),
+    (dict(chunk=32), 0),             # larger mini-batches: the paired d=64 bf16 kernel
+    (dict(chunk=1024, T=8192), 0),
+    (dict(chunk=24), 4),             # above 16 only multiples of 16
+    (dict(chunk=2048), 4),           # at most 1024
+    (dict(chunk=32, io="f32"), 4),   # no other kernel takes mini-batches above 16
+    (dict(chunk=32, B=16), 4),       # more heads than the paired kernel's 128
+    (dict(chunk=32, force_generic=True), 4),
+    (dict(chunk=32, one_wg_per_head=True), 4),
     (dict(chunk=0), 2),
     (dict(ln_eps=-1.0), 9),
     (dict(ln_eps=float("nan")), 9),
@@ -109,6 +116,16 @@ def test_kernel_selection_names():
     assert ops.bwd_kernel_name(mlp_d64(output_key=True)) == "ttt_bwd_generic"
     assert ops.decode_kernel_name(mlp_d64(output_key=True)) == "ttt_decode_generic"
     assert ops.validate(mlp_d64(output_key=True)) == 0
+    # mini-batches above 16 tokens: forward on the paired kernel, decode on the streaming
+    # one, no backward
+    assert ops.fwd_kernel_name(mlp_d64(chunk=256)) == "ttt_fwd_mfma_pair_d64"
+    assert ops.decode_kernel_name(mlp_d64(chunk=256)) == "ttt_decode_stream_d64"
+    assert ops.bwd_kernel_name(mlp_d64(chunk=256)) == ""
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(mlp_d64(chunk=256), ops.TTT_OP_BWD)
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(mlp_d64(chunk=256), ops.TTT_OP_FWD_MOMENTUM)
+    assert ops.saved_size(mlp_d64(chunk=256)) == 8 * 12 * 32 * 2 * 64 * 256 * 4
 
 
 class _FakeTensor:
@@ -195,3 +212,4 @@ def test_momentum_fwd_checks_before_launch():
     assert call(c, ws_ptr=0) == 6
     assert call(mlp_d64(T=17)) == 2                 # TTT_ERR_SHAPE
     assert call(mlp_d64(output_key=True)) == 4      # TTT_ERR_UNSUPPORTED
+
