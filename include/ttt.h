@@ -139,6 +139,26 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
                         const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
                         void* saved, void* workspace, size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of ttt_scan_fwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, kernels and results are those of ttt_scan_fwd, except that the workspace is a
+ * device array inside the library: 16 MiB on each GPU the library runs on, held until the
+ * process ends. A configuration whose ttt_workspace_size(TTT_OP_FWD) exceeds 16 MiB returns
+ * TTT_ERR_WORKSPACE before anything is enqueued (the paired d = 64 kernel needs 108 KiB per
+ * (batch, head), so all of its up to 128 heads fit; the portable kernel needs the fp32
+ * weights of every head).
+ *  status_out (nullable, 4-byte aligned device pointer): receives the call's status word on
+ *  the stream after the scan: 0, or bit 0 = a kernel saw a NaN/Inf, bit 1 = a bounded wait
+ *  between cooperating workgroups expired (the meanings ttt_read_status reports).
+ * Every call on one GPU shares that GPU's array and the array keeps the last call's
+ * contents (each call clears what it needs cleared): calls that overlap on one GPU (other
+ * streams, other threads) race, so the caller orders them. No call allocates or frees
+ * device memory. */
+ttt_status ttt_scan_fwd_static(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                               const float* eta, const float* ln_gamma, const float* ln_beta,
+                               const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                               void* saved, unsigned* status_out, void* stream);
+
 /* Forward scan with momentum and a forget gate: the page "Test-Time Training(TTT)과 LLM
  * 메모리", section "Titans와 Miras", Eq. 14 (S_t = mom_t S_{t-1} - theta_t grad l(M_{t-1}; x_t))
  * and Eq. 13 (M_t = (1 - alpha_t) M_{t-1} + S_t), with the loss, f and output of

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ttt_internal.h"
 
@@ -134,6 +135,28 @@ size_t bwd_ws_bytes(const ttt_config* c) {
 
 ttt_status map_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// Workspace of ttt_scan_fwd_static: a file-scope device array, one per GPU, held until the
+// process ends. In host code its name is only a stand-in; the device address of each GPU's
+// copy comes from hipGetSymbolAddress, taken once per device (with that device current) on
+// the first call there, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,10 +233,11 @@ const char* ttt_decode_kernel_name(const ttt_config* cfg) {
   return use_decode_stream(cfg) ? "ttt_decode_stream_d64" : "ttt_decode_generic";
 }
 
-ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
-                        const float* eta, const float* ln_gamma, const float* ln_beta,
-                        const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
-                        void* saved, void* workspace, size_t ws_bytes, void* stream) {
+// Checks of ttt_scan_fwd's pointers (everything but the workspace), host only.
+static ttt_status fwd_check_args(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                                 const float* eta, const float* ln_gamma, const float* ln_beta,
+                                 const ttt_weights* W0, const void* Z, const ttt_weights* W_T,
+                                 const float* loss, const void* saved) {
   ttt_status st = check_common(cfg, true);
   if (st != TTT_OK) return st;
   const bool mlp = cfg->kind == TTT_MLP;
@@ -226,10 +250,15 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   if (mlp && !aligned16(W0->w2)) return TTT_ERR_ALIGN;
   if (W_T && (!aligned16(W_T->w1) || (mlp && !aligned16(W_T->w2)))) return TTT_ERR_ALIGN;
   if ((loss && !aligned16(loss)) || (saved && !aligned16(saved))) return TTT_ERR_ALIGN;
-  if (!workspace) return TTT_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
-  if (ws_bytes < fwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
+  return TTT_OK;
+}
 
+// Enqueues the forward on `workspace` (already checked to be large enough).
+static ttt_status fwd_launch(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                             const float* eta, const float* ln_gamma, const float* ln_beta,
+                             const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                             void* saved, void* workspace, hipStream_t s) {
+  const bool mlp = cfg->kind == TTT_MLP;
   ScanParams p = scan_params(cfg);
   p.Q = Q;
   p.K = K;
@@ -246,11 +275,42 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.saved = static_cast<float*>(saved);
   p.status = static_cast<unsigned*>(workspace);
   p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
   if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // only the paired kernel takes these
   if (use_split(cfg) && fwd_split_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_split(p, s));
   return map_hip(use_mfma(cfg) ? launch_fwd_mfma(p, s) : launch_fwd_generic(p, s));
+}
+
+ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const float* ln_gamma, const float* ln_beta,
+                        const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                        void* saved, void* workspace, size_t ws_bytes, void* stream) {
+  ttt_status st = fwd_check_args(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved);
+  if (st != TTT_OK) return st;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < fwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
+  return fwd_launch(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+ttt_status ttt_scan_fwd_static(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                               const float* eta, const float* ln_gamma, const float* ln_beta,
+                               const ttt_weights* W0, void* Z, const ttt_weights* W_T, float* loss,
+                               void* saved, unsigned* status_out, void* stream) {
+  ttt_status st = fwd_check_args(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved);
+  if (st != TTT_OK) return st;
+  if (status_out && (reinterpret_cast<uintptr_t>(status_out) & 3u) != 0) return TTT_ERR_ALIGN;
+  if (fwd_ws_bytes(cfg) > kStaticScratchBytes) return TTT_ERR_WORKSPACE;
+  unsigned* ws = static_cast<unsigned*>(static_scratch());
+  if (!ws) return TTT_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the array keeps the previous call's contents: the status word starts at zero here, and
+  // every kernel that uses the rest of the region clears or initialises what it reads
+  if (launch_reset_status(ws, s) != hipSuccess) return TTT_ERR_HIP;
+  st = fwd_launch(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved, ws, s);
+  if (st != TTT_OK || !status_out) return st;
+  return map_hip(launch_copy_status(ws, status_out, s));
 }
 
 ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const void* K, const void* V,

@@ -516,6 +516,10 @@ __global__ void reset_status_kernel(unsigned* status) {
   if (threadIdx.x == 0) *status = 0u;
 }
 
+__global__ void copy_status_kernel(const unsigned* src, unsigned* dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
 }  // namespace
 
 size_t fwd_generic_lds_bytes(int kind, int d, int hid, int chunk, bool momentum) {
@@ -549,6 +553,11 @@ hipError_t launch_fwd_generic(const ScanParams& p, hipStream_t stream) {
 
 hipError_t launch_reset_status(unsigned* status, hipStream_t stream) {
   hipLaunchKernelGGL(reset_status_kernel, dim3(1), dim3(64), 0, stream, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_status(const unsigned* src, unsigned* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream, src, dst);
   return hipGetLastError();
 }
 

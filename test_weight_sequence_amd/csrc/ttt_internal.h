@@ -135,5 +135,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 bool decode_stream_supported(const DecodeParams& p);
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
 hipError_t launch_reset_status(unsigned* status, hipStream_t s);
+// dst[0] = src[0] on the stream (the status word of a workspace the caller cannot address)
+hipError_t launch_copy_status(const unsigned* src, unsigned* dst, hipStream_t s);
 
 }  // namespace ttt

@@ -30,7 +30,8 @@ STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE"
           7: "TTT_ERR_HIP", 8: "TTT_ERR_NONFINITE", 9: "TTT_ERR_ARG",
           10: "TTT_ERR_TIMEOUT"}
 
-EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd", "ttt_scan_fwd_momentum",
+EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd", "ttt_scan_fwd_static",
+           "ttt_scan_fwd_momentum",
            "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
            "ttt_fwd_kernel_name", "ttt_bwd_kernel_name", "ttt_decode_kernel_name", "ttt_status_str",
            "ttt_abi_version")
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_workspace_size.argtypes = [cfgp, I32, ctypes.POINTER(S)]
         L.ttt_saved_size.argtypes = [cfgp, ctypes.POINTER(S)]
         L.ttt_scan_fwd.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, S, P]
+        L.ttt_scan_fwd_static.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, P]
         L.ttt_scan_fwd_momentum.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, wp, P, wp, wp, P, P, S, P]
         L.ttt_scan_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, P, P, P, P, wp, P, P, P, S, P]
         L.ttt_decode_step.argtypes = [cfgp, P, P, P, P, P, P, wp, wp, I32, P, P, S, P]
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.ttt_status_str.argtypes = [I32]
         L.ttt_status_str.restype = ctypes.c_char_p
         for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
-                     "ttt_scan_fwd_momentum",
+                     "ttt_scan_fwd_static", "ttt_scan_fwd_momentum",
                      "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
                      "ttt_abi_version"):
             getattr(L, name).restype = I32
@@ -219,6 +221,30 @@ def scan_fwd(cfg: Config, Q, K, V, eta, W0, gamma, beta, *, want_wt=True, want_l
     _check(code, "ttt_scan_fwd")
     return {"Z": Z, "W_T": tuple(WT) if WT else None, "loss": loss, "saved": saved,
             "workspace": ws}
+
+
+def scan_fwd_static(cfg: Config, Q, K, V, eta, W0, gamma, beta, *, want_wt=True,
+                    want_loss=False, want_saved=False, want_status=True, out=None,
+                    stream=None) -> dict:
+    """ttt_scan_fwd_static: the forward scan with the library's own device workspace (no
+    workspace argument). Outputs are allocated here as for scan_fwd; the call itself
+    allocates nothing. "status" is a one-element int32 device tensor holding the call's
+    status word (0 = clean)."""
+    dev = Q.device
+    lead = (cfg.B, cfg.H)
+    Z = out if out is not None else torch.empty(*lead, cfg.T, cfg.d, dtype=cfg.io_dtype, device=dev)
+    WT = [torch.empty(s, dtype=torch.float32, device=dev) for s in cfg.weight_shapes(lead)] \
+        if want_wt else None
+    loss = torch.empty(*lead, cfg.T, dtype=torch.float32, device=dev) if want_loss else None
+    saved = torch.empty(saved_size(cfg) // 4, dtype=torch.float32, device=dev) \
+        if want_saved else None
+    status = torch.full((1,), -1, dtype=torch.int32, device=dev) if want_status else None
+    code = lib().ttt_scan_fwd_static(ctypes.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta),
+                                     _ptr(gamma), _ptr(beta), _weights(W0), _ptr(Z), _weights(WT),
+                                     _ptr(loss), _ptr(saved), _ptr(status), _stream(stream))
+    _check(code, "ttt_scan_fwd_static")
+    return {"Z": Z, "W_T": tuple(WT) if WT else None, "loss": loss, "saved": saved,
+            "status": status}
 
 
 def scan_fwd_momentum(cfg: Config, Q, K, V, theta, mom, alpha, W0, gamma, beta, S0=None, *,

@@ -213,3 +213,26 @@ def test_momentum_fwd_checks_before_launch():
     assert call(mlp_d64(T=17)) == 2                 # TTT_ERR_SHAPE
     assert call(mlp_d64(output_key=True)) == 4      # TTT_ERR_UNSUPPORTED
 
+
+def test_static_fwd_checks_before_launch():
+    """ttt_scan_fwd_static: null, alignment and shape errors, and a configuration whose
+    workspace exceeds the library's 16 MiB device array, are reported on the host before any
+    HIP call (fake device addresses, no GPU)."""
+    L = ops.lib()
+    P = ctypes.c_void_p
+    w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
+
+    def call(cfg, first=0x1000, status=None):
+        args = [P(first)] + [P(0x1000 * (i + 2)) for i in range(5)]  # Q K V eta gamma beta
+        return L.ttt_scan_fwd_static(ctypes.byref(cfg.c()), *args, w, P(0x80000), None, None, None,
+                                     P(status) if status else None, None)
+    assert call(mlp_d64(), first=0) == 1                  # TTT_ERR_NULL
+    assert call(mlp_d64(), first=0x1008) == 5             # TTT_ERR_ALIGN
+    assert call(mlp_d64(), status=0x90002) == 5           # status word not 4-byte aligned
+    assert call(mlp_d64(T=17)) == 2                       # TTT_ERR_SHAPE
+    # 32 heads of the d=128 shape: the portable fallback's per-head weights alone are 16 MiB
+    big = ops.Config(kind="mlp", B=1, H=32, T=64, d=128, hidden=512, chunk=16, io="bf16")
+    assert ops.workspace_size(big) > 16 << 20
+    assert call(big) == 6                                 # TTT_ERR_WORKSPACE
+    # the paired kernel's largest launch (128 heads) fits
+    assert ops.workspace_size(mlp_d64(B=8, H=16)) <= 16 << 20
