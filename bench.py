@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "ttt_fwd_mfma_split_d128": ("ttt_fwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
                                 "ttt_gelu.hpp"),
     "ttt_bwd_mfma_d64": ("ttt_bwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_fwd_mfma_mom_d64": ("ttt_fwd_mfma_mom.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
 }
 
 
@@ -218,13 +219,15 @@ def bench_scan_fwd(args, wid: str) -> dict:
 
 
 def bench_scan_fwd_momentum(args) -> dict:
-    """One step = one ttt_scan_fwd_momentum over the whole batch (the portable fp32 kernel),
-    d=64 T=8192 head shape at B=8, H=12, gates mom = 0.9 sigmoid(u), alpha = 0.01 sigmoid(u')."""
+    """One step = one ttt_scan_fwd_momentum over the whole batch (the tuned kernel; the portable
+    fp32 one with --force-generic), d=64 T=8192 head shape at B=8, H=12, gates
+    mom = 0.9 sigmoid(u), alpha = 0.01 sigmoid(u')."""
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS, momentum_gates
     w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
-    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk, io=w.io)
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk, io=w.io,
+                     force_generic=args.force_generic)
     dev = torch.device("cuda:0")
     d = _device_inputs(w, dev)
     gates = {k: v.to(dev) for k, v in momentum_gates(w).items()}
@@ -243,11 +246,15 @@ def bench_scan_fwd_momentum(args) -> dict:
     # the plain scan's products, plus Q S1 and A^Q S2 and the momentum's own update
     flop = units * (flops_per_token_head(w.d, w.hidden, w.chunk) + 8 * w.d * w.hidden)
     achieved = flop / (k_avg * 1e-3) / 1e12
+    kernel = ops.fwd_momentum_kernel_name(cfg)
+    mfma = kernel != "ttt_fwd_generic"
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
     out = _base_record(args, f"TTT-MLP momentum/forget-gate scan token*heads/s at d={w.d}, T={w.T}",
-                       units / (ms_step * 1e-3), ms_step, w, "ttt_fwd_generic (momentum)", "f32")
+                       units / (ms_step * 1e-3), ms_step, w, kernel, "bf16" if mfma else "f32")
     out["roofline"] = {
-        "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-        "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None, "kernel_ms": k_avg,
+        "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+        "frac": achieved / peak, "traffic": _traffic(kernel, units) if kernel in KERNEL_SOURCES else None,
+        "kernel_ms": k_avg,
         "kernel_ms_min": min(kms), "flop_per_launch": flop,
         "algorithmic_bytes_per_launch": units * (bytes_per_token_head(w.d, 2, 2 * w.d * w.hidden, w.T) + 8)}
     return out
@@ -397,7 +404,7 @@ def main():
                     help="instead of the scan, time a plain device-to-device copy of MIB MiB "
                          "(the known-size reference for scaling the HBM byte counters)")
     args = ap.parse_args()
-    long_run = args.workload in ("scan_fwd_d128", "scan_fwd_momentum")
+    long_run = args.workload == "scan_fwd_d128" or (args.workload == "scan_fwd_momentum" and args.force_generic)
     if args.steps is None:
         args.steps = 2 if long_run else 20
     if args.warmup is None:

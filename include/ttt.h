@@ -170,10 +170,13 @@ ttt_status ttt_scan_fwd_static(const ttt_config* cfg, const void* Q, const void*
  *  W0: initial memory, shaped as for ttt_scan_fwd. S0 (nullable = zero): momentum carried
  *  in, always per sequence [B,H,...]. W_T, S_T (nullable): final memory and momentum,
  *  [B,H,...] (written). Z, loss: as for ttt_scan_fwd.
- *  Runs the portable fp32 kernel for every supported shape and io dtype. TTT_OUTPUT_KEY is
- *  rejected (TTT_ERR_UNSUPPORTED); there is no saved state and no backward for this
- *  variant. Workspace: ttt_workspace_size(.., TTT_OP_FWD_MOMENTUM, ..) bytes (the fp32
- *  memory and momentum of every head). Errors as for ttt_scan_fwd. */
+ *  Kernels: for MLP, d = 64, hidden = 256, chunk 16, bf16 I/O a tuned bf16 MFMA kernel that
+ *  splits each head over two workgroups (the memory and the momentum in registers, bounded
+ *  waits between the two as in the split d = 128 forward, TTT_ERR_TIMEOUT on expiry);
+ *  every other supported shape (and TTT_FORCE_GENERIC) runs the portable fp32 kernel.
+ *  TTT_OUTPUT_KEY is rejected (TTT_ERR_UNSUPPORTED); there is no saved state and no
+ *  backward for this variant. Workspace: ttt_workspace_size(.., TTT_OP_FWD_MOMENTUM, ..)
+ *  bytes. Errors as for ttt_scan_fwd. */
 ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const void* K, const void* V,
                                  const float* theta, const float* mom, const float* alpha,
                                  const float* ln_gamma, const float* ln_beta, const ttt_weights* W0,
@@ -227,6 +230,11 @@ ttt_status ttt_reset_status(void* workspace, void* stream);
  * workgroups the device holds at once (64 heads on a 256-CU device), and launches
  * "ttt_fwd_generic" instead only if not even eight heads fit. */
 const char* ttt_fwd_kernel_name(const ttt_config* cfg);
+
+/* Name of the kernel variant ttt_scan_fwd_momentum would launch for cfg ("" if invalid):
+ * "ttt_fwd_mfma_mom_d64" for the tuned shape (the portable kernel runs instead if the device
+ * cannot hold a group of eight heads' workgroups at once), else "ttt_fwd_generic". Host only. */
+const char* ttt_fwd_momentum_kernel_name(const ttt_config* cfg);
 
 /* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */
 const char* ttt_bwd_kernel_name(const ttt_config* cfg);

@@ -182,8 +182,16 @@ const char* ttt_status_str(ttt_status s) {
 
 ttt_status ttt_validate(const ttt_config* cfg) { return check_common(cfg, true); }
 
+bool use_mom(const ttt_config* c) {
+  if (!tuned_allowed(c)) return false;
+  ScanParams p = scan_params(c);
+  return fwd_mom_supported(p);
+}
+
 size_t fwd_momentum_ws_bytes(const ttt_config* c) {
-  return kStatusBytes + static_cast<size_t>(c->B) * c->H * 2 * weights_per_head(c) * sizeof(float);
+  const size_t generic = static_cast<size_t>(c->B) * c->H * 2 * weights_per_head(c) * sizeof(float);
+  // the tuned kernel falls back to the portable one when its grid does not fit the device
+  return kStatusBytes + (use_mom(c) ? std::max(generic, fwd_mom_workspace_bytes(c->B * c->H)) : generic);
 }
 
 ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) {
@@ -221,6 +229,12 @@ const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
   if (use_pair(cfg)) return "ttt_fwd_mfma_pair_d64";
   if (use_split(cfg)) return "ttt_fwd_mfma_split_d128";
   return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
+}
+
+const char* ttt_fwd_momentum_kernel_name(const ttt_config* cfg) {
+  if (check_common(cfg, true) != TTT_OK || (cfg->flags & TTT_OUTPUT_KEY)) return "";
+  if (fwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk, true) > kMaxLds) return "";
+  return use_mom(cfg) ? "ttt_fwd_mfma_mom_d64" : "ttt_fwd_generic";
 }
 
 const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
@@ -363,7 +377,9 @@ ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const voi
   p.s0_2 = (S0 && mlp) ? S0->w2 : nullptr;
   p.st_1 = S_T ? S_T->w1 : nullptr;
   p.st_2 = (S_T && mlp) ? S_T->w2 : nullptr;
-  return map_hip(launch_fwd_generic(p, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_mom(cfg) && fwd_mom_fits()) return map_hip(launch_fwd_mfma_mom(p, s));
+  return map_hip(launch_fwd_generic(p, s));
 }
 
 ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,

@@ -115,6 +115,13 @@ size_t fwd_split_workspace_bytes(int nheads);
 int fwd_split_blocks(int nheads);
 bool fwd_split_fits(int nheads);
 hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t s);
+// Momentum / forget-gate forward for the d = 64, hidden = 256 bf16 head: each head split by
+// hidden units over two workgroups that hold the memory and the momentum in registers and
+// exchange [chunk x d] partial sums through the workspace.
+bool fwd_mom_supported(const ScanParams& p);
+size_t fwd_mom_workspace_bytes(int nheads);
+bool fwd_mom_fits();
+hipError_t launch_fwd_mfma_mom(const ScanParams& p, hipStream_t s);
 // Per-head backward workspace (floats): the carried dW, then kBwdArrays [chunk x hidden]
 // intermediates (MLP only).
 constexpr int kBwdArrays = 12;

@@ -33,7 +33,8 @@ STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE"
 EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd", "ttt_scan_fwd_static",
            "ttt_scan_fwd_momentum",
            "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
-           "ttt_fwd_kernel_name", "ttt_bwd_kernel_name", "ttt_decode_kernel_name", "ttt_status_str",
+           "ttt_fwd_kernel_name", "ttt_fwd_momentum_kernel_name", "ttt_bwd_kernel_name",
+           "ttt_decode_kernel_name", "ttt_status_str",
            "ttt_abi_version")
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_reset_status.argtypes = [P, P]
         L.ttt_fwd_kernel_name.argtypes = [cfgp]
         L.ttt_fwd_kernel_name.restype = ctypes.c_char_p
+        L.ttt_fwd_momentum_kernel_name.argtypes = [cfgp]
+        L.ttt_fwd_momentum_kernel_name.restype = ctypes.c_char_p
         L.ttt_bwd_kernel_name.argtypes = [cfgp]
         L.ttt_bwd_kernel_name.restype = ctypes.c_char_p
         L.ttt_decode_kernel_name.argtypes = [cfgp]
@@ -178,6 +181,10 @@ def saved_size(cfg: Config) -> int:
 
 def fwd_kernel_name(cfg: Config) -> str:
     return lib().ttt_fwd_kernel_name(ctypes.byref(cfg.c())).decode()
+
+
+def fwd_momentum_kernel_name(cfg: Config) -> str:
+    return lib().ttt_fwd_momentum_kernel_name(ctypes.byref(cfg.c())).decode()
 
 
 def bwd_kernel_name(cfg: Config) -> str:

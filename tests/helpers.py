@@ -84,7 +84,8 @@ def _rel_rows(err: torch.Tensor, ref: torch.Tensor) -> torch.Tensor:
 
 
 def assert_parity(gpu: torch.Tensor, ref: torch.Tensor, tol: float, what: str = "",
-                  time_axis: bool = True, per_token: bool = True, perturbed=None):
+                  time_axis: bool = True, per_token: bool = True, perturbed=None,
+                  whole_from_perturbed: bool = False):
     """gpu vs oracle for a tensor whose leading axis indexes (batch, head) pairs.
 
     Checks the relative L2 over the whole tensor and over each head (<= tol); with a token
@@ -95,14 +96,19 @@ def assert_parity(gpu: torch.Tensor, ref: torch.Tensor, tol: float, what: str = 
     scale (oracle_perturbed). Where the recurrence itself amplifies rounding at a chunk or a
     token (drifting d = 128 inputs make a few tokens 20-30x more sensitive than the average),
     that head's, chunk's or token's bound is raised to twice the largest oracle-to-oracle
-    change there; the whole-tensor bound stays at tol. Returns the whole-tensor error."""
+    change there; the whole-tensor bound stays at tol unless whole_from_perturbed, which raises
+    it the same way (for a state that the recurrence itself makes chaotic over a long scan).
+    Returns the whole-tensor error."""
     a = gpu.detach().to("cpu", torch.float64)
     b = ref.detach().to("cpu", torch.float64).reshape(a.shape)
     N = a.shape[0]
     pert = [p.detach().to("cpu", torch.float64).reshape(a.shape) - b for p in (perturbed or [])]
     e = a - b
     whole = (e.norm() / b.norm()).item()
-    assert whole <= tol, (what, "whole", whole, tol)
+    wlim = tol
+    if whole_from_perturbed:
+        wlim = max([tol] + [2.0 * (pe.norm() / b.norm()).item() for pe in pert])
+    assert whole <= wlim, (what, "whole", whole, wlim)
     heads = _rel_rows(e.reshape(N, -1), b.reshape(N, -1))
     hlim = torch.full_like(heads, tol)
     for pe in pert:

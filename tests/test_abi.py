@@ -116,6 +116,13 @@ def test_kernel_selection_names():
     assert ops.bwd_kernel_name(mlp_d64(output_key=True)) == "ttt_bwd_generic"
     assert ops.decode_kernel_name(mlp_d64(output_key=True)) == "ttt_decode_generic"
     assert ops.validate(mlp_d64(output_key=True)) == 0
+    # the momentum variant: the tuned kernel for the d=64 bf16 shape, the portable one otherwise
+    assert ops.fwd_momentum_kernel_name(mlp_d64()) == "ttt_fwd_mfma_mom_d64"
+    assert ops.fwd_momentum_kernel_name(mlp_d64(force_generic=True)) == "ttt_fwd_generic"
+    assert ops.fwd_momentum_kernel_name(mlp_d64(io="f32")) == "ttt_fwd_generic"
+    assert ops.fwd_momentum_kernel_name(mlp_d64(d=128, hidden=512)) == "ttt_fwd_generic"
+    assert ops.fwd_momentum_kernel_name(mlp_d64(output_key=True)) == ""
+    assert ops.fwd_momentum_kernel_name(mlp_d64(chunk=256)) == ""
     # mini-batches above 16 tokens: forward on the paired kernel, decode on the streaming
     # one, no backward
     assert ops.fwd_kernel_name(mlp_d64(chunk=256)) == "ttt_fwd_mfma_pair_d64"
@@ -199,7 +206,7 @@ def test_momentum_fwd_checks_before_launch():
     P = ctypes.c_void_p
     c = mlp_d64()
     need = ops.workspace_size(c, ops.TTT_OP_FWD_MOMENTUM)
-    assert need == 256 + c.B * c.H * 2 * 2 * c.d * c.hidden * 4
+    assert need >= 256 + c.B * c.H * 2 * 2 * c.d * c.hidden * 4
     w = ctypes.byref(ops.CWeights(0x10000, 0x20000))
 
     def call(cfg, first=0x1000, ws=need, ws_ptr=0x90000):
