@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
     "ttt_decode_stream_d64": ("ttt_decode_stream.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_decode_split_d64": ("ttt_decode_split.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_mfma_split_d128": ("ttt_fwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
                                 "ttt_gelu.hpp"),
     "ttt_bwd_mfma_d64": ("ttt_bwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
@@ -256,7 +257,9 @@ def bench_scan_fwd_momentum(args) -> dict:
         "frac": achieved / peak, "traffic": _traffic(kernel, units) if kernel in KERNEL_SOURCES else None,
         "kernel_ms": k_avg,
         "kernel_ms_min": min(kms), "flop_per_launch": flop,
-        "algorithmic_bytes_per_launch": units * (bytes_per_token_head(w.d, 2, 2 * w.d * w.hidden, w.T) + 8)}
+        # the plain scan's streams and W0 / W_T, the two gates (fp32) and the final momentum S_T
+        "algorithmic_bytes_per_launch": units * (bytes_per_token_head(w.d, 2, 2 * w.d * w.hidden, w.T) + 8)
+                                        + w.B * w.H * 2 * w.d * w.hidden * 4}
     return out
 
 
@@ -316,14 +319,20 @@ def bench_scan_bwd(args) -> dict:
 
 def bench_decode(args) -> dict:
     """One step = one full chunk of decode calls (16 tokens for every (batch, head) of the
-    d = 64 bf16 MLP shape), so every step includes one commit."""
+    d = 64 bf16 MLP shape), so every step includes one commit. The chunk's 16 calls are
+    captured once into a HIP graph (through torch.cuda.graph) and the graph is replayed, as a
+    serving loop would run them: a call through the Python binding costs more host time than
+    the kernel takes on the GPU. The eager per-call wall time is reported beside it."""
     import ctypes
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS
     w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    if args.decode_batch:
+        w = w.with_(B=args.decode_batch)
     b = w.chunk
-    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=b, d=w.d, hidden=w.hidden, chunk=b, io=w.io)
+    cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=b, d=w.d, hidden=w.hidden, chunk=b, io=w.io,
+                     force_generic=args.force_generic, decode_split=args.decode_split)
     dev = torch.device("cuda:0")
     d = _device_inputs(w.with_(T=b), dev)
     Ws = tuple(x.unsqueeze(0).expand(w.B, *x.shape).contiguous() for x in d["W0"])
@@ -341,14 +350,29 @@ def bench_decode(args) -> dict:
     per_tok = [[P(qkv[0][t].data_ptr()), P(qkv[1][t].data_ptr()), P(qkv[2][t].data_ptr()),
                 P(eta[t].data_ptr())] for t in range(b)]
     zp, ws_ptr = P(z.data_ptr()), P(ws.data_ptr())
-    stream = P(torch.cuda.current_stream().cuda_stream)
     dec = ops.lib().ttt_decode_step
 
-    def call(t):
+    def call(t, stream):
         q, k, v, e = per_tok[t]
         return dec(cfg_c, q, k, v, e, gam, bet, wsw, wacc, t, zp, ws_ptr, ws.numel(), stream)
 
-    ms_step, kms = _time_calls(call, args.steps, args.warmup, calls_per_step=b)
+    eager_stream = P(torch.cuda.current_stream().cuda_stream)
+    eager_ms_step, _ = _time_calls(lambda t: call(t, eager_stream), max(2, args.steps // 4), 1,
+                                   calls_per_step=b)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        cap = P(torch.cuda.current_stream().cuda_stream)
+        for t in range(b):
+            rc = call(t, cap)
+            if rc != 0:
+                raise ops.TTTError(rc, "ttt_decode_step (capture)")
+
+    def replay(i):
+        graph.replay()
+        return 0
+
+    ms_step, kms = _time_calls(replay, args.steps, args.warmup)
     if ops.read_status(ws) != 0:
         raise RuntimeError("kernel reported non-finite values")
     heads = w.B * w.H
@@ -356,18 +380,20 @@ def bench_decode(args) -> dict:
     # per head: every call reads W_start and acc; b - 1 calls write acc, the commit writes
     # W_start and clears acc
     bytes_step = heads * nW * (2 * b + (b - 1) + 2)
-    k_sum_step = sum(kms) / args.steps
+    k_sum_step = statistics.fmean(kms)
     achieved = bytes_step / (k_sum_step * 1e-3) / 1e9
+    kernel = ops.decode_kernel_name(cfg)
     out = _base_record(args, f"TTT-MLP decode token*heads/s at d={w.d} ({heads} heads, one token "
                              "per head per call)", heads * b / (ms_step * 1e-3), ms_step,
-                       w.with_(T=b), ops.decode_kernel_name(cfg), "f32")
-    kernel = ops.decode_kernel_name(cfg)
+                       w.with_(T=b), kernel, "f32", extra_cfg={"launch": f"HIP graph of {b} calls"})
     out["roofline"] = {
         "bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
         "frac": achieved / 8000.0,
         "traffic": _traffic(kernel, heads) if kernel in KERNEL_SOURCES else None,
-        "kernel_ms": statistics.fmean(kms), "kernel_ms_min": min(kms),
+        # GPU time of one replayed chunk (16 kernels back to back) / 16
+        "kernel_ms": k_sum_step / b, "kernel_ms_min": min(kms) / b,
         "algorithmic_bytes_per_launch": bytes_step / b}
+    out["eager_ms_per_call"] = eager_ms_step / b
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, w.B, 4096)
     return out
@@ -394,6 +420,10 @@ def main():
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
     ap.add_argument("--chunk", type=int, default=256, choices=[256, 1024],
                     help="mini-batch size of the scan_fwd_bigchunk workload")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
+                    help="decode workload only: B sequences of 12 heads instead of 8")
+    ap.add_argument("--decode-split", action="store_true",
+                    help="decode workload only: four workgroups per head (TTT_DECODE_SPLIT)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-T", type=int, default=8192)

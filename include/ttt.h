@@ -84,10 +84,15 @@ enum {
                              (the chunk start; W_{t-1} when chunk = 1), i.e. the key-side
                              prediction reused as the output. Q does not enter it (dQ = 0). Runs on
                              the portable kernels. */
-  TTT_FORCE_DEVICE_SCOPE = 1 << 4 /* tuned forward: the workgroups of a head hand partial results
+  TTT_FORCE_DEVICE_SCOPE = 1 << 4 /* tuned kernels with several workgroups per head (forward,
+                                     momentum forward, decode): they hand partial results
                                      to each other with device-scope atomics and fences even
                                      when they share an XCD (slower). This is the path taken when
-                                     they do not; the flag lets a test run it. */
+                                     they do not; the flag lets a test run it. */,
+  TTT_DECODE_SPLIT = 1 << 5 /* decode, MLP d = 64: four workgroups per (batch, head), split by
+                               hidden units, instead of one (at most 128 heads). Measured slower
+                               than one workgroup per head at every head count tried (12-120);
+                               kept as the alternative the library can run and test. */
 };
 /* op codes for ttt_workspace_size */
 enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2, TTT_OP_FWD_MOMENTUM = 3 };
@@ -101,7 +106,7 @@ typedef struct {
   int32_t io_dtype;  /* TTT_F32 or TTT_BF16 for Q, K, V, Z, dQ, dK, dV, dZ             */
   int32_t gelu;      /* TTT_GELU_ERF (exact) or TTT_GELU_TANH                          */
   int32_t flags;     /* TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD |
-                        TTT_OUTPUT_KEY | TTT_FORCE_DEVICE_SCOPE                       */
+                        TTT_OUTPUT_KEY | TTT_FORCE_DEVICE_SCOPE | TTT_DECODE_SPLIT    */
   float ln_eps;      /* LayerNorm epsilon inside the square root (e.g. 1e-6)           */
   float eta_scale;   /* multiplies every eta_t (1 = plain sum; 1/b = averaged sum)     */
 } ttt_config;
@@ -205,7 +210,11 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
  *  pos_in_chunk: 0..chunk-1, tracked by the caller. At pos_in_chunk == chunk-1 the
  *          step commits: W_start -= acc and acc = 0.
  *  z [B,H,d] io dtype (written) = f(q; W_start - acc), acc including this token.
- *  A scan of T tokens followed by decode steps equals a scan of the longer sequence. */
+ *  A scan of T tokens followed by decode steps equals a scan of the longer sequence.
+ *  workspace: ttt_workspace_size(.., TTT_OP_DECODE, ..) bytes, zero-filled before its first
+ *          use. For the four-workgroup kernel (TTT_DECODE_SPLIT) it holds, after the status
+ *          word, an exchange area per head that every call leaves zero; after TTT_ERR_TIMEOUT
+ *          zero-fill it again. Calls that overlap on one workspace race. */
 ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, const void* v,
                            const float* eta, const float* ln_gamma, const float* ln_beta,
                            const ttt_weights* W_start, const ttt_weights* acc,
@@ -239,7 +248,10 @@ const char* ttt_fwd_momentum_kernel_name(const ttt_config* cfg);
 /* Name of the kernel variant ttt_scan_bwd would launch for cfg ("" if invalid). Host only. */
 const char* ttt_bwd_kernel_name(const ttt_config* cfg);
 
-/* Name of the kernel variant ttt_decode_step would launch for cfg ("" if invalid). Host only. */
+/* Name of the kernel variant ttt_decode_step would launch for cfg ("" if invalid). Host
+ * only: for MLP d = 64, hidden = 256 "ttt_decode_stream_d64" (one workgroup per head), or
+ * "ttt_decode_split_d64" (four workgroups per head) with TTT_DECODE_SPLIT when B*H <= 128;
+ * "ttt_decode_generic" for every other shape or with TTT_FORCE_GENERIC. */
 const char* ttt_decode_kernel_name(const ttt_config* cfg);
 
 const char* ttt_status_str(ttt_status s);

@@ -35,7 +35,7 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
   if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
   if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH) return TTT_ERR_UNSUPPORTED;
   if (c->flags & ~(TTT_W0_PER_SEQ | TTT_FORCE_GENERIC | TTT_ONE_WG_PER_HEAD | TTT_OUTPUT_KEY |
-                   TTT_FORCE_DEVICE_SCOPE))
+                   TTT_FORCE_DEVICE_SCOPE | TTT_DECODE_SPLIT))
     return TTT_ERR_ARG;
   if (c->B < 1 || c->H < 1 || c->d < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
   if (need_T && c->T < 1) return TTT_ERR_SHAPE;
@@ -126,6 +126,16 @@ bool use_decode_stream(const ttt_config* c) {
   return decode_stream_supported(p);
 }
 
+// Four workgroups per head for the decode of the tuned shape, on request.
+bool use_decode_split(const ttt_config* c) {
+  return use_decode_stream(c) && (c->flags & TTT_DECODE_SPLIT) &&
+         static_cast<long>(c->B) * c->H <= kDecodeSplitMaxHeads;
+}
+
+size_t decode_ws_bytes(const ttt_config* c) {
+  return kStatusBytes + (use_decode_split(c) ? decode_split_workspace_bytes(c->B * c->H) : 0);
+}
+
 size_t bwd_ws_bytes(const ttt_config* c) {
   const size_t heads = static_cast<size_t>(c->B) * c->H;
   return kStatusBytes +
@@ -205,7 +215,7 @@ ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) 
       if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // no backward for these
       *bytes = bwd_ws_bytes(cfg);
       return TTT_OK;
-    case TTT_OP_DECODE: *bytes = kStatusBytes; return TTT_OK;
+    case TTT_OP_DECODE: *bytes = decode_ws_bytes(cfg); return TTT_OK;
     case TTT_OP_FWD_MOMENTUM:
       if (fwd_generic_lds_bytes(cfg->kind, cfg->d, hidden_of(cfg), cfg->chunk, true) > kMaxLds)
         return TTT_ERR_UNSUPPORTED;
@@ -244,6 +254,7 @@ const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
 
 const char* ttt_decode_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, false) != TTT_OK) return "";
+  if (use_decode_split(cfg)) return "ttt_decode_split_d64";
   return use_decode_stream(cfg) ? "ttt_decode_stream_d64" : "ttt_decode_generic";
 }
 
@@ -470,7 +481,7 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
   if (mlp && (!aligned16(W_start->w2) || !aligned16(acc->w2))) return TTT_ERR_ALIGN;
   if (!workspace) return TTT_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TTT_ERR_ALIGN;
-  if (ws_bytes < kStatusBytes) return TTT_ERR_WORKSPACE;
+  if (ws_bytes < decode_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
   DecodeParams p{};
   p.kind = cfg->kind;
   p.B = cfg->B;
@@ -497,6 +508,8 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
   p.z = z;
   p.status = static_cast<unsigned*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_decode_split(cfg))
+    return map_hip(launch_decode_split(p, static_cast<char*>(workspace) + kStatusBytes, s));
   return map_hip(use_decode_stream(cfg) ? launch_decode_stream(p, s) : launch_decode(p, s));
 }
 

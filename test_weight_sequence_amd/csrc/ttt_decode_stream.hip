@@ -15,6 +15,9 @@
 //   HK = k W1, AK = GELU, G = GELU';  ZK = AK W2;  E2 = eta' LN-backward(ZK)   (at W_start)
 //   E1 = (E2 W2^T) (.) G;  acc1 += k^T E1;  acc2 += AK^T E2
 //   HQ = q (W1 - acc1), AQ = GELU;  ZQ = AQ (W2 - acc2);  z = q + LN(ZQ)
+// HQ is formed as q (W1 - acc1_before) - (q . k) E1, so its reduction over d runs before E1 is
+// known, while wave 0 takes the LayerNorm of ZK; acc2 and acc1 are stored as soon as they are
+// final.
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -36,10 +39,11 @@ __device__ __forceinline__ void act_dv(float x, float& v, float& d1) {
 template <typename IO, int GELU_KIND>
 __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
   __shared__ float sq[D], sk[D], sv[D], sE2[D];
-  __shared__ float sA[HID], sG[HID], sE1[HID], sAQ[HID];
-  __shared__ float4 red1[NWV][HID / 4];  // [row block][h]: k W1 / q (W1 - acc1) partials
+  __shared__ float sA[HID], sG[HID], sE1[HID], sPQ[HID], sAQ[HID];
+  __shared__ float4 red1[NWV][HID / 4];  // [row block][h]: k W1 partials
+  __shared__ float4 redq[NWV][HID / 4];  // [row block][h]: q (W1 - acc1) partials (acc1 before this token)
   __shared__ float4 red2[NWV][D / 4];    // [wave][d]: A W2 partials
-  __shared__ float sEta;
+  __shared__ float sEta, sQK;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x, hidx = bh % p.H;
   const bool commit = p.pos == p.chunk - 1;
@@ -51,16 +55,17 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
   float* W2 = p.ws_2 + static_cast<size_t>(bh) * HID * D;
   float* A2 = p.acc_2 + static_cast<size_t>(bh) * HID * D;
   const int cg = tid & 15, rb = tid >> 4;
+  // loads in the order of first use (W1, W2, acc1, acc2), so that the first products start
+  // while the rest of the head's 256 KiB is still arriving
   float4 w1[4], a1[4], w2[4], a2[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t o1 = static_cast<size_t>(4 * wv + i) * HID + 4 * lane;
-    const size_t o2 = static_cast<size_t>(4 * rb + i) * D + 4 * cg;
-    w1[i] = *reinterpret_cast<const float4*>(W1 + o1);
-    w2[i] = *reinterpret_cast<const float4*>(W2 + o2);
-    a1[i] = *reinterpret_cast<const float4*>(A1 + o1);
-    a2[i] = *reinterpret_cast<const float4*>(A2 + o2);
-  }
+  for (int i = 0; i < 4; ++i) w1[i] = *reinterpret_cast<const float4*>(W1 + (4 * wv + i) * HID + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w2[i] = *reinterpret_cast<const float4*>(W2 + (4 * rb + i) * D + 4 * cg);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a1[i] = *reinterpret_cast<const float4*>(A1 + (4 * wv + i) * HID + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a2[i] = *reinterpret_cast<const float4*>(A2 + (4 * rb + i) * D + 4 * cg);
   if (tid < D) {
     const size_t o = static_cast<size_t>(bh) * D + tid;
     sq[tid] = to_f32(static_cast<const IO*>(p.q)[o]);
@@ -93,6 +98,9 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
     act_dv<GELU_KIND>(s, v, d1);
     sA[tid] = v;
     sG[tid] = d1;
+  } else if (wv == HID / 64) {
+    const float qk = wave_sum(sq[lane] * sk[lane]);
+    if (lane == 0) sQK = qk;
   }
   __syncthreads();
 
@@ -119,10 +127,24 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
     }
     if (lane < 16) red2[wv][cg] = z;
   };
-  // ---- Z^K = A^K W2 ----
+  // ---- Z^K = A^K W2; the part of H^Q that does not depend on this token's gradient:
+  //      q (W1 - acc1), acc1 before this token (H^Q = that - (q . k) E1) ----
   w2_partial(sA, w2, nullptr);
+  {
+    float4 h = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = sq[4 * wv + i];
+      h.x = fmaf(x, w1[i].x - a1[i].x, h.x);
+      h.y = fmaf(x, w1[i].y - a1[i].y, h.y);
+      h.z = fmaf(x, w1[i].z - a1[i].z, h.z);
+      h.w = fmaf(x, w1[i].w - a1[i].w, h.w);
+    }
+    redq[wv][lane] = h;
+  }
   __syncthreads();
-  // ---- LayerNorm forward/backward (wave 0, one d per lane): E2 = eta' delta2 ----
+  // ---- LayerNorm forward/backward (wave 0, one d per lane): E2 = eta' delta2; meanwhile
+  //      waves 4-7 sum the q (W1 - acc1) partials ----
   if (wv == 0) {
     const float* r = reinterpret_cast<const float*>(red2);
     float z = 0.f;
@@ -139,10 +161,18 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
     sE2[lane] = sEta * (gg - mg - x * mgx) * rs;
     const float loss = wave_sum(res * res);
     if (lane == 0) flag_nonfinite(p.status, loss);
+  } else if (tid >= HID && tid < 2 * HID) {
+    const float* r = reinterpret_cast<const float*>(redq);
+    const int j = tid - HID;
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < NWV; ++b) s += r[b * HID + j];
+    sPQ[j] = s;
   }
   __syncthreads();
 
-  // ---- E1 = (E2 W2^T) (.) G for this thread's four hidden rows; acc2 += A^K^T E2 ----
+  // ---- E1 = (E2 W2^T) (.) G for this thread's four hidden rows; acc2 += A^K^T E2 (stored
+  //      now: nothing after this changes it) ----
   {
     const float4 e = reinterpret_cast<const float4*>(sE2)[cg];
     float s[4];
@@ -170,29 +200,32 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
       a2[i].y = fmaf(a, e.y, a2[i].y);
       a2[i].z = fmaf(a, e.z, a2[i].z);
       a2[i].w = fmaf(a, e.w, a2[i].w);
+      const size_t o2 = static_cast<size_t>(4 * rb + i) * D + 4 * cg;
+      if (commit) {
+        *reinterpret_cast<float4*>(W2 + o2) =
+            float4{w2[i].x - a2[i].x, w2[i].y - a2[i].y, w2[i].z - a2[i].z, w2[i].w - a2[i].w};
+        *reinterpret_cast<float4*>(A2 + o2) = float4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        *reinterpret_cast<float4*>(A2 + o2) = a2[i];
+      }
     }
   }
   __syncthreads();
 
-  // ---- acc1 += k^T E1;  H^Q = q (W1 - acc1) (partial over the wave's rows) ----
+  // ---- H^Q = q (W1 - acc1) - (q . k) E1, A^Q = GELU;  acc1 += k^T E1 (stored) ----
+  if (tid < HID) {
+    const float hq = fmaf(-sQK, sE1[tid], sPQ[tid]);
+    sAQ[tid] = GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(hq) : gelu(hq, GELU_KIND);
+  }
   {
     const float4 e1 = reinterpret_cast<const float4*>(sE1)[lane];
-    float4 h = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float kk = sk[4 * wv + i], qq = sq[4 * wv + i];
+      const float kk = sk[4 * wv + i];
       a1[i].x = fmaf(kk, e1.x, a1[i].x);
       a1[i].y = fmaf(kk, e1.y, a1[i].y);
       a1[i].z = fmaf(kk, e1.z, a1[i].z);
       a1[i].w = fmaf(kk, e1.w, a1[i].w);
-      h.x = fmaf(qq, w1[i].x - a1[i].x, h.x);
-      h.y = fmaf(qq, w1[i].y - a1[i].y, h.y);
-      h.z = fmaf(qq, w1[i].z - a1[i].z, h.z);
-      h.w = fmaf(qq, w1[i].w - a1[i].w, h.w);
-    }
-    red1[wv][lane] = h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
       const size_t o1 = static_cast<size_t>(4 * wv + i) * HID + 4 * lane;
       if (commit) {
         *reinterpret_cast<float4*>(W1 + o1) =
@@ -204,28 +237,9 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (tid < HID) {
-    const float* r = reinterpret_cast<const float*>(red1);
-    float s = 0.f;
-#pragma unroll
-    for (int b = 0; b < NWV; ++b) s += r[b * HID + tid];
-    sAQ[tid] = GELU_KIND == TTT_GELU_ERF ? ttt_gelu::gelu(s) : gelu(s, GELU_KIND);
-  }
-  __syncthreads();
 
   // ---- Z^Q = A^Q (W2 - acc2) ----
   w2_partial(sAQ, w2, a2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t o2 = static_cast<size_t>(4 * rb + i) * D + 4 * cg;
-    if (commit) {
-      *reinterpret_cast<float4*>(W2 + o2) =
-          float4{w2[i].x - a2[i].x, w2[i].y - a2[i].y, w2[i].z - a2[i].z, w2[i].w - a2[i].w};
-      *reinterpret_cast<float4*>(A2 + o2) = float4{0.f, 0.f, 0.f, 0.f};
-    } else {
-      *reinterpret_cast<float4*>(A2 + o2) = a2[i];
-    }
-  }
   __syncthreads();
   // ---- z = q + LN(Z^Q) ----
   if (wv == 0) {

@@ -141,6 +141,13 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 // streams W_start and acc through registers once.
 bool decode_stream_supported(const DecodeParams& p);
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
+// Decode with four workgroups per head (MLP d = 64, hidden = 256); xbuf is its exchange area
+// in the workspace (after the status word), decode_split_workspace_bytes(B * H) bytes that are
+// zero before the first call and that every call leaves zero.
+constexpr int kDecodeSplitMaxHeads = 128;
+bool decode_split_supported(const DecodeParams& p);
+size_t decode_split_workspace_bytes(int heads);
+hipError_t launch_decode_split(const DecodeParams& p, void* xbuf, hipStream_t s);
 hipError_t launch_reset_status(unsigned* status, hipStream_t s);
 // dst[0] = src[0] on the stream (the status word of a workspace the caller cannot address)
 hipError_t launch_copy_status(const unsigned* src, unsigned* dst, hipStream_t s);

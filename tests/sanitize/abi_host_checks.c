@@ -58,6 +58,8 @@ int main(void) {
   b = c; b.T = 7; if (strcmp(ttt_fwd_kernel_name(&b), "") != 0) ++failures;
   if (strcmp(ttt_bwd_kernel_name(&c), "ttt_bwd_mfma_d64") != 0) ++failures;
   if (strcmp(ttt_decode_kernel_name(&c), "ttt_decode_stream_d64") != 0) ++failures;
+  b = c; b.flags = TTT_DECODE_SPLIT;
+  if (strcmp(ttt_decode_kernel_name(&b), "ttt_decode_split_d64") != 0) ++failures;
   /* forward: null, alignment, workspace */
   ttt_weights w = {(float*)P(0x10000), (float*)P(0x20000)};
   ttt_weights w_bad = {(float*)P(0x10000), NULL};
@@ -88,6 +90,10 @@ int main(void) {
   /* decode: position out of range */
   EXPECT(ttt_decode_step(&c, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), (float*)P(0x5000),
                          (float*)P(0x6000), &w, &w, 16, P(0x70000), P(0x90000), 256, NULL), TTT_ERR_ARG);
+  /* decode: a workspace without room for the four-workgroup kernel's exchange area */
+  b = c; b.flags = TTT_DECODE_SPLIT;
+  EXPECT(ttt_decode_step(&b, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), (float*)P(0x5000),
+                         (float*)P(0x6000), &w, &w, 3, P(0x70000), P(0x90000), 256, NULL), TTT_ERR_WORKSPACE);
   /* momentum: unsupported flag */
   b = c; b.flags = TTT_OUTPUT_KEY;
   EXPECT(ttt_scan_fwd_momentum(&b, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), (float*)P(0x5000),

@@ -90,7 +90,12 @@ def test_validate_bad_enums_and_flags():
 
 def test_workspace_and_saved_sizes():
     c = mlp_d64()
+    # decode: the status word, plus the exchange area of the four-workgroup kernel (4352 B per
+    # head, heads rounded up to a multiple of 8) where it runs
     assert ops.workspace_size(c, ops.TTT_OP_DECODE) == 256
+    assert ops.workspace_size(mlp_d64(decode_split=True), ops.TTT_OP_DECODE) == 256 + 96 * 4352
+    assert ops.workspace_size(mlp_d64(B=1, H=3, decode_split=True), ops.TTT_OP_DECODE) == 256 + 8 * 4352
+    assert ops.workspace_size(mlp_d64(B=16, decode_split=True), ops.TTT_OP_DECODE) == 256
     gen = ops.workspace_size(ops.Config(**{**c.__dict__, "force_generic": True}))
     assert gen == 256 + 8 * 12 * 2 * 64 * 256 * 4
     assert ops.workspace_size(c, ops.TTT_OP_BWD) > 256
@@ -110,6 +115,9 @@ def test_kernel_selection_names():
     assert ops.bwd_kernel_name(mlp_d64(io="f32")) == "ttt_bwd_generic"
     assert ops.bwd_kernel_name(mlp_d64(T=7)) == ""
     assert ops.decode_kernel_name(mlp_d64()) == "ttt_decode_stream_d64"
+    assert ops.decode_kernel_name(mlp_d64(decode_split=True)) == "ttt_decode_split_d64"
+    assert ops.decode_kernel_name(mlp_d64(B=16, decode_split=True)) == "ttt_decode_stream_d64"  # 192 heads
+    assert ops.decode_kernel_name(mlp_d64(io="f32", decode_split=True)) == "ttt_decode_split_d64"
     assert ops.decode_kernel_name(mlp_d64(force_generic=True)) == "ttt_decode_generic"
     # the Eq. 9 output rule runs on the portable kernels
     assert ops.fwd_kernel_name(mlp_d64(output_key=True)) == "ttt_fwd_generic"
@@ -123,10 +131,12 @@ def test_kernel_selection_names():
     assert ops.fwd_momentum_kernel_name(mlp_d64(d=128, hidden=512)) == "ttt_fwd_generic"
     assert ops.fwd_momentum_kernel_name(mlp_d64(output_key=True)) == ""
     assert ops.fwd_momentum_kernel_name(mlp_d64(chunk=256)) == ""
-    # mini-batches above 16 tokens: forward on the paired kernel, decode on the streaming
-    # one, no backward
+    # mini-batches above 16 tokens: forward on the paired kernel, decode on the tuned decode
+    # kernels, no backward
     assert ops.fwd_kernel_name(mlp_d64(chunk=256)) == "ttt_fwd_mfma_pair_d64"
     assert ops.decode_kernel_name(mlp_d64(chunk=256)) == "ttt_decode_stream_d64"
+    assert ops.decode_kernel_name(mlp_d64(chunk=256, decode_split=True)) == "ttt_decode_split_d64"
+    assert ops.decode_kernel_name(mlp_d64(chunk=256, one_wg_per_head=True)) == ""
     assert ops.bwd_kernel_name(mlp_d64(chunk=256)) == ""
     with pytest.raises(ops.TTTError):
         ops.workspace_size(mlp_d64(chunk=256), ops.TTT_OP_BWD)
@@ -178,6 +188,11 @@ def test_decode_rejects_bad_position():
                                  256, None) == 9
     assert L.ttt_decode_step(ctypes.byref(c.c()), *args, w, w, 3, P(0x70000), None, 256,
                              None) == 6
+    # the four-workgroup kernel's exchange area must fit in the workspace
+    cs = mlp_d64(decode_split=True)
+    need = ops.workspace_size(cs, ops.TTT_OP_DECODE)
+    assert L.ttt_decode_step(ctypes.byref(cs.c()), *args, w, w, 3, P(0x70000), P(0x90000),
+                             need - 16, None) == 6
 
 
 def test_bwd_rejects_missing_saved_buffer():

@@ -430,11 +430,22 @@ def test_decode_loop_equals_scan(wid):
         assert torch.count_nonzero(a).item() == 0
 
 
+DECODE_KERNELS = {
+    "split": (dict(decode_split=True), "ttt_decode_split_d64"),
+    "split_device_scope": (dict(decode_split=True, device_scope=True), "ttt_decode_split_d64"),
+    "stream": (dict(), "ttt_decode_stream_d64"),
+    "generic": (dict(force_generic=True), "ttt_decode_generic"),
+}
+
+
 @pytest.mark.parametrize("io,gelu", [("bf16", "erf"), ("f32", "tanh")])
-def test_decode_stream_equals_oracle(io, gelu):
-    """The tuned decode kernel (MLP, d=64) and the portable one: 48 decode steps (three
-    commits) over 2 x 3 heads of the d = 64 bf16 MLP workload's distributions, against the oracle scan of the
-    same tokens (z of every token, the committed weights)."""
+@pytest.mark.parametrize("kernel", list(DECODE_KERNELS))
+def test_decode_stream_equals_oracle(io, gelu, kernel):
+    """The tuned decode kernels (MLP, d=64: one workgroup per head, and four workgroups per
+    head on either exchange path) and the portable one: 48 decode steps (three commits) over
+    2 x 3 heads of the d = 64 bf16 MLP workload's distributions, against the oracle scan of the
+    same tokens (z of every token, the committed weights). All 48 calls share one workspace;
+    the four-workgroup kernel leaves its exchange area zero after every call."""
     w = WORKLOADS["ttt_mlp_bf16_d64_T8k"].with_(io=io)
     T, bi, hi = 48, [0, 5], [1, 6, 11]
     inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
@@ -444,24 +455,116 @@ def test_decode_stream_equals_oracle(io, gelu):
     sub = {**inp, "W0": tuple(x[0] for x in inp["W0"])}
     Zo, WTo, _ = oracle_heads(sub, pairs, "mlp", w.chunk, gelu=gelu)
     d = to_dev(inp)
-    for generic in (False, True):
-        cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io=io, gelu=gelu,
-                         w0_per_seq=True, force_generic=generic)
-        assert ops.decode_kernel_name(cfg) == ("ttt_decode_generic" if generic
-                                               else "ttt_decode_stream_d64")
-        note(f"decode {ops.decode_kernel_name(cfg)} io={io} gelu={gelu}")
-        Ws = tuple(x.clone() for x in d["W0"])
+    flags, name = DECODE_KERNELS[kernel]
+    cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io=io, gelu=gelu,
+                     w0_per_seq=True, **flags)
+    assert ops.decode_kernel_name(cfg) == name
+    note(f"decode {name} ({kernel}) io={io} gelu={gelu}")
+    ws = ops.new_workspace(cfg, ops.TTT_OP_DECODE, "cuda")
+    Ws = tuple(x.clone() for x in d["W0"])
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
+                          _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t % 16, workspace=ws)
+          for t in range(T)]
+    assert ops.read_status(ws) == 0
+    Z = torch.stack(zs, dim=2).cpu().reshape(B * H, T, 64)
+    tol = TOL[io]
+    assert_parity(Z, Zo, tol, f"decode Z {kernel}")
+    for a, b in zip(Ws, WTo):
+        assert rel_l2(a.cpu().reshape(b.shape), b) <= TOL["f32"], kernel
+    for a in acc:
+        assert torch.count_nonzero(a).item() == 0
+    assert torch.count_nonzero(ws[256:]).item() == 0
+
+
+def test_decode_full_size_both_tuned_kernels():
+    """Both tuned decode kernels on all 96 heads of the d = 64 workload (the launch the
+    benchmark times), one chunk of 16 calls on one workspace: each against the oracle on three
+    heads, and the two against each other on every head (the partial sums are added in another
+    order: fp32 rounding apart)."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    T = 16
+    inp = make_inputs(w, T=T)
+    d = to_dev(inp)
+    pairs = [(0, 0), (3, 7), (7, 11)]
+    Zo, WTo, _ = oracle_heads(inp, pairs, "mlp", w.chunk)
+    out = {}
+    for kernel in ("stream", "split"):
+        flags, name = DECODE_KERNELS[kernel]
+        cfg = ops_config(w, T=T, **flags)
+        assert ops.decode_kernel_name(cfg) == name
+        note(f"decode full size {name}")
+        ws = ops.new_workspace(cfg, ops.TTT_OP_DECODE, "cuda")
+        Ws = tuple(x.unsqueeze(0).expand(w.B, *x.shape).contiguous().clone() for x in d["W0"])
         acc = tuple(torch.zeros_like(x) for x in Ws)
         zs = [ops.decode_step(cfg, _tok(d["Q"], t), _tok(d["K"], t), _tok(d["V"], t),
-                              _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t % 16)
+                              _tok(d["eta"], t), d["gamma"], d["beta"], Ws, acc, t, workspace=ws)
               for t in range(T)]
-        Z = torch.stack(zs, dim=2).cpu().reshape(B * H, T, 64)
-        tol = TOL[io]
-        assert_parity(Z, Zo, tol, f"decode Z generic={generic}")
-        for a, b in zip(Ws, WTo):
-            assert rel_l2(a.cpu().reshape(b.shape), b) <= TOL["f32"], generic
+        assert ops.read_status(ws) == 0
+        Z, W = torch.stack(zs, dim=2).cpu(), tuple(x.cpu() for x in Ws)
+        out[kernel] = (Z, W)
+        assert_parity(torch.stack([Z[b, h] for b, h in pairs]), Zo, TOL["bf16"], f"decode Z {kernel} full size")
+        for k in range(2):
+            g = torch.stack([W[k][b, h] for b, h in pairs])
+            assert rel_l2(g.reshape(WTo[k].shape), WTo[k]) <= TOL["f32"], kernel
+    assert rel_l2(out["split"][0].float(), out["stream"][0].float()) <= 1e-2
+    for a, b in zip(out["split"][1], out["stream"][1]):
+        assert rel_l2(a, b) <= 1e-5
+
+
+@pytest.mark.parametrize("kernel", ["split", "stream"])
+def test_decode_chunk_replayed_as_graph(kernel):
+    """One chunk of 16 decode calls captured into a HIP graph (through torch.cuda.graph, on the
+    capture stream) and replayed three times, each replay after eager copies that reset the
+    weights and the accumulator and a synchronisation: every replay equals the eager run bit
+    for bit (the same kernels on the same inputs), and the exchange area stays zero."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    T, bi, hi = 16, [0, 5], [1, 6, 11]
+    inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
+    B, H = len(bi), len(hi)
+    flags, name = DECODE_KERNELS[kernel]
+    cfg = ops_config(w, T=T, B=B, H=H, **flags)
+    assert ops.decode_kernel_name(cfg) == name
+    note(f"decode graph replay {name}")
+    d = to_dev(inp)
+    toks = [[_tok(d[k], t) for k in ("Q", "K", "V", "eta")] for t in range(T)]
+    W0 = tuple(x.unsqueeze(0).expand(B, *x.shape).contiguous() for x in d["W0"])
+    ws = ops.new_workspace(cfg, ops.TTT_OP_DECODE, "cuda")
+    Ws = tuple(x.clone() for x in W0)
+    acc = tuple(torch.zeros_like(x) for x in Ws)
+    zs = [torch.empty(B, H, 64, dtype=cfg.io_dtype, device="cuda") for _ in range(T)]
+
+    def chunk(stream=None):
+        for t in range(T):
+            ops.decode_step(cfg, *toks[t][:3], toks[t][3], d["gamma"], d["beta"], Ws, acc, t,
+                            z=zs[t], workspace=ws, stream=stream)
+
+    chunk()
+    torch.cuda.synchronize()
+    ref_z = [z.clone() for z in zs]
+    ref_w = tuple(x.clone() for x in Ws)
+    g = torch.cuda.CUDAGraph()
+    for x, x0 in zip(Ws, W0):
+        x.copy_(x0)
+    for a in acc:
+        a.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        chunk(torch.cuda.current_stream())
+    for rep in range(3):
+        for x, x0 in zip(Ws, W0):
+            x.copy_(x0)
         for a in acc:
-            assert torch.count_nonzero(a).item() == 0
+            a.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert ops.read_status(ws) == 0
+        for t in range(T):
+            assert torch.equal(zs[t], ref_z[t]), (rep, t)
+        for x, r in zip(Ws, ref_w):
+            assert torch.equal(x, r), rep
+        assert torch.count_nonzero(ws[256:]).item() == 0
 
 
 @pytest.mark.parametrize("wid,kind", [("ttt_mlp_fp32_d16", "mlp"), ("ttt_linear_fp32_d64", "linear"),
