@@ -45,6 +45,8 @@ KERNEL_SOURCES = {
     "ttt_fwd_mfma_split_d128": ("ttt_fwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
                                 "ttt_gelu.hpp"),
     "ttt_bwd_mfma_d64": ("ttt_bwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_bwd_mfma_split_d64": ("ttt_bwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
+                               "ttt_gelu.hpp"),
     "ttt_fwd_mfma_mom_d64": ("ttt_fwd_mfma_mom.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
 }
 
@@ -279,7 +281,7 @@ def bench_scan_bwd(args) -> dict:
     from test_weight_sequence_amd.synth import WORKLOADS
     w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
-                     io=w.io)
+                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
     kernel = ops.bwd_kernel_name(cfg)
     dev = torch.device("cuda:0")
     d = _device_inputs(w, dev, with_dz=True)

@@ -136,11 +136,26 @@ size_t decode_ws_bytes(const ttt_config* c) {
   return kStatusBytes + (use_decode_split(c) ? decode_split_workspace_bytes(c->B * c->H) : 0);
 }
 
-size_t bwd_ws_bytes(const ttt_config* c) {
+// The tuned backward over two workgroups per head, unless TTT_ONE_WG_PER_HEAD asks for one
+// (host only; at launch the one-workgroup kernel runs instead if the device cannot hold a group
+// of eight heads' workgroups at once).
+bool use_bwd_split(const ttt_config* c) {
+  return use_bwd_mfma(c) && !(c->flags & TTT_ONE_WG_PER_HEAD);
+}
+
+// Workspace of the backward: status word, per-head dW (and the portable kernel's chunk
+// intermediates), per-head dgamma / dbeta partials, then the split kernel's exchange region.
+size_t bwd_ws_base_bytes(const ttt_config* c) {
   const size_t heads = static_cast<size_t>(c->B) * c->H;
   return kStatusBytes +
          heads * bwd_work_floats_per_head(c->kind, c->d, hidden_of(c), c->chunk) * sizeof(float) +
          heads * 2 * c->d * sizeof(float);
+}
+
+size_t bwd_ws_bytes(const ttt_config* c) {
+  const size_t base = bwd_ws_base_bytes(c);
+  if (!use_bwd_split(c)) return base;
+  return (base + 255) / 256 * 256 + bwd_split_workspace_bytes(c->B * c->H);
 }
 
 ttt_status map_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
@@ -249,6 +264,7 @@ const char* ttt_fwd_momentum_kernel_name(const ttt_config* cfg) {
 
 const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK || cfg->chunk > kMaxChunk) return "";
+  if (use_bwd_split(cfg)) return "ttt_bwd_mfma_split_d64";
   return use_bwd_mfma(cfg) ? "ttt_bwd_mfma_d64" : "ttt_bwd_generic";
 }
 
@@ -456,7 +472,14 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
   p.work = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
   p.dgb = p.work + heads * bwd_work_floats_per_head(cfg->kind, cfg->d, p.hid, cfg->chunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = tuned ? launch_bwd_mfma(p, s) : launch_bwd_generic(p, s);
+  hipError_t e;
+  if (use_bwd_split(cfg) && bwd_split_fits()) {
+    float* xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           (bwd_ws_base_bytes(cfg) + 255) / 256 * 256);
+    e = launch_bwd_mfma_split(p, xbuf, s);
+  } else {
+    e = tuned ? launch_bwd_mfma(p, s) : launch_bwd_generic(p, s);
+  }
   if (e != hipSuccess) return TTT_ERR_HIP;
   return map_hip(launch_bwd_finalize(p, s));
 }

@@ -134,6 +134,12 @@ hipError_t launch_bwd_generic(const BwdParams& p, hipStream_t s);
 // and dgamma/dbeta partials as the portable kernel, for the same finalize kernel.
 bool bwd_mfma_supported(const BwdParams& p);
 hipError_t launch_bwd_mfma(const BwdParams& p, hipStream_t s);
+// The same backward with two workgroups per head: the bytes of its exchange region (in the
+// workspace after the per-head dW and dgamma / dbeta regions), whether the device can hold
+// one group of eight heads' workgroups at once, and its launcher (xbuf: the region).
+size_t bwd_split_workspace_bytes(int heads);
+bool bwd_split_fits();
+hipError_t launch_bwd_mfma_split(const BwdParams& p, float* xbuf, hipStream_t s);
 size_t bwd_generic_lds_bytes(int kind, int d, int hid, int chunk);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);

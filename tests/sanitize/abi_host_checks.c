@@ -56,7 +56,9 @@ int main(void) {
   /* kernel names (host only) */
   if (strcmp(ttt_fwd_kernel_name(&c), "ttt_fwd_mfma_pair_d64") != 0) ++failures;
   b = c; b.T = 7; if (strcmp(ttt_fwd_kernel_name(&b), "") != 0) ++failures;
-  if (strcmp(ttt_bwd_kernel_name(&c), "ttt_bwd_mfma_d64") != 0) ++failures;
+  if (strcmp(ttt_bwd_kernel_name(&c), "ttt_bwd_mfma_split_d64") != 0) ++failures;
+  b = c; b.flags = TTT_ONE_WG_PER_HEAD;
+  if (strcmp(ttt_bwd_kernel_name(&b), "ttt_bwd_mfma_d64") != 0) ++failures;
   if (strcmp(ttt_decode_kernel_name(&c), "ttt_decode_stream_d64") != 0) ++failures;
   b = c; b.flags = TTT_DECODE_SPLIT;
   if (strcmp(ttt_decode_kernel_name(&b), "ttt_decode_split_d64") != 0) ++failures;

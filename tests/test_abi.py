@@ -114,6 +114,8 @@ def test_kernel_selection_names():
     assert ops.fwd_kernel_name(mlp_d64(T=7)) == ""
     assert ops.bwd_kernel_name(mlp_d64(io="f32")) == "ttt_bwd_generic"
     assert ops.bwd_kernel_name(mlp_d64(T=7)) == ""
+    assert ops.bwd_kernel_name(mlp_d64()) == "ttt_bwd_mfma_split_d64"
+    assert ops.bwd_kernel_name(mlp_d64(one_wg_per_head=True)) == "ttt_bwd_mfma_d64"
     assert ops.decode_kernel_name(mlp_d64()) == "ttt_decode_stream_d64"
     assert ops.decode_kernel_name(mlp_d64(decode_split=True)) == "ttt_decode_split_d64"
     assert ops.decode_kernel_name(mlp_d64(B=16, decode_split=True)) == "ttt_decode_stream_d64"  # 192 heads

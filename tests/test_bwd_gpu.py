@@ -134,41 +134,54 @@ def test_bwd_mlp_fp32_d16_full_T():
     _compare(gpu, ora, TOL["f32"])
 
 
-BWD_KERNELS = {"mfma": "ttt_bwd_mfma_d64", "generic": "ttt_bwd_generic"}
+BWD_KERNELS = {
+    "split": ("ttt_bwd_mfma_split_d64", {}),
+    "split_device_scope": ("ttt_bwd_mfma_split_d64", dict(device_scope=True)),
+    "one_wg": ("ttt_bwd_mfma_d64", dict(one_wg_per_head=True)),
+    "generic": ("ttt_bwd_generic", dict(force_generic=True)),
+}
 
 
-@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+@pytest.mark.parametrize("kernel", ["split", "one_wg", "generic"])
 @pytest.mark.parametrize("T", [64, 512])
 def test_bwd_mlp_bf16_d64_shape(T, kernel):
     """The d=64, hidden=256, bf16 I/O head shape through the tuned forward and each
-    backward kernel, two heads of two sequences, against the oracle."""
+    backward kernel (two workgroups per head, one, the portable kernel), two heads of two
+    sequences, against the oracle."""
     w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     inp = make_inputs(w, batch_idx=[0, 3], head_idx=[2, 15], T=T, with_dz=True)
     dZ = inp.pop("dZ")
+    name, flags = BWD_KERNELS[kernel]
     cfg = ops.Config(kind="mlp", B=2, H=2, T=T, d=w.d, hidden=w.hidden, chunk=w.chunk, io="bf16",
-                     force_generic=kernel == "generic")
-    assert ops.bwd_kernel_name(cfg) == BWD_KERNELS[kernel]
+                     **flags)
+    assert ops.bwd_kernel_name(cfg) == name
     note(f"bwd mlp bf16 d64 shape T={T} fwd={ops.fwd_kernel_name(cfg)} bwd={ops.bwd_kernel_name(cfg)}")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     ora = _oracle_grads(inp, dZ, None, "mlp", w.chunk, False)
     _compare(gpu, ora, TOL["bf16"])
 
 
-@pytest.mark.parametrize("T,per_seq,with_dwt,gelu,B,H", [
-    (48, True, True, "erf", 2, 3),
-    (80, False, True, "tanh", 3, 2),
-    (32, True, False, "tanh", 1, 5),
+@pytest.mark.parametrize("T,per_seq,with_dwt,gelu,B,H,kernel", [
+    (48, True, True, "erf", 2, 3, "split"),
+    (80, False, True, "tanh", 3, 2, "split"),
+    (32, True, False, "tanh", 1, 5, "split"),
+    (48, True, True, "erf", 2, 3, "one_wg"),
+    (80, False, True, "tanh", 3, 2, "one_wg"),
+    (32, True, False, "tanh", 1, 5, "one_wg"),
+    (48, False, True, "erf", 2, 5, "split_device_scope"),
 ])
-def test_bwd_mfma_variants(T, per_seq, with_dwt, gelu, B, H):
-    """The tuned backward with per-sequence W0, a nonzero adjoint of W_T and both GELU forms,
-    per-head gamma/beta, against the oracle. The weights are N(0, 0.2^2): with much smaller
+def test_bwd_mfma_variants(T, per_seq, with_dwt, gelu, B, H, kernel):
+    """The tuned backward kernels (two workgroups per head on either exchange path, and one)
+    with per-sequence W0, a nonzero adjoint of W_T and both GELU forms, per-head gamma/beta,
+    and head counts that leave most of the last group of eight empty, against the oracle. The weights are N(0, 0.2^2): with much smaller
     weights and these step sizes the chunk updates dwarf W, 1/sigma of the inner LayerNorm
     reaches ~50, and the bf16 operands of the tuned kernels lose 1-4% (forward 0.7%)."""
     inp, dZ, dWT = _rand_case("mlp", B, H, T, 64, "bf16", seed=T + B + H, per_seq=per_seq)
     dWT = dWT if with_dwt else None
+    name, flags = BWD_KERNELS[kernel]
     cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io="bf16",
-                     gelu=gelu, w0_per_seq=per_seq, eta_scale=0.5)
-    assert ops.bwd_kernel_name(cfg) == "ttt_bwd_mfma_d64"
+                     gelu=gelu, w0_per_seq=per_seq, eta_scale=0.5, **flags)
+    assert ops.bwd_kernel_name(cfg) == name
     note(f"bwd mfma {cfg}")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(),
                         None if dWT is None else tuple(x.cuda() for x in dWT))
@@ -185,7 +198,7 @@ def test_bwd_mlp_bf16_d64_B4H16_sampled_heads():
     dZ = inp.pop("dZ")
     cfg = ops.Config(kind="mlp", B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
                      io="bf16")
-    assert ops.bwd_kernel_name(cfg) == "ttt_bwd_mfma_d64"
+    assert ops.bwd_kernel_name(cfg) == "ttt_bwd_mfma_split_d64"
     note("bwd B=4 H=16 T=8192, sampled heads")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     torch.cuda.synchronize()
