@@ -413,6 +413,11 @@ bwd_split_kernel(BwdParams p, BSplit x) {
     gload(nchunks - 1, kk, qq, vv, zz, e);
     stage_write(sm.st[(nchunks - 1) & 1], kk, qq, vv, zz, e);
   }
+  // the start weights of the chunk to process next, loaded one chunk ahead (issued after the
+  // chunk's last exchange, so that no poll of the exchange waits for them)
+  f4 Wn1[NHT][NDT], Wn2[NDT][NHT];
+  wT_load(saved + static_cast<size_t>(nchunks - 1) * 2 * D * HID,
+          saved + static_cast<size_t>(nchunks - 1) * 2 * D * HID + D * HID, g, c16, hs, Wn1, Wn2);
   __syncthreads();
 
   for (int c = nchunks - 1; c >= 0; --c) {
@@ -429,9 +434,6 @@ bwd_split_kernel(BwdParams p, BSplit x) {
     // this chunk's start weights, as bf16 operand tiles in both orientations
     bf16x4 W1b[NDT][NHT], W2b[NHT][NDT], W1T[NHT][NDT], W2T[NDT][NHT];
     {
-      f4 Wn1[NHT][NDT], Wn2[NDT][NHT];
-      wT_load(saved + static_cast<size_t>(c) * 2 * D * HID,
-              saved + static_cast<size_t>(c) * 2 * D * HID + D * HID, g, c16, hs, Wn1, Wn2);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -789,6 +791,9 @@ bwd_split_kernel(BwdParams p, BSplit x) {
     __syncthreads();  // ---- 6
 
     // ================= G: dAK, dHK, dK, remaining dW terms =================
+    if (has_next)
+      wT_load(saved + static_cast<size_t>(c - 1) * 2 * D * HID,
+              saved + static_cast<size_t>(c - 1) * 2 * D * HID + D * HID, g, c16, hs, Wn1, Wn2);
     I4 = fresh(I4);
     bf16x8 aZK[2];
     rows2(sm.dZK, c16, g, aZK);

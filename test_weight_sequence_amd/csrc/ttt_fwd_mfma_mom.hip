@@ -23,8 +23,11 @@
 //
 // The memory and the momentum together are 256 KiB of fp32 per head, twice what one CU's
 // registers can hold next to the rest, so a head is split by hidden units over S = 2
-// workgroups of 4 waves: wave w of part s holds hidden units 128 s + 32 w .. + 32 of both M and
-// S as MFMA accumulator tiles. The two sums over all hidden units, Z^K and Z^Q, are formed from
+// workgroups of 8 waves, two per SIMD: wave w of part s holds hidden units 128 s + 16 w .. + 16
+// of both M and S as MFMA accumulator tiles (its products over hidden units are 16 deep, one
+// half of the 32-deep instruction's operands zero; the matrix cores have room, and two waves
+// per SIMD hide each other's VALU latencies). Waves 0-3 also run the per-token phases, 16 lanes
+// per token. The two sums over all hidden units, Z^K and Z^Q, are formed from
 // the parts' [16 x 64] partials, exchanged through the L2 of the XCD both parts sit on as
 // (value, chunk tag) pairs that the reader polls; each part adds the partials in the same
 // order, so both compute the same Z^K, En2 and outputs. Across XCDs the exchange falls back
@@ -50,15 +53,16 @@ constexpr int HID = 256;
 constexpr int BC = 16;
 constexpr int NDT = D / 16;          // d tiles
 constexpr int S = 2;                 // workgroups per head
-constexpr int NW = 4;                // waves per workgroup
+constexpr int NW = 8;                // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
-constexpr int HS = HID / (S * NW);   // hidden units per wave (32)
-constexpr int NHT = HS / 16;         // h tiles per wave (2)
+constexpr int HS = HID / (S * NW);   // hidden units per wave (16)
+constexpr int NHT = HS / 16;         // h tiles per wave (1)
+constexpr int NLN = 4;               // waves 0..3 run the per-token phases, 16 lanes per token
 constexpr int NKD = D / 32;          // 32-wide k-steps over d (2)
 constexpr int RS = D + 8;            // row stride (bf16) of [token][d] arrays
 constexpr int DPL = D / 16;          // d values per LayerNorm lane
 constexpr int kSpinLimit = 1 << 20;
-static_assert(NHT == 2 && NW * 4 == BC, "tile split");
+static_assert(NHT == 1 && NLN * 4 == BC, "tile split");
 
 // Workspace per head: two exchange areas (Z^K, Z^Q) of two chunk-parity slots of S partial
 // [16 x 64] sums, each element a (value, chunk index + 1) pair of 32-bit words; then (after
@@ -226,7 +230,7 @@ __device__ __forceinline__ void coef_fill(const Stage& st, Coef& cf, int lane) {
 }
 
 template <int GELU_KIND>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mom_kernel(ScanParams p, Split x) {
   __shared__ Smem sm;
   // block -> (head, part): the S parts of a head are 8 blocks apart (same XCD)
@@ -305,7 +309,8 @@ fwd_mom_kernel(ScanParams p, Split x) {
     float th, mo, al;
   };
   auto gload = [&](int chunk) {
-    Ld r;
+    Ld r{};
+    if (tid >= NLN * 64) return r;
     const size_t off = (static_cast<size_t>(chunk) * BC + st_t) * D + st_d;
     r.k = *reinterpret_cast<const uint2*>(Kg + off);
     r.q = *reinterpret_cast<const uint2*>(Qg + off);
@@ -317,6 +322,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
     return r;
   };
   auto stage_write = [&](Stage& St, const Ld& r) {
+    if (tid >= NLN * 64) return;
     *reinterpret_cast<uint2*>(&St.K[st_t * RS + st_d]) = r.k;
     *reinterpret_cast<uint2*>(&St.Q[st_t * RS + st_d]) = r.q;
     *reinterpret_cast<uint2*>(&St.V[st_t * RS + st_d]) = r.v;
@@ -415,7 +421,8 @@ fwd_mom_kernel(ScanParams p, Split x) {
     chk = sum16(chk);
     if (c16 == 0) flag_nonfinite(p.status, chk);
   };
-  const bool out_wave = (w & 1) == s;  // waves that write outputs: 2 per part, 4 tokens each
+  const bool ln_wave = w < NLN;                 // waves with per-token lanes
+  const bool out_wave = ln_wave && (w & 1) == s;  // waves that write outputs: 2 per part, 4 tokens each
 
   stage_write(sm.st[0], gload(0));
   __syncthreads();
@@ -486,7 +493,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
     for (int ht = 0; ht < NHT; ++ht) akT[ht] = cvt4(mfma16(akR[ht], I4, zero4()));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const f4 acc = mfma32(cat(akT[0], akT[1]), cat(M2b[0][dt], M2b[1][dt]), zero4());
+      const f4 acc = mfma16(akT[0], M2b[0][dt], zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
     }
@@ -499,13 +506,13 @@ fwd_mom_kernel(ScanParams p, Split x) {
     // whose output is written now), LayerNorm forward/backward -> En2 and its two weighted
     // copies for the chunk-end updates ----
     float ownK[DPL];
-    put_own(false, slot, c1, ownK);
+    if (ln_wave) put_own(false, slot, c1, ownK);
     if (!m.local) {
       publish(m, 0, s, c1);
       wait_all(m, 0, s, c1, p.status);
     }
     if (c > 0 && out_wave) ln_out(c - 1);
-    {
+    if (ln_wave) {
       const int t = ln_t;
       float z[DPL];
       total(false, slot, c1, ownK, z);
@@ -589,7 +596,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
       for (int r = 0; r < 4; ++r) a[r] = mfma::act_fwd<GELU_KIND>(h[r]);
       aqT[ht] = cvt4(mfma16(cvt4(a), I4, zero4()));
     }
-    f4 s2t = mfma32(cat(akT[0], akT[1]), cat(aqT[0], aqT[1]), zero4());  // C[s][t] = A^K_s . A^Q_t
+    f4 s2t = mfma16(akT[0], aqT[0], zero4());  // this wave's share of C[s][t] = A^K_s . A^Q_t
     f4 s2m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) s2m[r] = wmask[r] * s2t[r];
@@ -599,8 +606,8 @@ fwd_mom_kernel(ScanParams p, Split x) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const bf16x4 be = mfma::tgroup(sm.E2, RS, dt, g, c16);
-      f4 accm = mfma32(cat(aqT[0], aqT[1]), cat(M2b[0][dt], M2b[1][dt]), zero4());
-      const f4 accs = mfma32(cat(aqT[0], aqT[1]), cat(S2b[0][dt], S2b[1][dt]), zero4());
+      f4 accm = mfma16(aqT[0], M2b[0][dt], zero4());
+      const f4 accs = mfma16(aqT[0], S2b[0][dt], zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) accm[r] = rA[r] * accm[r] + rB[r] * accs[r];
       accm = mfma16(s2a, be, accm);
@@ -623,7 +630,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
     __syncthreads();
 
     // ---- publish this part's Z^Q partial of chunk c (its output is written next chunk) ----
-    put_own(true, slot, c1, ownQ);
+    if (ln_wave) put_own(true, slot, c1, ownQ);
     if (!m.local) publish(m, 8, s, c1);
   }
   if (!m.local) wait_all(m, 8, s, static_cast<unsigned>(nchunks), p.status);
