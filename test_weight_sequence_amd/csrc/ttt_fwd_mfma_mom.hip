@@ -229,6 +229,34 @@ __device__ __forceinline__ void coef_fill(const Stage& st, Coef& cf, int lane) {
   }
 }
 
+// The same coefficients from gates held in registers (lane t < 16: mom_t, alpha_t), for a
+// wave with nothing else to do: the values travel between lanes by readlane instead of being
+// read from LDS inside the recurrence, and the operations are those of coef_fill in the same
+// order.
+__device__ __forceinline__ void coef_regs(float mo, float al, Coef& cf, int lane) {
+  const int s = lane & 15;
+  float dd = 1.f, cc = 0.f, a = 1.f, b = 0.f, pp = 1.f;
+#pragma unroll
+  for (int t = 0; t < BC; ++t) {
+    const float mt = __shfl(mo, t, 64), at = __shfl(al, t, 64);
+    if (t > s) dd *= mt;
+    cc = t >= s ? (1.f - at) * cc + dd : 0.f;
+    if (lane < BC) {
+      cf.C[t][s] = cc;
+      cf.Dm[t][s] = t >= s ? dd : 0.f;
+    }
+    const float keep = 1.f - at;
+    pp *= mt;
+    a *= keep;
+    b = keep * b + pp;
+    if (lane == 0) {
+      cf.A[t] = a;
+      cf.B[t] = b;
+      cf.P[t] = pp;
+    }
+  }
+}
+
 template <int GELU_KIND>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mom_kernel(ScanParams p, Split x) {
@@ -438,6 +466,13 @@ fwd_mom_kernel(ScanParams p, Split x) {
     const bool has_next = c + 1 < nchunks;
     Ld nx{};
     if (has_next) nx = gload(c + 1);
+    // the next chunk's gates for its coefficients, computed by wave NLN during the per-token
+    // phase below (it has no per-token lanes)
+    float mo_n = 0.f, al_n = 0.f;
+    if (w == NLN && has_next && lane < BC) {
+      mo_n = mog[(c + 1) * BC + lane];
+      al_n = alg[(c + 1) * BC + lane];
+    }
 
     bf16x8 aK[NKD], aQ[NKD];
 #pragma unroll
@@ -547,6 +582,8 @@ fwd_mom_kernel(ScanParams p, Split x) {
       }
     }
     if (has_next) stage_write(sm.st[(c + 1) % 3], nx);
+    // coefficients of chunk c + 1 (chunk c uses the other buffer)
+    if (w == NLN && has_next) coef_regs(mo_n, al_n, sm.cf[(c + 1) & 1], lane);
     __syncthreads();
 
     // ---- E1n = (En2 M2^T) (.) G and its weighted copies; H^Q; A^Q; Z^Q partial ----
@@ -625,8 +662,6 @@ fwd_mom_kernel(ScanParams p, Split x) {
         S2c[ht][dt] = mfma16(akR[ht], bd, Pb * S2c[ht][dt]);
       }
     }
-    // coefficients of chunk c + 1 (its gates were staged before the last barrier)
-    if (has_next && w == 0) coef_fill(sm.st[(c + 1) % 3], sm.cf[(c + 1) & 1], lane);
     __syncthreads();
 
     // ---- publish this part's Z^Q partial of chunk c (its output is written next chunk) ----
