@@ -87,11 +87,15 @@ struct Coef {
 
 struct Smem {
   Stage st[3];                       // chunk c lives in st[c % 3]
-  float red[NW][NDT][4][64];         // per-wave [token x d] partial tiles (lane-rotated rows)
   alignas(16) __bf16 E2[BC * RS];    // En2 = -theta delta2, [token][d]
   alignas(16) __bf16 E2c[BC * RS];   // C_bt En2_t (the memory's update)
   alignas(16) __bf16 E2d[BC * RS];   // D_bt En2_t (the momentum's update)
   Coef cf[2];                        // chunk c uses cf[c & 1]
+  // per-wave [token x d] partial tiles (lane-rotated rows): [0] Z^K, [1] Z^Q. Separate
+  // buffers, so that a chunk's Z^K partials are never written while the previous chunk's Z^Q
+  // partials are still being read (no barrier lies between those reads and these writes).
+  // Last, so that the small arrays stay within the LDS instructions' 16-bit offsets.
+  float red[2][NW][NDT][4][64];
 };
 
 __device__ __forceinline__ int prot(int r, int lane) { return (lane + 16 * r) & 63; }
@@ -361,13 +365,13 @@ fwd_mom_kernel(ScanParams p, Split x) {
     }
   };
   // this part's [16 x 64] partial for the LayerNorm lanes' elements (fixed wave order)
-  auto own_partial = [&](float (&o)[DPL]) {
+  auto own_partial = [&](bool zq, float (&o)[DPL]) {
     const int t = ln_t;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
       float a = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) a += sm.red[ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
+      for (int ww = 0; ww < NW; ++ww) a += sm.red[zq][ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
       o[i] = a;
     }
   };
@@ -382,7 +386,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
     rs = __builtin_amdgcn_rsqf(sum16(v) * (1.0f / D) + p.eps);
   };
   auto put_own = [&](bool zq, int slot, unsigned tag, float (&own)[DPL]) {
-    own_partial(own);
+    own_partial(zq, own);
 #pragma unroll
     for (int i = 0; i < DPL; ++i)
       part_store(m, zq, (slot * S + s) * kPartFloats + ln_t * D + 16 * i + c16, own[i], tag);
@@ -530,7 +534,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
     for (int dt = 0; dt < NDT; ++dt) {
       const f4 acc = mfma16(akT[0], M2b[0][dt], zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.red[0][w][dt][r][prot(r, lane)] = acc[r];
     }
     f4 s1t = zero4();  // C[s][t] = K_s . Q_t
 #pragma unroll
@@ -649,7 +653,7 @@ fwd_mom_kernel(ScanParams p, Split x) {
       for (int r = 0; r < 4; ++r) accm[r] = rA[r] * accm[r] + rB[r] * accs[r];
       accm = mfma16(s2a, be, accm);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = accm[r];
+      for (int r = 0; r < 4; ++r) sm.red[1][w][dt][r][prot(r, lane)] = accm[r];
       // chunk-end updates of this wave's fp32 memory and momentum
       const bf16x4 kt = mfma::tgroup(St.K, RS, dt, g, c16);
       const bf16x4 bc = mfma::tgroup(sm.E2c, RS, dt, g, c16);

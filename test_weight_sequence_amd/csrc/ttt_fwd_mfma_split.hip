@@ -79,7 +79,10 @@ struct Stage {
 
 struct Smem {
   Stage st[3];                        // chunk c lives in st[c % 3]
-  float red[NW][NDT][4][64];          // per-wave [token x d] partial tiles (lane-rotated rows)
+  // per-wave [token x d] partial tiles (lane-rotated rows): [0] Z^K, [1] Z^Q. Separate
+  // buffers, so that a chunk's Z^K partials are never written while the previous chunk's Z^Q
+  // partials are still being read (no barrier lies between those reads and these writes).
+  float red[2][NW][NDT][4][64];
   alignas(16) __bf16 E2[BC * RS];     // En2, [token][d]
 };
 
@@ -284,13 +287,13 @@ fwd_split_kernel(ScanParams p, Split x) {
   };
   // this workgroup's [16 x 128] partial for the LayerNorm lanes' elements, from the waves'
   // tiles in red (fixed wave order)
-  auto own_partial = [&](float (&o)[DPL]) {
+  auto own_partial = [&](bool zq, float (&o)[DPL]) {
     const int t = ln_t;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
       float a = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) a += sm.red[ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
+      for (int ww = 0; ww < NW; ++ww) a += sm.red[zq][ww][i][t & 3][prot(t & 3, 16 * (t >> 2) + c16)];
       o[i] = a;
     }
   };
@@ -306,7 +309,7 @@ fwd_split_kernel(ScanParams p, Split x) {
   };
   // store this part's partial of chunk parity `slot` (the LayerNorm lanes' elements)
   auto put_own = [&](bool zq, int slot, unsigned tag, float (&own)[DPL]) {
-    own_partial(own);
+    own_partial(zq, own);
 #pragma unroll
     for (int i = 0; i < DPL; ++i)
       part_store(m, zq, (slot * S + s) * kPartFloats + ln_t * D + 16 * i + c16, own[i], tag);
@@ -441,7 +444,7 @@ fwd_split_kernel(ScanParams p, Split x) {
     for (int dt = 0; dt < NDT; ++dt) {
       const f4 acc = mfma32(cat(akT[0], akT[1]), cat(W2b[0][dt], W2b[1][dt]), zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.red[0][w][dt][r][prot(r, lane)] = acc[r];
     }
     f4 s1t = zero4();  // C[s][t] = K_s . Q_t
 #pragma unroll
@@ -530,7 +533,7 @@ fwd_split_kernel(ScanParams p, Split x) {
       f4 acc = mfma32(cat(aqT[0], aqT[1]), cat(W2b[0][dt], W2b[1][dt]), zero4());
       acc = mfma16(s2a, be, acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.red[w][dt][r][prot(r, lane)] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.red[1][w][dt][r][prot(r, lane)] = acc[r];
       // chunk-end update of this wave's fp32 weights
       const bf16x4 kt = mfma::tgroup(St.K, RS, dt, g, c16);
 #pragma unroll
