@@ -551,6 +551,21 @@ fwd_mom_kernel(ScanParams p, Split x) {
       wait_all(m, 0, s, c1, p.status);
     }
     if (c > 0 && out_wave) ln_out(c - 1);
+    // the chunk-end state before this chunk's gradients: M <- A_b M + B_b S, S <- P_b S (the
+    // bf16 operand copies of the chunk-start state were taken above), while the other part's
+    // Z^K partial is on its way
+    {
+      const float Ab = cf.A[BC - 1], Bb = cf.B[BC - 1], Pb = cf.P[BC - 1];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          M1c[dt][ht] = Ab * M1c[dt][ht] + Bb * S1c[dt][ht];
+          S1c[dt][ht] = Pb * S1c[dt][ht];
+          M2c[ht][dt] = Ab * M2c[ht][dt] + Bb * S2c[ht][dt];
+          S2c[ht][dt] = Pb * S2c[ht][dt];
+        }
+    }
     if (ln_wave) {
       const int t = ln_t;
       float z[DPL];
@@ -642,8 +657,6 @@ fwd_mom_kernel(ScanParams p, Split x) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s2m[r] = wmask[r] * s2t[r];
     const bf16x4 s2a = cvt4(s2m);
-    // the chunk-end state before the updates: M <- A_b M + B_b S, S <- P_b S
-    const float Ab = cf.A[BC - 1], Bb = cf.B[BC - 1], Pb = cf.P[BC - 1];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const bf16x4 be = mfma::tgroup(sm.E2, RS, dt, g, c16);
@@ -660,10 +673,10 @@ fwd_mom_kernel(ScanParams p, Split x) {
       const bf16x4 bd = mfma::tgroup(sm.E2d, RS, dt, g, c16);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        M1c[dt][ht] = mfma16(kt, e1c[ht], Ab * M1c[dt][ht] + Bb * S1c[dt][ht]);
-        S1c[dt][ht] = mfma16(kt, e1d[ht], Pb * S1c[dt][ht]);
-        M2c[ht][dt] = mfma16(akR[ht], bc, Ab * M2c[ht][dt] + Bb * S2c[ht][dt]);
-        S2c[ht][dt] = mfma16(akR[ht], bd, Pb * S2c[ht][dt]);
+        M1c[dt][ht] = mfma16(kt, e1c[ht], M1c[dt][ht]);
+        S1c[dt][ht] = mfma16(kt, e1d[ht], S1c[dt][ht]);
+        M2c[ht][dt] = mfma16(akR[ht], bc, M2c[ht][dt]);
+        S2c[ht][dt] = mfma16(akR[ht], bd, S2c[ht][dt]);
       }
     }
     __syncthreads();
