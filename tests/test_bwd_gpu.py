@@ -191,8 +191,10 @@ def test_bwd_mfma_variants(T, per_seq, with_dwt, gelu, B, H, kernel):
 
 
 def test_bwd_mlp_bf16_d64_B4H16_sampled_heads():
-    """Full launch at B=4, H=16, T=8192 of the tuned backward; the oracle checks the
-    per-token gradients (dQ, dK, dV, deta) of two heads at full length."""
+    """Full launch at B=4, H=16, T=8192 of the tuned backward. The oracle checks head 4 on all
+    four sequences at full length: the per-token gradients (dQ, dK, dV, deta) and, summed over
+    the batch as W0, gamma and beta are shared, dW0, dgamma and dbeta of that head; and the
+    per-token gradients of head 13 of sequence 3."""
     w = WORKLOADS["ttt_mlp_bf16_d64_fwd_bwd"]
     inp = make_inputs(w, with_dz=True)
     dZ = inp.pop("dZ")
@@ -202,12 +204,20 @@ def test_bwd_mlp_bf16_d64_B4H16_sampled_heads():
     note("bwd B=4 H=16 T=8192, sampled heads")
     _, gpu = _gpu_grads(cfg, to_dev(inp), dZ.cuda(), None)
     torch.cuda.synchronize()
-    for b, h in [(1, 4), (3, 13)]:
-        sub = make_inputs(w, batch_idx=[b], head_idx=[h], with_dz=True)
-        sdz = sub.pop("dZ")
-        ora = _oracle_grads(sub, sdz, None, "mlp", w.chunk, False)
-        one = {k: gpu[k][b:b + 1, h:h + 1] for k in ("dQ", "dK", "dV", "deta")}
-        _compare(one, ora, TOL["bf16"], keys=("dQ", "dK", "dV", "deta"))
+    gpu = {k: (tuple(x.cpu() for x in v) if isinstance(v, tuple) else v.cpu()) for k, v in gpu.items()
+           if k in ("dQ", "dK", "dV", "deta", "dgamma", "dbeta", "dW0")}
+    sub = make_inputs(w, batch_idx=range(w.B), head_idx=[4], with_dz=True)
+    sdz = sub.pop("dZ")
+    ora = _oracle_grads(sub, sdz, None, "mlp", w.chunk, False)
+    mine = {k: gpu[k][:, 4:5] for k in ("dQ", "dK", "dV", "deta")}
+    mine.update({k: gpu[k][4:5] for k in ("dgamma", "dbeta")})
+    mine["dW0"] = tuple(x[4:5] for x in gpu["dW0"])
+    _compare(mine, ora, TOL["bf16"])
+    sub = make_inputs(w, batch_idx=[3], head_idx=[13], with_dz=True)
+    sdz = sub.pop("dZ")
+    ora = _oracle_grads(sub, sdz, None, "mlp", w.chunk, False)
+    one = {k: gpu[k][3:4, 13:14] for k in ("dQ", "dK", "dV", "deta")}
+    _compare(one, ora, TOL["bf16"], keys=("dQ", "dK", "dV", "deta"))
 
 
 def test_bwd_mlp_bf16_d64_B4H16_runs_and_is_finite():
