@@ -31,6 +31,12 @@ def flops_per_token_head(d: int, h: int, b: int) -> int:
     return 14 * d * h + 4 * b * (d + h)
 
 
+def key_flops_per_token_head(d: int, h: int) -> int:
+    # the key-side output rule (z_t = f(K_t; W at the chunk start)): the two query-side
+    # products and the four dual-form products drop out, five d*h-sized products remain
+    return 10 * d * h
+
+
 def bytes_per_token_head(d: int, io_bytes: int, nW: int, T: int) -> float:
     # Q, K, V in, Z out (io dtype), eta (fp32), W0 read + W_T written, amortised over T
     return 4 * d * io_bytes + 4 + 2 * nW * 4 / T
@@ -38,6 +44,7 @@ def bytes_per_token_head(d: int, io_bytes: int, nW: int, T: int) -> float:
 
 KERNEL_SOURCES = {
     "ttt_fwd_mfma_pair_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
+    "ttt_fwd_mfma_key_d64": ("ttt_fwd_mfma_pair.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_mfma_d64": ("ttt_fwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_generic": ("ttt_fwd_generic.hip",),
     "ttt_decode_stream_d64": ("ttt_decode_stream.hip", "ttt_device.hpp", "ttt_gelu.hpp"),
@@ -59,10 +66,11 @@ def _source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, n_launch_units: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+def _traffic(kernel: str, n_launch_units: int, variant: str = ""):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (of the launch
+    variant named by `variant`, e.g. "_b256"), if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}{variant}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -84,10 +92,11 @@ def _cpu_model() -> str:
     return ""
 
 
-def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool = False) -> dict:
+def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool = False,
+                 output: str = "query") -> dict:
     """The fp64 oracle on the first n_seq sequences (the first n_heads heads of each, default
     all), first T tokens; with grads, the oracle's outer-loop gradients (autograd through
-    its primal scan) instead of the forward."""
+    its primal scan) instead of the forward; `output` picks the output rule."""
     import torch
     from oracle import OracleConfig, scan, scan_outer_grads
     from test_weight_sequence_amd.synth import flatten_heads, make_inputs
@@ -97,7 +106,7 @@ def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool 
     inp = flatten_heads(make_inputs(w, batch_idx=list(range(n_seq)), head_idx=list(range(nh)),
                                     T=T, with_dz=grads))
     pairs = n_seq * nh
-    cfg = OracleConfig(kind=w.kind, chunk=w.chunk)
+    cfg = OracleConfig(kind=w.kind, chunk=w.chunk, output=output)
     t0 = time.perf_counter()
     if grads:
         scan_outer_grads(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"],
@@ -106,6 +115,8 @@ def cpu_baseline(w, n_seq: int, T: int, n_heads: int | None = None, grads: bool 
         scan(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], inp["gamma"], inp["beta"], cfg)
     dt = time.perf_counter() - t0
     what = "outer-loop gradients (autograd through the primal scan)" if grads else "forward scan"
+    if output != "query":
+        what += f" ({output}-side output rule)"
     return {"value": pairs * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
             "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"fp64 oracle {what} on sequences 0..{n_seq - 1} x heads 0..{nh - 1} "
@@ -159,16 +170,18 @@ def _device_inputs(w, dev, with_dz=False):
             for k, v in inp.items()}
 
 
-def bench_scan_fwd(args, wid: str) -> dict:
-    """One step = one ttt_scan_fwd over the whole batch."""
+def bench_scan_fwd(args, wid: str, output_key: bool = False) -> dict:
+    """One step = one ttt_scan_fwd over the whole batch (with the key-side output rule of
+    Eq. 9 in the E2E paper review, section 2.4.2, when output_key)."""
     import ctypes
     import torch
     from test_weight_sequence_amd import ops
     from test_weight_sequence_amd.synth import WORKLOADS
     w = WORKLOADS[wid]
-    headline = wid == "ttt_mlp_bf16_d64_T8k"
+    headline = wid == "ttt_mlp_bf16_d64_T8k" and not output_key
     cfg = ops.Config(kind=w.kind, B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk,
-                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg)
+                     io=w.io, force_generic=args.force_generic, one_wg_per_head=args.one_wg,
+                     output_key=output_key)
     kernel = ops.fwd_kernel_name(cfg)
     dev = torch.device("cuda:0")
     d = _device_inputs(w, dev)
@@ -196,28 +209,36 @@ def bench_scan_fwd(args, wid: str) -> dict:
     # A mini-batch larger than 16 tokens is evaluated in 16-token blocks (the dual-form tril
     # products inside a block, the earlier blocks through the running weights), so the work per
     # token is that of b = 16 however large the mini-batch is.
-    flop = units * flops_per_token_head(w.d, w.hidden, min(w.chunk, 16))
+    flop = units * (key_flops_per_token_head(w.d, w.hidden) if output_key else
+                    flops_per_token_head(w.d, w.hidden, min(w.chunk, 16)))
     achieved = flop / (k_avg * 1e-3) / 1e12
     mfma = kernel != "ttt_fwd_generic"
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_VALU_TFLOPS
     io_bytes = 2 if w.io == "bf16" else 4
     metric = ("TTT-MLP scan token*heads/s at d=64, T=8K (+ fraction of MI355X dense bf16 MFMA peak)"
               if headline else f"TTT-MLP scan token*heads/s at d={w.d}, T={w.T}" +
-              (f", mini-batch {w.chunk}" if w.chunk != 16 else ""))
+              (f", mini-batch {w.chunk}" if w.chunk != 16 else "") +
+              (", key-side output rule (z_t = f(K_t; W at the chunk start))" if output_key else ""))
     out = _base_record(args, metric, units / (ms_step * 1e-3), ms_step, w, kernel,
-                       "bf16" if mfma else "f32")
+                       "bf16" if mfma else "f32", {"output": "key"} if output_key else None)
+    # counter summaries are per launch variant: larger mini-batches move different bytes
+    # from the 16-token launch of the same kernel
+    variant = "" if w.chunk == 16 else f"_b{w.chunk}"
     out["roofline"] = {
         "bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
         "unit": "TFLOP/s", "frac": achieved / peak,
-        "traffic": _traffic(kernel, units) if kernel in KERNEL_SOURCES else None,
+        "traffic": _traffic(kernel, units, variant) if kernel in KERNEL_SOURCES else None,
         "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
-        "algorithmic_bytes_per_launch": units * bytes_per_token_head(
-            w.d, io_bytes, 2 * w.d * w.hidden, w.T)}
+        # (Q is not read under the key-side rule)
+        "algorithmic_bytes_per_launch": units * (bytes_per_token_head(
+            w.d, io_bytes, 2 * w.d * w.hidden, w.T) - (w.d * io_bytes if output_key else 0))}
     if not args.no_cpu_baseline:
         if headline:
             out["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, args.cpu_T)
         else:
-            out["cpu_baseline"] = cpu_baseline(w, 1, 2048)
+            # about 10-15 s of oracle work: up to 8 sequences x 4096 tokens
+            out["cpu_baseline"] = cpu_baseline(w, min(w.B, 8), 4096,
+                                               output="key" if output_key else "query")
     return out
 
 
@@ -410,7 +431,7 @@ def main():
                     help="untimed steps (default 5; 1 for the d=128 workload)")
     ap.add_argument("--workload", default="scan_fwd",
                     choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode",
-                             "scan_fwd_momentum", "scan_fwd_bigchunk"],
+                             "scan_fwd_momentum", "scan_fwd_bigchunk", "scan_fwd_key"],
                     help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
                          "scan_fwd_b16: the same head shape at B=16 (192 heads, 131,072 tokens "
                          "per batch); "
@@ -418,6 +439,7 @@ def main():
                          "scan_fwd_momentum: the B=8 forward with momentum and forget gate; "
                          "scan_fwd_bigchunk: the B=8 forward with mini-batches of --chunk "
                          "tokens (256 or 1024); "
+                         "scan_fwd_key: the B=8 forward with the key-side output rule; "
                          "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
     ap.add_argument("--chunk", type=int, default=256, choices=[256, 1024],
@@ -474,6 +496,8 @@ def main():
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
     elif args.workload == "scan_fwd_bigchunk":
         out = bench_scan_fwd(args, f"ttt_mlp_bf16_d64_T8k_b{args.chunk}")
+    elif args.workload == "scan_fwd_key":
+        out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k", output_key=True)
     elif args.workload == "scan_bwd":
         out = bench_scan_bwd(args)
     elif args.workload == "scan_fwd_momentum":

@@ -75,9 +75,17 @@ ScanParams scan_params(const ttt_config* c) {
   return p;
 }
 
-// The tuned kernels implement the default output rule only; TTT_OUTPUT_KEY runs on the
-// portable ones.
+// The tuned kernels implement the default output rule; TTT_OUTPUT_KEY has its own tuned
+// forward (use_key) and otherwise runs on the portable kernels.
 bool tuned_allowed(const ttt_config* c) { return !(c->flags & (TTT_FORCE_GENERIC | TTT_OUTPUT_KEY)); }
+
+// Forward with the key-side output rule, MLP d = 64 bf16 chunk 16: the paired kernel's
+// producer alone, one workgroup per head (any number of heads).
+bool use_key(const ttt_config* c) {
+  if (c->flags & TTT_FORCE_GENERIC) return false;
+  ScanParams p = scan_params(c);
+  return fwd_key_supported(p);
+}
 
 bool use_mfma(const ttt_config* c) {
   if (!tuned_allowed(c)) return false;
@@ -98,6 +106,7 @@ bool use_split(const ttt_config* c) {
 }
 
 size_t fwd_ws_bytes(const ttt_config* c) {
+  if (use_key(c)) return kStatusBytes;
   if (use_pair(c)) return kStatusBytes + fwd_pair_workspace_bytes(c->B * c->H);
   if (use_mfma(c)) return kStatusBytes;
   const size_t generic = static_cast<size_t>(c->B) * c->H * weights_per_head(c) * sizeof(float);
@@ -251,6 +260,7 @@ ttt_status ttt_saved_size(const ttt_config* cfg, size_t* bytes) {
 
 const char* ttt_fwd_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, true) != TTT_OK) return "";
+  if (use_key(cfg)) return "ttt_fwd_mfma_key_d64";
   if (use_pair(cfg)) return "ttt_fwd_mfma_pair_d64";
   if (use_split(cfg)) return "ttt_fwd_mfma_split_d128";
   return use_mfma(cfg) ? "ttt_fwd_mfma_d64" : "ttt_fwd_generic";
@@ -316,6 +326,7 @@ static ttt_status fwd_launch(const ttt_config* cfg, const void* Q, const void* K
   p.saved = static_cast<float*>(saved);
   p.status = static_cast<unsigned*>(workspace);
   p.wbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
+  if (use_key(cfg)) return map_hip(launch_fwd_mfma_key(p, s));
   if (use_pair(cfg) && fwd_pair_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_pair(p, s));
   if (cfg->chunk > kMaxChunk) return TTT_ERR_UNSUPPORTED;  // only the paired kernel takes these
   if (use_split(cfg) && fwd_split_fits(cfg->B * cfg->H)) return map_hip(launch_fwd_mfma_split(p, s));

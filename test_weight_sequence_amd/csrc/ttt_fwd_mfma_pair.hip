@@ -44,6 +44,11 @@
 // transposes and the look-ahead correction are made once per mini-batch instead of once per
 // sub-tile; the fp32 weights still take each sub-tile's update in order, bit for bit as in
 // the consumer.
+//
+// Key-side output rule (Eq. 9 of the E2E paper review, section 2.4.2: z_t = f(K_t; W at the
+// mini-batch start), 16-token mini-batches): the output is K + LN(Z^K), which the producer's
+// LayerNorm lanes already hold, so a separate kernel runs the producer alone, one workgroup
+// per head, and writes it there; no consumer, no hand-off.
 #include "ttt_mfma_common.hpp"
 
 namespace ttt {
@@ -307,11 +312,14 @@ __device__ __forceinline__ void head_init(const ScanParams& p, const Ctx& x, Hea
   }
 }
 
-template <int GELU_KIND, bool LOCAL, bool LARGE>
+template <int GELU_KIND, bool LOCAL, bool LARGE, bool KEY = false>
 __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x, ProdSmem& S) {
   const int tid = x.tid, lane = x.lane, w = x.w, g = x.g, c16 = x.c16, head = x.head, hs = x.hs;
   const int T = x.T, nchunks = x.nchunks;
   const HandOff<LOCAL> ho(x.flags, x.ring);
+  // Output rule z_t = f(K_t; W at the mini-batch start) (TTT_OUTPUT_KEY): the LayerNorm lanes
+  // write it from Z^K, and there is no consumer to hand anything to.
+  constexpr bool key_out = KEY;
   const __bf16* Kg = x.Kg;
   const __bf16* Xg = x.Xg;
   const float* etag = x.etag;
@@ -497,13 +505,13 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     }
     // publish chunk c - 1: its slot stores were the last vector-memory operations before
     // this chunk's three input loads
-    if (c > 0) {
+    if (c > 0 && !key_out) {
       asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
       if (lane == 0) ho.st(w, static_cast<unsigned>(c));
       compiler_fence();
     }
     // chunks the consumer is done reading (checked after the barriers)
-    const unsigned cons = ho.ld(16);
+    const unsigned cons = key_out ? 0u : ho.ld(16);
     if (p.saved && first) {
       float* sv = p.saved + (static_cast<size_t>(head) * (nchunks / m) + c / m) * (2 * D * HID);
       wtiles_store(sv, sv + D * HID, g, c16, hs, W1c, W2c);
@@ -547,6 +555,14 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
         const float loss = sum16(l2);
         if (c16 == 0) p.loss[static_cast<size_t>(head) * T + t0 + t] = loss;
       }
+      if (key_out) {
+        // z = K + gamma xhat + beta = (K + beta - V) + gamma xhat + V
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+          const int d = 16 * i + c16;
+          x.Zg[static_cast<size_t>(t0 + t) * D + d] = (__bf16)(kvb[i] + gam[i] * xh[i] + bf(st.X[t * RS + d]));
+        }
+      }
       // mean(g) is non-finite whenever any residual (inputs, Z^K) is
       if (c16 == 0) flag_nonfinite(p.status, mg);
     } else {
@@ -573,17 +589,19 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
     TTT_STAMP(s7);
 
     // hand chunk c to the consumer: slot c % RING must have been read (chunk c - RING)
-    const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
-    if (cons < need) spin_geq(ho, 16, need, p.status);
-    compiler_fence();
-    const int base = (c % RING) * SLOT_BYTES;
-    ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
-    ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
-    if (w == 0) {
-      ho.st16(base + SLOT_E2 + lane * 32, cat(tgroup(S.E2, RS, 0, g, c16), tgroup(S.E2, RS, 1, g, c16)));
-      ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, RS, 2, g, c16), tgroup(S.E2, RS, 3, g, c16)));
+    if (!key_out) {
+      const unsigned need = c >= RING ? static_cast<unsigned>(c - RING + 1) : 0u;
+      if (cons < need) spin_geq(ho, 16, need, p.status);
+      compiler_fence();
+      const int base = (c % RING) * SLOT_BYTES;
+      ho.st16(base + SLOT_E1 + (w * 64 + lane) * 16, out.e1);
+      ho.st16(base + SLOT_AK + (w * 64 + lane) * 16, out.ak);
+      if (w == 0) {
+        ho.st16(base + SLOT_E2 + lane * 32, cat(tgroup(S.E2, RS, 0, g, c16), tgroup(S.E2, RS, 1, g, c16)));
+        ho.st16(base + SLOT_E2 + lane * 32 + 16, cat(tgroup(S.E2, RS, 2, g, c16), tgroup(S.E2, RS, 3, g, c16)));
+      }
+      compiler_fence();
     }
-    compiler_fence();
 #ifdef TTT_PHASE_CLOCKS
     TTT_STAMP(s8);
     if (c >= 16) {
@@ -605,7 +623,7 @@ __device__ __forceinline__ void producer_body(const ScanParams& p, const Ctx& x,
   if (c < nchunks) step(c, ca, cb);
   const Carry& last = (nchunks & 1) ? cb : ca;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (lane == 0) ho.st(w, static_cast<unsigned>(nchunks));
+  if (lane == 0 && !key_out) ho.st(w, static_cast<unsigned>(nchunks));
   // the last chunk's update (its En2 is still in E2)
   chunk_update(W1c, W2c, S.st[(nchunks - 1) & 3].K, S.E2, last.e1, last.ak, g, c16, zz);
   if (p.wt_1)
@@ -845,6 +863,34 @@ fwd_mfma_pair_kernel(ScanParams p, Pair q) {
   }
 }
 
+// The key-side output rule: one workgroup per (batch, head) running the producer alone (its
+// hand-off code is compiled out, so the flags and ring are never touched).
+template <int GELU_KIND>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_mfma_key_kernel(ScanParams p) {
+  __shared__ ProdSmem sm;
+  Ctx x;
+  x.tid = threadIdx.x;
+  x.lane = x.tid & 63;
+  x.w = x.tid >> 6;
+  x.g = x.lane >> 4;
+  x.c16 = x.lane & 15;
+  x.head = blockIdx.x;
+  x.hidx = x.head % p.H;
+  x.hs = x.w * HS;
+  x.T = p.T;
+  x.nchunks = p.T / BC;
+  x.m = 1;
+  x.flags = nullptr;
+  x.ring = nullptr;
+  const size_t io_off = static_cast<size_t>(x.head) * p.T * D;
+  x.Kg = static_cast<const __bf16*>(p.K) + io_off;
+  x.Xg = static_cast<const __bf16*>(p.V) + io_off;
+  x.Zg = static_cast<__bf16*>(p.Z) + io_off;
+  x.etag = p.eta + static_cast<size_t>(x.head) * p.T;
+  producer_body<GELU_KIND, true, false, true>(p, x, sm);
+}
+
 __global__ void pair_reset_kernel(unsigned* flags, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0u;
 }
@@ -906,6 +952,19 @@ hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t stream) {
                        : (large ? reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF, true>)
                                 : reinterpret_cast<const void*>(fwd_mfma_pair_kernel<TTT_GELU_ERF, false>));
   return hipLaunchCooperativeKernel(fn, dim3(fwd_pair_blocks(nheads)), dim3(NT), args, 0, stream);
+}
+
+bool fwd_key_supported(const ScanParams& p) {
+  return fwd_pair_supported(p) && p.chunk == BC && (p.flags & TTT_OUTPUT_KEY);
+}
+
+hipError_t launch_fwd_mfma_key(const ScanParams& p, hipStream_t stream) {
+  const int nheads = p.B * p.H;
+  if (p.gelu == TTT_GELU_TANH)
+    hipLaunchKernelGGL(fwd_mfma_key_kernel<TTT_GELU_TANH>, dim3(nheads), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(fwd_mfma_key_kernel<TTT_GELU_ERF>, dim3(nheads), dim3(NT), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace ttt

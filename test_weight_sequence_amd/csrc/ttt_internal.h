@@ -108,6 +108,10 @@ size_t fwd_pair_workspace_bytes(int nheads);
 int fwd_pair_blocks(int nheads);
 bool fwd_pair_fits(int nheads);
 hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t s);
+// The key-side output rule (TTT_OUTPUT_KEY) on the same head shape, 16-token mini-batches:
+// the paired kernel's producer alone, one workgroup per head, no workspace.
+bool fwd_key_supported(const ScanParams& p);
+hipError_t launch_fwd_mfma_key(const ScanParams& p, hipStream_t s);
 // Forward for the d = 128, hidden = 512 head: each head split by hidden units over four
 // workgroups that exchange [chunk x d] partial sums through the workspace.
 bool fwd_split_supported(const ScanParams& p);

@@ -98,6 +98,8 @@ def test_workspace_and_saved_sizes():
     assert ops.workspace_size(mlp_d64(B=16, decode_split=True), ops.TTT_OP_DECODE) == 256
     gen = ops.workspace_size(ops.Config(**{**c.__dict__, "force_generic": True}))
     assert gen == 256 + 8 * 12 * 2 * 64 * 256 * 4
+    # key-side output rule: the tuned kernel needs the status word only
+    assert ops.workspace_size(mlp_d64(output_key=True)) == 256
     assert ops.workspace_size(c, ops.TTT_OP_BWD) > 256
     assert ops.saved_size(c) == 8 * 12 * 512 * 2 * 64 * 256 * 4
     lin = ops.Config(kind="linear", B=4, H=12, T=2048, d=64, io="f32", force_generic=True)
@@ -121,8 +123,13 @@ def test_kernel_selection_names():
     assert ops.decode_kernel_name(mlp_d64(B=16, decode_split=True)) == "ttt_decode_stream_d64"  # 192 heads
     assert ops.decode_kernel_name(mlp_d64(io="f32", decode_split=True)) == "ttt_decode_split_d64"
     assert ops.decode_kernel_name(mlp_d64(force_generic=True)) == "ttt_decode_generic"
-    # the Eq. 9 output rule runs on the portable kernels
-    assert ops.fwd_kernel_name(mlp_d64(output_key=True)) == "ttt_fwd_generic"
+    # the Eq. 9 output rule: a tuned forward (the paired kernel's producer alone, one
+    # workgroup per head, any head count), the rest on the portable kernels
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True)) == "ttt_fwd_mfma_key_d64"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, one_wg_per_head=True)) == "ttt_fwd_mfma_key_d64"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, B=64)) == "ttt_fwd_mfma_key_d64"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, io="f32")) == "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, force_generic=True)) == "ttt_fwd_generic"
     assert ops.bwd_kernel_name(mlp_d64(output_key=True)) == "ttt_bwd_generic"
     assert ops.decode_kernel_name(mlp_d64(output_key=True)) == "ttt_decode_generic"
     assert ops.validate(mlp_d64(output_key=True)) == 0

@@ -103,16 +103,18 @@ def test_bwd_fp32_matches_oracle_autograd(kind, d, chunk, T, per_seq, with_dwt, 
     _compare(gpu, ora, TOL["f32"])
 
 
-@pytest.mark.parametrize("kind,d,chunk,T", [("mlp", 16, 16, 64), ("linear", 32, 8, 32),
-                                           ("mlp", 64, 16, 48)])
-def test_bwd_key_output_matches_oracle(kind, d, chunk, T):
+@pytest.mark.parametrize("kind,d,chunk,T,io", [("mlp", 16, 16, 64, "f32"), ("linear", 32, 8, 32, "f32"),
+                                              ("mlp", 64, 16, 48, "f32"), ("mlp", 64, 16, 64, "bf16")])
+def test_bwd_key_output_matches_oracle(kind, d, chunk, T, io):
     """Outer-loop gradients with the Eq. 9 output rule through the portable backward: dz
-    reaches K directly and through the first LayerNorm; dQ is exactly zero."""
+    reaches K directly and through the first LayerNorm; dQ is exactly zero. The bf16 d = 64
+    case takes its saved chunk-start weights from the tuned key-output forward."""
     B, H = 2, 2
-    inp, dZ, dWT = _rand_case(kind, B, H, T, d, "f32", seed=d + T + 1, per_seq=False)
-    cfg = ops.Config(kind=kind, B=B, H=H, T=T, d=d, hidden=4 * d, chunk=chunk, io="f32",
+    inp, dZ, dWT = _rand_case(kind, B, H, T, d, io, seed=d + T + 1, per_seq=False)
+    cfg = ops.Config(kind=kind, B=B, H=H, T=T, d=d, hidden=4 * d, chunk=chunk, io=io,
                      output_key=True, eta_scale=0.5)
     assert ops.bwd_kernel_name(cfg) == "ttt_bwd_generic"
+    assert ops.fwd_kernel_name(cfg) == ("ttt_fwd_mfma_key_d64" if io == "bf16" else "ttt_fwd_generic")
     note(f"bwd key output {cfg}")
     dv = to_dev(inp)
     _, gpu = _gpu_grads(cfg, dv, dZ.cuda(), tuple(w.cuda() for w in dWT))
@@ -120,7 +122,7 @@ def test_bwd_key_output_matches_oracle(kind, d, chunk, T):
     assert torch.count_nonzero(gpu["dQ"]).item() == 0
     ora = _oracle_grads(inp, dZ, dWT, kind, chunk, False, eta_scale=0.5, output="key")
     assert torch.count_nonzero(ora["dQ"]).item() == 0
-    _compare(gpu, ora, TOL["f32"], keys=("dK", "dV", "deta", "dgamma", "dbeta", "dW0"))
+    _compare(gpu, ora, TOL[io], keys=("dK", "dV", "deta", "dgamma", "dbeta", "dW0"))
 
 
 def test_bwd_mlp_fp32_d16_full_T():

@@ -305,6 +305,29 @@ def test_pair_tanh_per_seq():
         assert_parity(g.reshape(o.shape), o, TOL["bf16"], "W_T", time_axis=False)
 
 
+@pytest.mark.parametrize("B,H,T,gelu,per_seq", [(2, 3, 160, "tanh", True), (9, 16, 48, "erf", False)])
+def test_key_output_tuned_variants(B, H, T, gelu, per_seq):
+    """The tuned key-output forward with tanh GELU and per-sequence W0, and with 144 heads
+    (above the paired kernel's head limit), all heads, Z, W_T and the loss."""
+    inp = _rand_case("mlp", B, H, T, 64, 16, "bf16", seed=B * 100 + T, per_seq=per_seq)
+    cfg = ops.Config(kind="mlp", B=B, H=H, T=T, d=64, hidden=256, chunk=16, io="bf16",
+                     gelu=gelu, w0_per_seq=per_seq, eta_scale=0.5, output_key=True)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_key_d64"
+    note(f"key output tuned B={B} H={H} T={T} {gelu} per_seq={per_seq}")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    flat, ocfg = _oracle_all(inp, "mlp", 16, per_seq=per_seq, gelu=gelu, eta_scale=0.5,
+                             output="key")
+    from oracle import scan as oracle_scan
+    Z, WT, L = oracle_scan(flat["Q"], flat["K"], flat["V"], flat["eta"], flat["W0"],
+                           flat["gamma"], flat["beta"], ocfg)
+    assert_parity(res["Z"].reshape(B * H, T, 64), Z, TOL["bf16"], "Z")
+    assert_parity(res["loss"].reshape(B * H, T), L, TOL["bf16"], "loss", per_token=False)
+    for g, o in zip(res["W_T"], WT):
+        assert_parity(g.reshape(o.shape), o, TOL["bf16"], "W_T", time_axis=False)
+
+
 def _rand_case(kind, B, H, T, d, chunk, io, seed, per_seq=False):
     g = torch.Generator().manual_seed(seed)
     hid = 4 * d if kind == "mlp" else d
@@ -570,16 +593,17 @@ def test_decode_chunk_replayed_as_graph(kernel):
 @pytest.mark.parametrize("wid,kind", [("ttt_mlp_fp32_d16", "mlp"), ("ttt_linear_fp32_d64", "linear"),
                                       ("ttt_mlp_bf16_d64_T8k", "mlp")])
 def test_key_output_forward_and_decode(wid, kind):
-    """The Eq. 9 output rule (z_t = f(K_t; W at the chunk start)) through the portable forward
-    and the portable decode, against the oracle with the same rule; the per-token loss equals
-    ||z_t - V_t||^2 up to the output rounding."""
+    """The Eq. 9 output rule (z_t = f(K_t; W at the chunk start)) through the forward (the
+    tuned kernel for the bf16 d = 64 shape, the portable one otherwise) and the portable
+    decode, against the oracle with the same rule."""
     w = WORKLOADS[wid]
     T = 64
     bi, hi = [0], ([0, 1] if w.H > 1 else [0])
     inp = make_inputs(w, batch_idx=bi, head_idx=hi, T=T)
     B, H = len(bi), len(hi)
     cfg = ops_config(w, T=T, B=B, H=H, output_key=True)
-    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_generic"
+    want = "ttt_fwd_mfma_key_d64" if wid == "ttt_mlp_bf16_d64_T8k" else "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(cfg) == want
     note(f"key output {wid}")
     d = to_dev(inp)
     res = _run(cfg, d, want_loss=True)
@@ -593,8 +617,34 @@ def test_key_output_forward_and_decode(wid, kind):
           for t in range(T)]
     assert_parity(torch.stack(zs, dim=2).reshape(B * H, T, -1), res["Z"].reshape(B * H, T, -1),
                   TOL[w.io], "key-output decode vs scan")
-    for a, b in zip(Ws, res["W_T"]):
-        assert rel_l2(a, b) <= TOL["f32"]
+    # the decode's final memory against the oracle's, and against the scan's (the tuned bf16
+    # forward rounds its update operands to bf16, the portable kernels do not)
+    WTo = oracle_heads(inp, pairs, w.kind, w.chunk, output="key")[1]
+    for a, b, o in zip(Ws, res["W_T"], WTo):
+        assert_parity(a.reshape(o.shape), o, TOL[w.io], "key-output decode W_T", time_axis=False)
+        assert rel_l2(a, b) <= TOL[w.io]
+
+
+@pytest.mark.parametrize("kernel", ["tuned", "generic"])
+def test_key_output_bf16_d64_T8k_sampled_heads(kernel):
+    """The Eq. 9 output rule over the full launch at B=8, H=12, T=8192 (the tuned kernel: the
+    paired kernel's producer alone; or the portable kernel); the oracle with the same rule checks three heads
+    at full T. Under this rule the per-token loss is ||z_t - V_t||^2, which every head's device
+    output must reproduce up to the bf16 rounding of z."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    cfg = ops_config(w, output_key=True, force_generic=kernel == "generic")
+    want = "ttt_fwd_mfma_key_d64" if kernel == "tuned" else "ttt_fwd_generic"
+    assert ops.fwd_kernel_name(cfg) == want
+    note(f"key output bf16 d64 T8k full {kernel}")
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    res = _run(cfg, d, want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    _check_heads(res, inp, [(0, 0), (3, 7), (7, 11)], w, TOL["bf16"], cfg_kw=dict(output="key"))
+    # the loss is the squared distance of the (unrounded) output to V
+    zl = ((res["Z"].float() - d["V"].float()) ** 2).sum(-1)
+    assert rel_l2(zl, res["loss"]) <= TOL["bf16"]
 
 
 def test_scan_then_decode_continues_the_sequence():
