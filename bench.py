@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "ttt_bwd_mfma_d64": ("ttt_bwd_mfma.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_bwd_mfma_split_d64": ("ttt_bwd_mfma_split.hip", "ttt_mfma_common.hpp", "ttt_device.hpp",
                                "ttt_gelu.hpp"),
+    "ttt_lact_fwd_d64": ("ttt_lact.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
     "ttt_fwd_mfma_mom_d64": ("ttt_fwd_mfma_mom.hip", "ttt_mfma_common.hpp", "ttt_device.hpp", "ttt_gelu.hpp"),
 }
 
@@ -286,6 +287,75 @@ def bench_scan_fwd_momentum(args) -> dict:
     return out
 
 
+def lact_flops_per_token_head(d: int, h: int) -> int:
+    # nine d*h-sized products per token: K W1, K W3, V W2^T, the three gradient sums
+    # (K^T gA, K^T gC, u~^T V) and the read-out Q W1, Q W3, U W2
+    return 18 * d * h
+
+
+def bench_lact(args) -> dict:
+    """One step = one ttt_lact_fwd (the large-chunk SwiGLU layer) over the whole batch:
+    B=8, H=12, T=8192, d=64, hidden=256, chunks of 2048 tokens."""
+    import torch
+    from test_weight_sequence_amd import ops
+    from test_weight_sequence_amd.synth import WORKLOADS
+    w = WORKLOADS["lact_swiglu_bf16_d64_T8k_b2048"]
+    cfg = ops.Config(kind="swiglu", B=w.B, H=w.H, T=w.T, d=w.d, hidden=w.hidden, chunk=w.chunk, io=w.io)
+    dev = torch.device("cuda:0")
+    d = _device_inputs(w, dev)
+    ws = ops.new_workspace(cfg, ops.TTT_OP_LACT, dev)
+    Z = torch.empty(w.B, w.H, w.T, w.d, dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        ops.lact_fwd(cfg, d["Q"], d["K"], d["V"], d["eta"], d["W0"], workspace=ws, out=Z)
+        return 0
+
+    ms_step, kms = _time_calls(call, args.steps, args.warmup)
+    if ops.read_status(ws) != 0:
+        raise RuntimeError("kernel reported non-finite values")
+    k_avg = statistics.fmean(kms)
+    units = w.B * w.H * w.T
+    flop = units * lact_flops_per_token_head(w.d, w.hidden)
+    achieved = flop / (k_avg * 1e-3) / 1e12
+    kernel = "ttt_lact_fwd_d64"
+    out = _base_record(args, f"LaCT SwiGLU layer token*heads/s at d={w.d}, T={w.T}, chunk {w.chunk}",
+                       units / (ms_step * 1e-3), ms_step, w, kernel, "bf16")
+    out["data"] = ("synthetic (seeded N(0,1/d) Q/K/V, W1, W3 ~ N(0,1/d), W2 ~ N(0,1/hidden), "
+                   "eta=1.0*sigmoid(N(0,1)))")
+    nW = 3 * w.d * w.hidden
+    out["roofline"] = {
+        "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic(kernel, units),
+        # one call = T/chunk + 1 launches of the step kernel and the W_T copy-out; the
+        # duration is the whole call's, bracketed by events on the launch stream
+        "kernel_ms": k_avg, "kernel_ms_min": min(kms), "flop_per_launch": flop,
+        # Q, K, V in and Z out (bf16), eta in, W0 in and W_T out (fp32, three matrices)
+        "algorithmic_bytes_per_launch": units * (4 * w.d * 2 + 4) + w.H * nW * 4 + w.B * w.H * nW * 4}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_lact(w, 1, 4096)
+    return out
+
+
+def cpu_baseline_lact(w, n_seq: int, T: int) -> dict:
+    """The fp64 oracle's large-chunk layer (scan_lact) on the first n_seq sequences, all heads,
+    first T tokens."""
+    import torch
+    from oracle import scan_lact
+    from test_weight_sequence_amd.synth import flatten_heads, make_inputs
+    torch.set_num_threads(max(1, torch.get_num_threads()))
+    cores = torch.get_num_threads()
+    inp = flatten_heads(make_inputs(w, batch_idx=list(range(n_seq)), T=T))
+    t0 = time.perf_counter()
+    scan_lact(inp["Q"], inp["K"], inp["V"], inp["eta"], inp["W0"], w.chunk)
+    dt = time.perf_counter() - t0
+    pairs = n_seq * w.H
+    return {"value": pairs * T / dt, "unit": "token*heads/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"fp64 oracle scan_lact on sequences 0..{n_seq - 1} x heads 0..{w.H - 1} "
+                      f"({pairs} (batch, head) pairs) x first T={T} tokens of the same workload "
+                      f"({dt:.1f} s wall, torch intra-op threads={cores})"}
+
+
 def bwd_flops_per_token_head(d: int, h: int, b: int) -> int:
     # The chunk's forward recomputed from its saved start weights (the five forward products:
     # K W1, A^K W2, E2 W2^T, Q W1, A^Q W2, and the four dual terms), then two adjoint
@@ -431,7 +501,7 @@ def main():
                     help="untimed steps (default 5; 1 for the d=128 workload)")
     ap.add_argument("--workload", default="scan_fwd",
                     choices=["scan_fwd", "scan_fwd_b16", "scan_fwd_d128", "scan_bwd", "decode",
-                             "scan_fwd_momentum", "scan_fwd_bigchunk", "scan_fwd_key"],
+                             "scan_fwd_momentum", "scan_fwd_bigchunk", "scan_fwd_key", "lact"],
                     help="scan_fwd: B=8 H=12 T=8192 d=64 forward (the headline); "
                          "scan_fwd_b16: the same head shape at B=16 (192 heads, 131,072 tokens "
                          "per batch); "
@@ -440,6 +510,7 @@ def main():
                          "scan_fwd_bigchunk: the B=8 forward with mini-batches of --chunk "
                          "tokens (256 or 1024); "
                          "scan_fwd_key: the B=8 forward with the key-side output rule; "
+                         "lact: the large-chunk SwiGLU layer, B=8 H=12 T=8192, chunks of 2048; "
                          "scan_bwd: B=4 H=16 T=8192 d=64 outer-loop backward; "
                          "decode: one chunk of decode steps at the B=8 H=12 d=64 shape")
     ap.add_argument("--chunk", type=int, default=256, choices=[256, 1024],
@@ -496,6 +567,8 @@ def main():
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d128_T128k")
     elif args.workload == "scan_fwd_bigchunk":
         out = bench_scan_fwd(args, f"ttt_mlp_bf16_d64_T8k_b{args.chunk}")
+    elif args.workload == "lact":
+        out = bench_lact(args)
     elif args.workload == "scan_fwd_key":
         out = bench_scan_fwd(args, "ttt_mlp_bf16_d64_T8k", output_key=True)
     elif args.workload == "scan_bwd":

@@ -70,7 +70,8 @@ typedef enum {
   TTT_ERR_TIMEOUT = 10     /* a bounded wait between cooperating workgroups expired */
 } ttt_status;
 
-enum { TTT_LINEAR = 0, TTT_MLP = 1 };
+/* TTT_SWIGLU: the large-chunk SwiGLU layer of ttt_lact_fwd (no other entry point takes it) */
+enum { TTT_LINEAR = 0, TTT_MLP = 1, TTT_SWIGLU = 2 };
 enum { TTT_F32 = 0, TTT_BF16 = 1 };
 enum { TTT_GELU_ERF = 0, TTT_GELU_TANH = 1 };
 /* ttt_config.flags */
@@ -92,13 +93,15 @@ enum {
                                      to each other with device-scope atomics and fences even
                                      when they share an XCD (slower). This is the path taken when
                                      they do not; the flag lets a test run it. */,
-  TTT_DECODE_SPLIT = 1 << 5 /* decode, MLP d = 64: four workgroups per (batch, head), split by
+  TTT_DECODE_SPLIT = 1 << 5, /* decode, MLP d = 64: four workgroups per (batch, head), split by
                                hidden units, instead of one (at most 128 heads). Measured slower
                                than one workgroup per head at every head count tried (12-120);
                                kept as the alternative the library can run and test. */
+  TTT_LACT_READ_BEFORE = 1 << 6 /* ttt_lact_fwd only: a chunk's tokens are read out with the
+                                   weights the chunk started from instead of the updated ones */
 };
 /* op codes for ttt_workspace_size */
-enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2, TTT_OP_FWD_MOMENTUM = 3 };
+enum { TTT_OP_FWD = 0, TTT_OP_BWD = 1, TTT_OP_DECODE = 2, TTT_OP_FWD_MOMENTUM = 3, TTT_OP_LACT = 4 };
 
 typedef struct {
   int32_t kind;      /* TTT_LINEAR or TTT_MLP                                         */
@@ -121,11 +124,19 @@ typedef struct {
   float* w2;
 } ttt_weights;
 
+/* SwiGLU fast weights of ttt_lact_fwd, fp32 device pointers: w1, w3 [.., d, hidden],
+ * w2 [.., hidden, d]. */
+typedef struct {
+  float* w1;
+  float* w2;
+  float* w3;
+} ttt_swiglu_weights;
+
 /* Host-only check of a configuration (no HIP call). */
 ttt_status ttt_validate(const ttt_config* cfg);
 
 /* Bytes of workspace the op needs (TTT_OP_FWD / TTT_OP_BWD / TTT_OP_DECODE /
- * TTT_OP_FWD_MOMENTUM).
+ * TTT_OP_FWD_MOMENTUM / TTT_OP_LACT; the last one with a TTT_SWIGLU config).
  * Host only. The first 256 bytes of every workspace hold the status word; the
  * caller zero-fills a new workspace once (or calls ttt_reset_status). */
 ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes);
@@ -223,6 +234,29 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
                            const ttt_weights* W_start, const ttt_weights* acc,
                            int32_t pos_in_chunk, void* z, void* workspace, size_t ws_bytes,
                            void* stream);
+
+/* The large-chunk SwiGLU TTT layer ("Test-Time Training(TTT)과 LLM 메모리", section "LaCT"):
+ *   f_W(x) = (SiLU(x W1) * (x W3)) W2                          (Eq. 6, row vectors)
+ *   chunk of b tokens: g = eta_scale * sum_t eta_t grad_W (-f_W(K_t) . V_t) at the chunk-start
+ *                      W (Eq. 7 and 4);  W <- L2-Normalize(W - g)  (Eq. 8)
+ *   z_t = f_W(Q_t)  (Eq. 2) with the weights after the chunk's update (TTT_LACT_READ_BEFORE:
+ *                      with the chunk-start weights).
+ * L2-Normalize scales every output unit's weight vector to unit norm: each column of W1 and
+ * W3 (over d) and each column of W2 (over hidden); W0 itself is used as given.
+ *  cfg: kind TTT_SWIGLU, d = 64, hidden = 256, io TTT_BF16, chunk a multiple of 64 that
+ *       divides T; flags from TTT_W0_PER_SEQ | TTT_LACT_READ_BEFORE; ln_eps and gelu ignored
+ *       (anything else: TTT_ERR_UNSUPPORTED or TTT_ERR_ARG).
+ *  Q, K, V, Z [B,H,T,d] bf16; eta [B,H,T] fp32; W0 [H,..] or [B,H,..] (TTT_W0_PER_SEQ);
+ *  W_T (nullable) [B,H,..], the weights after the last chunk.
+ *  workspace: ttt_workspace_size(.., TTT_OP_LACT, ..) bytes (status word, then two weight
+ *  buffers and the W2 column sums of every head, about 385 KiB per (batch, head)).
+ *  Runs one launch per chunk (plus one) of the kernel "ttt_lact_fwd_d64" (bf16 MFMA
+ *  products, fp32 weights and sums) and a copy-out for W_T. Errors as for ttt_scan_fwd;
+ *  a non-finite weight norm sets TTT_ERR_NONFINITE in the status word. */
+ttt_status ttt_lact_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const ttt_swiglu_weights* W0, void* Z,
+                        const ttt_swiglu_weights* W_T, void* workspace, size_t ws_bytes,
+                        void* stream);
 
 /* Synchronises `stream`, then reads the workspace status word: TTT_OK,
  * TTT_ERR_TIMEOUT if a forward launch of cooperating workgroups (the paired d = 64 or the

@@ -56,6 +56,21 @@ ttt_status check_common(const ttt_config* c, bool need_T) {
 
 int hidden_of(const ttt_config* c) { return c->kind == TTT_MLP ? c->hidden : c->d; }
 
+// Configuration check of the large-chunk SwiGLU layer (ttt_lact_fwd), host only.
+ttt_status check_lact(const ttt_config* c) {
+  if (!c) return TTT_ERR_NULL;
+  if (c->kind != TTT_SWIGLU) return TTT_ERR_UNSUPPORTED;
+  if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16) return TTT_ERR_DTYPE;
+  if (c->flags & ~(TTT_W0_PER_SEQ | TTT_LACT_READ_BEFORE)) return TTT_ERR_ARG;
+  if (c->B < 1 || c->H < 1 || c->T < 1 || c->d < 1 || c->hidden < 1 || c->chunk < 1) return TTT_ERR_SHAPE;
+  if (c->T % c->chunk != 0) return TTT_ERR_SHAPE;
+  if (!std::isfinite(c->eta_scale)) return TTT_ERR_ARG;
+  // one launch holds a block per (head rounded up to 8, up to 1024 tokens of a chunk)
+  if (static_cast<double>(c->B) * c->H > (1 << 24)) return TTT_ERR_SHAPE;
+  if (!lact_supported(c->d, c->hidden, c->io_dtype, c->chunk)) return TTT_ERR_UNSUPPORTED;
+  return TTT_OK;
+}
+
 size_t weights_per_head(const ttt_config* c) { return n_weights(c->kind, c->d, hidden_of(c)); }
 
 ScanParams scan_params(const ttt_config* c) {
@@ -214,7 +229,47 @@ const char* ttt_status_str(ttt_status s) {
   return "unknown status";
 }
 
-ttt_status ttt_validate(const ttt_config* cfg) { return check_common(cfg, true); }
+ttt_status ttt_validate(const ttt_config* cfg) {
+  return (cfg && cfg->kind == TTT_SWIGLU) ? check_lact(cfg) : check_common(cfg, true);
+}
+
+ttt_status ttt_lact_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
+                        const float* eta, const ttt_swiglu_weights* W0, void* Z,
+                        const ttt_swiglu_weights* W_T, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  ttt_status st = check_lact(cfg);
+  if (st != TTT_OK) return st;
+  if (!Q || !K || !V || !eta || !W0 || !W0->w1 || !W0->w2 || !W0->w3 || !Z) return TTT_ERR_NULL;
+  if (W_T && (!W_T->w1 || !W_T->w2 || !W_T->w3)) return TTT_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, eta, W0->w1, W0->w2, W0->w3, Z};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+  if (W_T && (!aligned16(W_T->w1) || !aligned16(W_T->w2) || !aligned16(W_T->w3))) return TTT_ERR_ALIGN;
+  if (!workspace) return TTT_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+  if (ws_bytes < kStatusBytes + lact_workspace_bytes(cfg->B * cfg->H)) return TTT_ERR_WORKSPACE;
+  LactLaunch L{};
+  L.B = cfg->B;
+  L.H = cfg->H;
+  L.T = cfg->T;
+  L.chunk = cfg->chunk;
+  L.flags = cfg->flags;
+  L.eta_scale = cfg->eta_scale;
+  L.Q = Q;
+  L.K = K;
+  L.V = V;
+  L.eta = eta;
+  L.w0_1 = W0->w1;
+  L.w0_2 = W0->w2;
+  L.w0_3 = W0->w3;
+  L.Z = Z;
+  L.wt_1 = W_T ? W_T->w1 : nullptr;
+  L.wt_2 = W_T ? W_T->w2 : nullptr;
+  L.wt_3 = W_T ? W_T->w3 : nullptr;
+  L.status = static_cast<unsigned*>(workspace);
+  L.work = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
+  return map_hip(launch_lact_fwd(L, static_cast<hipStream_t>(stream)));
+}
 
 bool use_mom(const ttt_config* c) {
   if (!tuned_allowed(c)) return false;
@@ -230,6 +285,12 @@ size_t fwd_momentum_ws_bytes(const ttt_config* c) {
 
 ttt_status ttt_workspace_size(const ttt_config* cfg, int32_t op, size_t* bytes) {
   if (!bytes) return TTT_ERR_NULL;
+  if (op == TTT_OP_LACT) {
+    const ttt_status sl = check_lact(cfg);
+    if (sl != TTT_OK) return sl;
+    *bytes = kStatusBytes + lact_workspace_bytes(cfg->B * cfg->H);
+    return TTT_OK;
+  }
   const bool need_T = op != TTT_OP_DECODE;
   ttt_status st = check_common(cfg, need_T);
   if (st != TTT_OK) return st;

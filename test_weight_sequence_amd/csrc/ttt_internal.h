@@ -108,6 +108,28 @@ size_t fwd_pair_workspace_bytes(int nheads);
 int fwd_pair_blocks(int nheads);
 bool fwd_pair_fits(int nheads);
 hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t s);
+// The large-chunk SwiGLU layer (ttt_lact_fwd), MLP-like d = 64, hidden = 256, bf16 I/O.
+struct LactLaunch {
+  int B, H, T, chunk, flags;
+  float eta_scale;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* eta;
+  const float* w0_1;
+  const float* w0_2;
+  const float* w0_3;
+  void* Z;
+  float* wt_1;  // nullable (then wt_2, wt_3 unused)
+  float* wt_2;
+  float* wt_3;
+  unsigned* status;
+  float* work;  // lact_workspace_bytes(B * H), 16-byte aligned
+};
+bool lact_supported(int d, int hid, int io, int chunk);
+size_t lact_workspace_bytes(int nheads);
+hipError_t launch_lact_fwd(const LactLaunch& L, hipStream_t s);
+
 // The key-side output rule (TTT_OUTPUT_KEY) on the same head shape, 16-token mini-batches:
 // the paired kernel's producer alone, one workgroup per head, no workspace.
 bool fwd_key_supported(const ScanParams& p);

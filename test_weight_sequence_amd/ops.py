@@ -4,7 +4,7 @@ Every step of the scan runs in the HIP library; torch is used here only to alloc
 device memory and to obtain the current HIP stream. If libttt.so is missing or
 cannot be loaded, every entry point raises: there is no fallback path.
 
-Names mirror include/ttt.h: scan_fwd, scan_fwd_momentum, scan_bwd, decode_step, validate,
+Names mirror include/ttt.h: scan_fwd, scan_fwd_momentum, scan_bwd, decode_step, lact_fwd, validate,
 workspace_size, saved_size, read_status, reset_status, fwd_kernel_name, bwd_kernel_name,
 decode_kernel_name.
 """
@@ -18,13 +18,14 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
 
-TTT_LINEAR, TTT_MLP = 0, 1
+TTT_LINEAR, TTT_MLP, TTT_SWIGLU = 0, 1, 2
 TTT_F32, TTT_BF16 = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
 TTT_W0_PER_SEQ, TTT_FORCE_GENERIC, TTT_ONE_WG_PER_HEAD, TTT_OUTPUT_KEY = 1, 2, 4, 8
 TTT_FORCE_DEVICE_SCOPE = 16
 TTT_DECODE_SPLIT = 32
-TTT_OP_FWD, TTT_OP_BWD, TTT_OP_DECODE, TTT_OP_FWD_MOMENTUM = 0, 1, 2, 3
+TTT_LACT_READ_BEFORE = 64
+TTT_OP_FWD, TTT_OP_BWD, TTT_OP_DECODE, TTT_OP_FWD_MOMENTUM, TTT_OP_LACT = 0, 1, 2, 3, 4
 
 STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE",
           4: "TTT_ERR_UNSUPPORTED", 5: "TTT_ERR_ALIGN", 6: "TTT_ERR_WORKSPACE",
@@ -33,7 +34,7 @@ STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE"
 
 EXPORTS = ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd", "ttt_scan_fwd_static",
            "ttt_scan_fwd_momentum",
-           "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
+           "ttt_scan_bwd", "ttt_decode_step", "ttt_lact_fwd", "ttt_read_status", "ttt_reset_status",
            "ttt_fwd_kernel_name", "ttt_fwd_momentum_kernel_name", "ttt_bwd_kernel_name",
            "ttt_decode_kernel_name", "ttt_status_str",
            "ttt_abi_version")
@@ -55,6 +56,10 @@ class CConfig(ctypes.Structure):
 
 class CWeights(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
+class CSwiGLUWeights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w3", ctypes.c_void_p)]
 
 
 _lib = None
@@ -79,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_scan_fwd_momentum.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, wp, P, wp, wp, P, P, S, P]
         L.ttt_scan_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, P, P, P, P, wp, P, P, P, S, P]
         L.ttt_decode_step.argtypes = [cfgp, P, P, P, P, P, P, wp, wp, I32, P, P, S, P]
+        sp = ctypes.POINTER(CSwiGLUWeights)
+        L.ttt_lact_fwd.argtypes = [cfgp, P, P, P, P, sp, P, sp, P, S, P]
         L.ttt_read_status.argtypes = [P, P]
         L.ttt_reset_status.argtypes = [P, P]
         L.ttt_fwd_kernel_name.argtypes = [cfgp]
@@ -93,8 +100,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_status_str.restype = ctypes.c_char_p
         for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
                      "ttt_scan_fwd_static", "ttt_scan_fwd_momentum",
-                     "ttt_scan_bwd", "ttt_decode_step", "ttt_read_status", "ttt_reset_status",
-                     "ttt_abi_version"):
+                     "ttt_scan_bwd", "ttt_decode_step", "ttt_lact_fwd", "ttt_read_status",
+                     "ttt_reset_status", "ttt_abi_version"):
             getattr(L, name).restype = I32
         _lib = L
     return _lib
@@ -102,7 +109,7 @@ def lib() -> ctypes.CDLL:
 
 @dataclass(frozen=True)
 class Config:
-    kind: str = "mlp"          # "mlp" | "linear"
+    kind: str = "mlp"          # "mlp" | "linear" | "swiglu" (the large-chunk layer, lact_fwd)
     B: int = 1
     H: int = 1
     T: int = 16
@@ -117,6 +124,7 @@ class Config:
     output_key: bool = False       # Eq. 9 output rule: z_t = f(K_t; W at the chunk start)
     device_scope: bool = False     # tuned forward: device-scope hand-offs between workgroups
     decode_split: bool = False     # decode: four workgroups per head (MLP d = 64)
+    read_before: bool = False      # lact_fwd: read a chunk out with its start weights
     ln_eps: float = 1e-6
     eta_scale: float = 1.0
 
@@ -126,9 +134,11 @@ class Config:
                 (TTT_ONE_WG_PER_HEAD if self.one_wg_per_head else 0) | \
                 (TTT_OUTPUT_KEY if self.output_key else 0) | \
                 (TTT_FORCE_DEVICE_SCOPE if self.device_scope else 0) | \
-                (TTT_DECODE_SPLIT if self.decode_split else 0)
-        return CConfig(TTT_MLP if self.kind == "mlp" else TTT_LINEAR, self.B, self.H, self.T,
-                       self.d, self.hidden if self.kind == "mlp" else self.d, self.chunk,
+                (TTT_DECODE_SPLIT if self.decode_split else 0) | \
+                (TTT_LACT_READ_BEFORE if self.read_before else 0)
+        kind = {"mlp": TTT_MLP, "linear": TTT_LINEAR, "swiglu": TTT_SWIGLU}[self.kind]
+        return CConfig(kind, self.B, self.H, self.T,
+                       self.d, self.d if self.kind == "linear" else self.hidden, self.chunk,
                        TTT_BF16 if self.io == "bf16" else TTT_F32,
                        TTT_GELU_TANH if self.gelu == "tanh" else TTT_GELU_ERF, flags,
                        float(self.ln_eps), float(self.eta_scale))
@@ -138,6 +148,8 @@ class Config:
         return torch.bfloat16 if self.io == "bf16" else torch.float32
 
     def weight_shapes(self, lead: tuple) -> list:
+        if self.kind == "swiglu":
+            return [(*lead, self.d, self.hidden), (*lead, self.hidden, self.d), (*lead, self.d, self.hidden)]
         if self.kind == "mlp":
             return [(*lead, self.d, self.hidden), (*lead, self.hidden, self.d)]
         return [(*lead, self.d, self.d)]
@@ -312,3 +324,22 @@ def decode_step(cfg: Config, q, k, v, eta, gamma, beta, W_start, acc, pos_in_chu
                                  _stream(stream))
     _check(code, "ttt_decode_step")
     return z
+
+
+def lact_fwd(cfg: Config, Q, K, V, eta, W0, *, want_wt=True, workspace=None, out=None,
+             stream=None) -> dict:
+    """The large-chunk SwiGLU layer (ttt_lact_fwd). Q, K, V [B,H,T,d] bf16, eta [B,H,T] fp32,
+    W0 = (W1, W2, W3) fp32 ([H,...] or [B,H,...] with w0_per_seq). Returns Z and W_T."""
+    lead = (cfg.B, cfg.H)
+    dev = Q.device
+    Z = out if out is not None else torch.empty(*lead, cfg.T, cfg.d, dtype=cfg.io_dtype, device=dev)
+    WT = tuple(torch.empty(s, dtype=torch.float32, device=dev) for s in cfg.weight_shapes(lead)) \
+        if want_wt else None
+    ws = workspace if workspace is not None else new_workspace(cfg, TTT_OP_LACT, dev)
+    w0 = CSwiGLUWeights(W0[0].data_ptr(), W0[1].data_ptr(), W0[2].data_ptr())
+    wt = CSwiGLUWeights(WT[0].data_ptr(), WT[1].data_ptr(), WT[2].data_ptr()) if WT else None
+    code = lib().ttt_lact_fwd(ctypes.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(eta),
+                              ctypes.byref(w0), _ptr(Z), ctypes.byref(wt) if wt else None,
+                              _ptr(ws), ws.numel(), _stream(stream))
+    _check(code, "ttt_lact_fwd")
+    return {"Z": Z, "W_T": WT, "workspace": ws}

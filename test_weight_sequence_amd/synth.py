@@ -22,7 +22,7 @@ _TENSOR_CODE = {"Q": 0, "K": 1, "V": 2, "u": 3, "W0": 4, "dZ": 5, "u_mom": 6, "u
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str          # "mlp" or "linear"
+    kind: str          # "mlp", "linear" or "swiglu" (the large-chunk SwiGLU layer)
     B: int
     H: int
     T: int
@@ -31,7 +31,8 @@ class Workload:
     chunk: int
     io: str            # "f32" or "bf16" for Q, K, V, Z
     eta_base: float    # eta_t = eta_base * sigmoid(u_t), u_t ~ N(0, 1)
-    w0: str            # "normal": N(0, 0.02^2); "identity_plus": I + N(0, 0.02^2)
+    w0: str            # "normal": N(0, 0.02^2); "identity_plus": I + N(0, 0.02^2);
+                       # "fan_in": entries N(0, 1/inputs) (the SwiGLU layer's W1, W2, W3)
     drift: float = 0.0  # AR(1) coefficient along tokens (0 = i.i.d.)
     seed: int = 0
 
@@ -64,6 +65,9 @@ WORKLOADS = {
                 "normal", seed=1003),
     "ttt_mlp_bf16_d64_T8k_b1024": Workload("ttt_mlp_bf16_d64_T8k_b1024", "mlp", 8, 12, 8192, 64, 256, 1024, "bf16",
                 0.1, "normal", seed=1003),
+    # the large-chunk SwiGLU layer at the same head shape and token count, chunks of 2048
+    "lact_swiglu_bf16_d64_T8k_b2048": Workload("lact_swiglu_bf16_d64_T8k_b2048", "swiglu", 8, 12, 8192, 64, 256,
+                2048, "bf16", 1.0, "fan_in", seed=1006),
 }
 
 
@@ -124,7 +128,14 @@ def make_inputs(w: Workload, batch_idx=None, head_idx=None, T: int | None = None
             u = _rng(w.seed, "u", b, h).standard_normal(T)
             eta[i, j] = w.eta_base / (1.0 + np.exp(-u))
     out["eta"] = torch.from_numpy(eta).to(torch.float32)
-    if w.kind == "mlp":
+    if w.kind == "swiglu":
+        # W1, W3 [d, hidden] with N(0, 1/d) entries, W2 [hidden, d] with N(0, 1/hidden)
+        Ws = [np.empty((len(hi), d, hid)), np.empty((len(hi), hid, d)), np.empty((len(hi), d, hid))]
+        for j, h in enumerate(hi):
+            for k, (shape, fan) in enumerate((((d, hid), d), ((hid, d), hid), ((d, hid), d))):
+                Ws[k][j] = _rng(w.seed, "W0", h, k).standard_normal(shape) * math.sqrt(1.0 / fan)
+        out["W0"] = tuple(torch.from_numpy(x).float() for x in Ws)
+    elif w.kind == "mlp":
         W1 = np.empty((len(hi), d, hid))
         W2 = np.empty((len(hi), hid, d))
         for j, h in enumerate(hi):

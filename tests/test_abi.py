@@ -267,3 +267,27 @@ def test_static_fwd_checks_before_launch():
     assert call(big) == 6                                 # TTT_ERR_WORKSPACE
     # the paired kernel's largest launch (128 heads) fits
     assert ops.workspace_size(mlp_d64(B=8, H=16)) <= 16 << 20
+
+
+def test_lact_configuration_checks():
+    """The large-chunk SwiGLU layer's host checks (ttt_validate and its workspace size)."""
+    cfg = ops.Config(kind="swiglu", B=2, H=3, T=256, d=64, hidden=256, chunk=64)
+    assert ops.validate(cfg) == 0
+    heads = 6
+    assert ops.workspace_size(cfg, ops.TTT_OP_LACT) == 256 + heads * (2 * 3 * 64 * 256 + 2 * 2 * 64) * 4
+    bad = lambda **kw: ops.validate(ops.Config(**{**cfg.__dict__, **kw}))
+    assert bad(chunk=48, T=240) == 4               # chunk not a multiple of 64
+    assert bad(T=250) == 2                         # T not a multiple of chunk
+    assert bad(io="f32") == 4
+    assert bad(d=128, hidden=512) == 4
+    assert bad(hidden=128) == 4
+    assert bad(force_generic=True) == 9            # not a flag of this layer
+    assert bad(eta_scale=float("nan")) == 9
+    assert bad(read_before=True, w0_per_seq=True) == 0
+    # the other entry points do not take this kind, and this op does not take theirs
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(cfg, ops.TTT_OP_FWD)
+    with pytest.raises(ops.TTTError):
+        ops.workspace_size(mlp_d64(), ops.TTT_OP_LACT)
+    assert ops.fwd_kernel_name(cfg) == ""
+    assert ops.validate(mlp_d64(read_before=True)) == 9
