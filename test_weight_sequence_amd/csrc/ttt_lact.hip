@@ -19,7 +19,7 @@
 //    256 hidden units) spans both blocks of a head, so W2 is stored unnormalised together with
 //    each block's partial sum of squares per column; every reader scales W2 by
 //    1 / sqrt(the sum of the two partials) as it loads it.
-//  - read-out blocks, one per (head, up to 1024 tokens of a chunk): the weights as bf16 MFMA
+//  - read-out blocks, one per (head, up to 512 tokens of a chunk): the weights as bf16 MFMA
 //    operands in LDS (96 KiB), each of the 8 waves computing z for 64 tokens at a time:
 //      A^Q^T = W1^T Q^T, C^Q^T = W3^T Q^T, U^T = SiLU(A^Q^T) C^Q^T, z^T = W2^T U^T.
 // The weights live in two state buffers of the workspace: the step that runs the gradient of
@@ -39,15 +39,16 @@ constexpr int NT = NW * 64;
 constexpr int NHB = 2;           // gradient blocks per head
 constexpr int HB = LH / NHB;     // hidden units per gradient block
 constexpr int GT = HB / 16 / NW; // 16-unit hidden tiles per gradient wave
-constexpr int SS = 32;           // tokens per step
+constexpr int SS = 32;           // tokens per gradient step
+constexpr int ST = 128;          // tokens staged per barrier (64 when the chunk is not a multiple)
 constexpr int KRS = D + 8;       // LDS row stride of staged K / V rows (bf16)
 constexpr int W_FLOATS = 3 * D * LH;  // W1, W3 [d][h] then W2 [h][d], fp32
 constexpr int OR = 64;           // tokens per read-out round of a wave
 
 struct GStage {
-  alignas(16) __bf16 K[SS * KRS];
-  alignas(16) __bf16 V[SS * KRS];
-  float eta[SS];
+  alignas(16) __bf16 K[ST * KRS];
+  alignas(16) __bf16 V[ST * KRS];
+  float eta[ST];
 };
 struct GSmem {
   GStage st[2];
@@ -132,18 +133,41 @@ __device__ __forceinline__ void xcd_map(int b, int per_head, int& head, int& sub
 // ---------------------------------------------------------------------------------------
 // gradient role
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void g_load(const LactParams& p, size_t tok0, int ss, int tid, uint4& kq,
-                                       float& e) {
-  // threads 0..255 stage K, 256..511 V: 32 rows x 8 16-byte pieces each
-  const int row = (tid & 255) >> 3, col = (tid & 7) * 8;
-  const size_t off = (tok0 + static_cast<size_t>(ss) * SS + row) * D + col;
-  kq = *reinterpret_cast<const uint4*>((tid < 256 ? p.K : p.V) + off);
-  e = tid < SS ? p.eta[tok0 + static_cast<size_t>(ss) * SS + tid] * p.eta_scale : 0.f;
+// Staging of `rows` tokens (64 or 128) of K and V (rows x 8 16-byte pieces each) and eta: two
+// or four pieces per thread, all loads issued before any is used.
+struct GLoad {
+  uint4 q0, q1, q2, q3;
+  float e;
+};
+__device__ __forceinline__ const __bf16* g_src(const LactParams& p, size_t tok0, int n, int idx) {
+  const int k = idx < n ? idx : idx - n;
+  return (idx < n ? p.K : p.V) + (tok0 + (k >> 3)) * D + (k & 7) * 8;
 }
-__device__ __forceinline__ void g_store(GStage& st, int tid, const uint4& kq, float e) {
-  const int row = (tid & 255) >> 3, col = (tid & 7) * 8;
-  *reinterpret_cast<uint4*>(&(tid < 256 ? st.K : st.V)[row * KRS + col]) = kq;
-  if (tid < SS) st.eta[tid] = e;
+__device__ __forceinline__ __bf16* g_dst(GStage& st, int n, int idx) {
+  const int k = idx < n ? idx : idx - n;
+  return &(idx < n ? st.K : st.V)[(k >> 3) * KRS + (k & 7) * 8];
+}
+__device__ __forceinline__ GLoad g_load(const LactParams& p, size_t tok0, int rows, int tid) {
+  const int n = rows * 8;  // 512 or 1024 pieces per tensor
+  GLoad l;
+  l.q0 = *reinterpret_cast<const uint4*>(g_src(p, tok0, n, tid));
+  l.q1 = *reinterpret_cast<const uint4*>(g_src(p, tok0, n, NT + tid));
+  if (rows == ST) {
+    l.q2 = *reinterpret_cast<const uint4*>(g_src(p, tok0, n, 2 * NT + tid));
+    l.q3 = *reinterpret_cast<const uint4*>(g_src(p, tok0, n, 3 * NT + tid));
+  }
+  l.e = tid < rows ? p.eta[tok0 + tid] * p.eta_scale : 0.f;
+  return l;
+}
+__device__ __forceinline__ void g_store(GStage& st, int rows, int tid, const GLoad& l) {
+  const int n = rows * 8;
+  *reinterpret_cast<uint4*>(g_dst(st, n, tid)) = l.q0;
+  *reinterpret_cast<uint4*>(g_dst(st, n, NT + tid)) = l.q1;
+  if (rows == ST) {
+    *reinterpret_cast<uint4*>(g_dst(st, n, 2 * NT + tid)) = l.q2;
+    *reinterpret_cast<uint4*>(g_dst(st, n, 3 * NT + tid)) = l.q3;
+  }
+  if (tid < rows) st.eta[tid] = l.e;
 }
 
 __device__ void g_role(const LactParams& p, int head, int hb, LSmem& sm) {
@@ -154,10 +178,10 @@ __device__ void g_role(const LactParams& p, int head, int hb, LSmem& sm) {
   const WRef in = wref(p, c, head);
   GSmem& S = sm.g;
   if (tid < D) S.scale[tid] = col_scale(in, tid);
-  uint4 kq;
-  float eq;
-  g_load(p, tok0, 0, tid, kq, eq);
-  g_store(S.st[0], tid, kq, eq);
+  const int rows = p.chunk % ST == 0 ? ST : ST / 2;  // tokens per stage
+  const int nst = p.chunk / rows;
+  GLoad ld = g_load(p, tok0, rows, tid);
+  g_store(S.st[0], rows, tid, ld);
   __syncthreads();
 
   // B operands [k = d, n = h]: lane (g, c16) holds d = 32 ks + 8 g + j of hidden unit
@@ -192,14 +216,8 @@ __device__ void g_role(const LactParams& p, int head, int hb, LSmem& sm) {
       gW2[j][i] = zero4();
     }
 
-  const int nss = p.chunk / SS;
-  for (int ss = 0; ss < nss; ++ss) {
-    const GStage& st = S.st[ss & 1];
-    if (ss + 1 < nss) g_load(p, tok0, ss + 1, tid, kq, eq);
-    const __bf16* Kt = st.K;
-    const __bf16* Vt = st.V;
-    const float* et = st.eta;
-    bf16x4 gAb[2][GT], gCb[2][GT], ueb[2][GT];
+  // K W1, K W3 and V W2^T of one 32-token sub-step: [token][this wave's hidden units] tiles
+  auto fwd = [&](const __bf16* Kt, const __bf16* Vt, f4 (&A)[2][GT], f4 (&C)[2][GT], f4 (&P)[2][GT]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       bf16x8 kr[2], vr[2];
@@ -208,43 +226,74 @@ __device__ void g_role(const LactParams& p, int head, int hb, LSmem& sm) {
         kr[ks] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * tt + c16) * KRS + 32 * ks + 8 * g]);
         vr[ks] = *reinterpret_cast<const bf16x8*>(&Vt[(16 * tt + c16) * KRS + 32 * ks + 8 * g]);
       }
-      float e[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) e[r] = et[16 * tt + 4 * g + r];
 #pragma unroll
       for (int ht = 0; ht < GT; ++ht) {
-        const f4 A = mfma32(kr[1], W1B[ht][1], mfma32(kr[0], W1B[ht][0], zero4()));
-        const f4 C = mfma32(kr[1], W3B[ht][1], mfma32(kr[0], W3B[ht][0], zero4()));
-        const f4 P = mfma32(vr[1], W2B[ht][1], mfma32(vr[0], W2B[ht][0], zero4()));
-        f4 ga, gc, ue;
+        A[tt][ht] = mfma32(kr[1], W1B[ht][1], mfma32(kr[0], W1B[ht][0], zero4()));
+        C[tt][ht] = mfma32(kr[1], W3B[ht][1], mfma32(kr[0], W3B[ht][0], zero4()));
+        P[tt][ht] = mfma32(vr[1], W2B[ht][1], mfma32(vr[0], W2B[ht][0], zero4()));
+      }
+    }
+  };
+  for (int sg = 0; sg < nst; ++sg) {
+    const GStage& st = S.st[sg & 1];
+    if (sg + 1 < nst) ld = g_load(p, tok0 + static_cast<size_t>(sg + 1) * rows, rows, tid);
+    // the forward products of sub-step s + 1 are issued before the element-wise work and the
+    // gradient sums of sub-step s, which do not depend on them
+    const int nsub = rows / SS;
+    f4 A[2][GT], C[2][GT], P[2][GT];
+    fwd(st.K, st.V, A, C, P);
+    for (int sub = 0; sub < nsub; ++sub) {
+      const __bf16* Kt = st.K + sub * SS * KRS;
+      const __bf16* Vt = st.V + sub * SS * KRS;
+      const float* et = st.eta + sub * SS;
+      f4 A2[2][GT], C2[2][GT], P2[2][GT];
+      if (sub + 1 < nsub) fwd(Kt + SS * KRS, Vt + SS * KRS, A2, C2, P2);
+      bf16x4 gAb[2][GT], gCb[2][GT], ueb[2][GT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = A[r], cc = C[r];
-          const float sg = sigmoid(a);
-          const float si = a * sg;
-          const float gu = -e[r] * P[r];
-          ga[r] = gu * cc * (sg + si * (1.f - sg));
-          gc[r] = gu * si;
-          ue[r] = -e[r] * si * cc;
+      for (int tt = 0; tt < 2; ++tt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = et[16 * tt + 4 * g + r];
+#pragma unroll
+        for (int ht = 0; ht < GT; ++ht) {
+          f4 ga, gc, ue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = A[tt][ht][r], cc = C[tt][ht][r];
+            const float sg = sigmoid(a);
+            const float si = a * sg;
+            const float gu = -e[r] * P[tt][ht][r];
+            ga[r] = gu * cc * (sg + si * (1.f - sg));
+            gc[r] = gu * si;
+            ue[r] = -e[r] * si * cc;
+          }
+          gAb[tt][ht] = cvt4(ga);
+          gCb[tt][ht] = cvt4(gc);
+          ueb[tt][ht] = cvt4(ue);
         }
-        gAb[tt][ht] = cvt4(ga);
-        gCb[tt][ht] = cvt4(gc);
-        ueb[tt][ht] = cvt4(ue);
       }
-    }
-    // sums over the 32 tokens (k = token: the two 16-token tiles stacked)
+      // sums over the 32 tokens (k = token: the two 16-token tiles stacked)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const bf16x8 KT = cat(tgroup(Kt, KRS, dt, g, c16), tgroup(Kt + 16 * KRS, KRS, dt, g, c16));
-      const bf16x8 VT = cat(tgroup(Vt, KRS, dt, g, c16), tgroup(Vt + 16 * KRS, KRS, dt, g, c16));
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 KT = cat(tgroup(Kt, KRS, dt, g, c16), tgroup(Kt + 16 * KRS, KRS, dt, g, c16));
+        const bf16x8 VT = cat(tgroup(Vt, KRS, dt, g, c16), tgroup(Vt + 16 * KRS, KRS, dt, g, c16));
 #pragma unroll
-      for (int ht = 0; ht < GT; ++ht) {
-        gW1[dt][ht] = mfma32(KT, cat(gAb[0][ht], gAb[1][ht]), gW1[dt][ht]);
-        gW3[dt][ht] = mfma32(KT, cat(gCb[0][ht], gCb[1][ht]), gW3[dt][ht]);
-        gW2[ht][dt] = mfma32(cat(ueb[0][ht], ueb[1][ht]), VT, gW2[ht][dt]);
+        for (int ht = 0; ht < GT; ++ht) {
+          gW1[dt][ht] = mfma32(KT, cat(gAb[0][ht], gAb[1][ht]), gW1[dt][ht]);
+          gW3[dt][ht] = mfma32(KT, cat(gCb[0][ht], gCb[1][ht]), gW3[dt][ht]);
+          gW2[ht][dt] = mfma32(cat(ueb[0][ht], ueb[1][ht]), VT, gW2[ht][dt]);
+        }
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int ht = 0; ht < GT; ++ht) {
+          A[tt][ht] = A2[tt][ht];
+          C[tt][ht] = C2[tt][ht];
+          P[tt][ht] = P2[tt][ht];
+        }
     }
-    if (ss + 1 < nss) g_store(S.st[(ss + 1) & 1], tid, kq, eq);
+    if (sg + 1 < nst) g_store(S.st[(sg + 1) & 1], rows, tid, ld);
     __syncthreads();
   }
 
@@ -328,47 +377,41 @@ __device__ void o_role(const LactParams& p, int head, int tb, LSmem& sm) {
   // operand tiles: W1^T / W3^T [m = h, k = d]: lane (g, c16) holds h = 16 ht + c16,
   // d = 32 ks + 8 g + j; W2^T [m = d, k = h]: lane holds d = 16 dt + c16 and, for the pair of h
   // tiles 2 q and 2 q + 1, h = 32 q + 4 g + j (j < 4) and 32 q + 16 + 4 g + (j - 4).
-  // Filled from coalesced float4 rows (four consecutive h of W1 / W3, four consecutive d of
-  // W2), each value written to its slot of four operand tiles; all loads are issued first.
+  // Each thread gathers eight float4s (eight d rows of four hidden units of W1 / W3; eight h
+  // rows of four output units of W2, coalesced across threads) and writes four whole tiles'
+  // slots (16 bytes each).
   {
-    __bf16* w1s = reinterpret_cast<__bf16*>(&S.w1[0][0][0]);
-    __bf16* w3s = reinterpret_cast<__bf16*>(&S.w3[0][0][0]);
-    __bf16* w2s = reinterpret_cast<__bf16*>(&S.w2[0][0][0]);
-    constexpr int NQ = D * LH / 4 / NT;  // float4s per thread per matrix
-    float4 a[NQ], b[NQ], c2[NQ];
+    const int o8 = tid >> 6, q64 = tid & 63;  // W1 / W3: d = 8 o8 + j, h = 4 q64 + u
+    float4 a[8], b[8];
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int f = i * NT + tid;  // float4 index in a [64][256] or [256][64] matrix
-      a[i] = reinterpret_cast<const float4*>(in.w1)[f];
-      b[i] = reinterpret_cast<const float4*>(in.w3)[f];
-      c2[i] = reinterpret_cast<const float4*>(in.w2)[f];
+    for (int j = 0; j < 8; ++j) {
+      a[j] = *reinterpret_cast<const float4*>(in.w1 + (8 * o8 + j) * LH + 4 * q64);
+      b[j] = *reinterpret_cast<const float4*>(in.w3 + (8 * o8 + j) * LH + 4 * q64);
+    }
+    const int q = tid >> 6, lg = (tid >> 4) & 3, dq = tid & 15;  // W2: h_j of (q, lg), d = 4 dq + u
+    float4 c2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int h = 32 * q + (j < 4 ? 4 * lg + j : 16 + 4 * lg + (j - 4));
+      c2[j] = *reinterpret_cast<const float4*>(in.w2 + h * D + 4 * dq);
     }
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int f = i * NT + tid;
-      {  // W1 / W3 row d, hidden units h .. h + 3
-        const int d = f >> 6, h = (f & 63) * 4;
-        const int ks = d >> 5, lg = (d >> 3) & 3, j = d & 7;
-        const float va[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-        const float vb[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+    for (int u = 0; u < 4; ++u) {
+      const int h = 4 * q64 + u;
+      bf16x8 x, y, z;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int hh = h + u, ht = hh >> 4, lc = hh & 15;
-          const int slot = ((ht * 2 + ks) * 64 + lg * 16 + lc) * 8 + j;
-          w1s[slot] = (__bf16)va[u];
-          w3s[slot] = (__bf16)vb[u];
-        }
+      for (int j = 0; j < 8; ++j) {
+        x[j] = (__bf16)(u == 0 ? a[j].x : u == 1 ? a[j].y : u == 2 ? a[j].z : a[j].w);
+        y[j] = (__bf16)(u == 0 ? b[j].x : u == 1 ? b[j].y : u == 2 ? b[j].z : b[j].w);
       }
-      {  // W2 row h, output units d .. d + 3
-        const int h = f >> 4, d = (f & 15) * 4;
-        const int q = h >> 5, hi = (h >> 4) & 1, lg = (h >> 2) & 3, j = (h & 3) + 4 * hi;
-        const float vc[4] = {c2[i].x, c2[i].y, c2[i].z, c2[i].w};
+      S.w1[h >> 4][o8 >> 2][(o8 & 3) * 16 + (h & 15)] = x;
+      S.w3[h >> 4][o8 >> 2][(o8 & 3) * 16 + (h & 15)] = y;
+      const int d = 4 * dq + u;
+      const float sc = S.scale[d];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dd = d + u, dt = dd >> 4, lc = dd & 15;
-          w2s[((dt * 8 + q) * 64 + lg * 16 + lc) * 8 + j] = (__bf16)(vc[u] * S.scale[dd]);
-        }
-      }
+      for (int j = 0; j < 8; ++j)
+        z[j] = (__bf16)(sc * (u == 0 ? c2[j].x : u == 1 ? c2[j].y : u == 2 ? c2[j].z : c2[j].w));
+      S.w2[d >> 4][q][lg * 16 + (d & 15)] = z;
     }
   }
   __syncthreads();
@@ -456,9 +499,11 @@ __global__ void __launch_bounds__(256) lact_final_kernel(LactParams p, int k, fl
   reinterpret_cast<float4*>(wt2)[o] = v;
 }
 
+// Tokens per read-out block: the largest power-of-two multiple of 64 up to 512 that divides the
+// chunk (512 balances the read-out blocks against the gradient blocks they share a launch with)
 int read_tokens(int chunk) {
   int t = 64;
-  while (t < 1024 && chunk % (2 * t) == 0) t *= 2;
+  while (t < 512 && chunk % (2 * t) == 0) t *= 2;
   return t;
 }
 
