@@ -101,6 +101,38 @@ int main(void) {
   EXPECT(ttt_scan_fwd_momentum(&b, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), (float*)P(0x5000),
                                (float*)P(0x6000), (float*)P(0x7000), (float*)P(0x8000), &w, NULL, P(0x70000),
                                NULL, NULL, NULL, P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_UNSUPPORTED);
+  /* the large-chunk SwiGLU layer: its own kind, checks and workspace op */
+  {
+    ttt_config l = c;
+    l.kind = TTT_SWIGLU; l.chunk = 2048;
+    EXPECT(ttt_validate(&l), TTT_OK);
+    EXPECT(ttt_workspace_size(&l, TTT_OP_LACT, &n), TTT_OK);
+    if (n != 256 + (size_t)96 * (2 * 3 * 64 * 256 + 2 * 2 * 64) * 4) ++failures;
+    EXPECT(ttt_workspace_size(&l, TTT_OP_FWD, &n), TTT_ERR_UNSUPPORTED);
+    EXPECT(ttt_workspace_size(&c, TTT_OP_LACT, &n), TTT_ERR_UNSUPPORTED);
+    ttt_swiglu_weights w3 = {(float*)P(0x10000), (float*)P(0x20000), (float*)P(0x30000)};
+    ttt_swiglu_weights w3n = {(float*)P(0x10000), NULL, (float*)P(0x30000)};
+    /* every call below is rejected before anything is enqueued */
+    EXPECT(ttt_lact_fwd(&l, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3n, P(0x5000), NULL,
+                        P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_NULL);
+    EXPECT(ttt_lact_fwd(&l, P(0x1008), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_ALIGN);
+    EXPECT(ttt_lact_fwd(&l, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        P(0x90000), 4096, NULL), TTT_ERR_WORKSPACE);
+    EXPECT(ttt_lact_fwd(&l, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        NULL, (size_t)1 << 40, NULL), TTT_ERR_WORKSPACE);
+    EXPECT(ttt_lact_fwd(&c, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_UNSUPPORTED);
+    ttt_config lb = l; lb.flags = TTT_FORCE_GENERIC;
+    EXPECT(ttt_lact_fwd(&lb, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_ARG);
+    lb = l; lb.chunk = 96;
+    EXPECT(ttt_validate(&lb), TTT_ERR_SHAPE);
+    lb = l; lb.chunk = 48; lb.T = 96;
+    EXPECT(ttt_validate(&lb), TTT_ERR_UNSUPPORTED);
+    EXPECT(ttt_lact_fwd(NULL, P(0x1000), P(0x2000), P(0x3000), (float*)P(0x4000), &w3, P(0x5000), NULL,
+                        P(0x90000), (size_t)1 << 40, NULL), TTT_ERR_NULL);
+  }
   EXPECT(ttt_read_status(NULL, NULL), TTT_ERR_NULL);
   EXPECT(ttt_reset_status(NULL, NULL), TTT_ERR_NULL);
   if (failures) {
