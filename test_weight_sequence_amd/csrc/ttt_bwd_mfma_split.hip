@@ -107,7 +107,10 @@ __device__ __forceinline__ bf16x8 hcat(const bf16x4 (&x)[NHT], int ks) { return 
 
 // The chunk-start weights of one wave in the transposed tile orientations: W1^T tiles
 // (C[h][d]: lane holds W1[d][h .. h+3]) and W2^T tiles (C[d][h]: lane holds W2[h][d .. d+3]),
-// 16 contiguous bytes per lane per tile from the row-major saved copy.
+// 16 contiguous bytes per lane per tile from the row-major saved copy. Each part reads its own
+// hidden units once, so the loads are non-temporal (cache policy nt): the 4 GB stream of saved
+// weights then does not push the exchange areas' lines out of the L2.
+constexpr int kLoadNT = 2;
 __device__ __forceinline__ void wT_load(const float* w1, const float* w2, int g, int c16, int hs,
                                         f4 (&W1T)[NHT][NDT], f4 (&W2T)[NDT][NHT]) {
   const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w1), 0, D * HID * 4, kBufFlags);
@@ -117,8 +120,8 @@ __device__ __forceinline__ void wT_load(const float* w1, const float* w2, int g,
   for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      W1T[ht][dt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r1, v1, (16 * dt * HID + 16 * ht) * 4, 0));
-      W2T[dt][ht] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r2, v2, (16 * ht * D + 16 * dt) * 4, 0));
+      W1T[ht][dt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r1, v1, (16 * dt * HID + 16 * ht) * 4, kLoadNT));
+      W2T[dt][ht] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r2, v2, (16 * ht * D + 16 * dt) * 4, kLoadNT));
     }
 }
 
