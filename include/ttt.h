@@ -84,10 +84,10 @@ enum {
                              z_t = f(K_t; W) with W the weights the token's gradient is taken at
                              (the chunk start; W_{t-1} when chunk = 1), i.e. the key-side
                              prediction reused as the output. Q does not enter it (dQ = 0). The
-                             forward of MLP d = 64, hidden 256, bf16, chunk 16 runs it on a tuned
-                             kernel (the paired kernel's producer alone, one workgroup per head);
-                             backward, decode and every other shape run it on the portable
-                             kernels. */
+                             forward of MLP d = 64, hidden 256, bf16 (chunk 16, or a multiple of
+                             16 up to 1024) runs it on a tuned kernel (the paired kernel's
+                             producer alone, one workgroup per head); backward and decode (chunk
+                             up to 16) and every other shape run it on the portable kernels. */
   TTT_FORCE_DEVICE_SCOPE = 1 << 4 /* tuned kernels with several workgroups per head (forward,
                                      momentum forward, decode): they hand partial results
                                      to each other with device-scope atomics and fences even
@@ -271,8 +271,8 @@ ttt_status ttt_reset_status(void* workspace, void* stream);
  * only: "ttt_fwd_mfma_pair_d64" is chosen for the tuned shape when B*H <= 128 and
  * TTT_ONE_WG_PER_HEAD is not set; if the device then cannot hold all 2*ceil(B*H/8)*8
  * workgroups at once, ttt_scan_fwd launches "ttt_fwd_mfma_d64" instead. With TTT_OUTPUT_KEY the
- * tuned shape (chunk 16) takes "ttt_fwd_mfma_key_d64" (one workgroup per head, any head
- * count, workspace: the status word only). For MLP d = 128,
+ * tuned shape (chunk a multiple of 16 up to 1024) takes "ttt_fwd_mfma_key_d64" (one workgroup
+ * per head, any head count, workspace: the status word only). For MLP d = 128,
  * hidden = 512, chunk 16, bf16 I/O the name is "ttt_fwd_mfma_split_d128" (four workgroups per
  * head that wait for each other); ttt_scan_fwd launches it once per group of heads whose
  * workgroups the device holds at once (64 heads on a 256-CU device), and launches

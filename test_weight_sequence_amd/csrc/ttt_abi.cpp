@@ -22,11 +22,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Mini-batches above kMaxChunk tokens run on the paired d = 64 kernel only (forward scan and
 // decode): MLP, d = 64, hidden = 256, bf16 I/O, a multiple of 16 up to kMaxPairChunk tokens,
 // at most kPairMaxHeads (batch, head) pairs, and none of the flags that select another kernel.
+// With TTT_OUTPUT_KEY the forward runs the key-output kernel instead (one workgroup per head,
+// no head limit) and decode is not available.
 bool large_chunk_ok(const ttt_config* c) {
+  const bool key = (c->flags & TTT_OUTPUT_KEY) != 0;
   return c->kind == TTT_MLP && c->d == 64 && c->hidden == 256 && c->io_dtype == TTT_BF16 &&
          c->chunk % 16 == 0 && c->chunk <= kMaxPairChunk &&
-         !(c->flags & (TTT_FORCE_GENERIC | TTT_OUTPUT_KEY | TTT_ONE_WG_PER_HEAD)) &&
-         static_cast<long long>(c->B) * c->H <= kPairMaxHeads;
+         !(c->flags & TTT_FORCE_GENERIC) &&
+         (key || (!(c->flags & TTT_ONE_WG_PER_HEAD) && static_cast<long long>(c->B) * c->H <= kPairMaxHeads));
 }
 
 ttt_status check_common(const ttt_config* c, bool need_T) {
@@ -94,8 +97,8 @@ ScanParams scan_params(const ttt_config* c) {
 // forward (use_key) and otherwise runs on the portable kernels.
 bool tuned_allowed(const ttt_config* c) { return !(c->flags & (TTT_FORCE_GENERIC | TTT_OUTPUT_KEY)); }
 
-// Forward with the key-side output rule, MLP d = 64 bf16 chunk 16: the paired kernel's
-// producer alone, one workgroup per head (any number of heads).
+// Forward with the key-side output rule, MLP d = 64 bf16, chunk a multiple of 16 up to
+// kMaxPairChunk: the paired kernel's producer alone, one workgroup per head (any number of heads).
 bool use_key(const ttt_config* c) {
   if (c->flags & TTT_FORCE_GENERIC) return false;
   ScanParams p = scan_params(c);
@@ -341,6 +344,7 @@ const char* ttt_bwd_kernel_name(const ttt_config* cfg) {
 
 const char* ttt_decode_kernel_name(const ttt_config* cfg) {
   if (check_common(cfg, false) != TTT_OK) return "";
+  if (cfg->chunk > kMaxChunk && !use_decode_stream(cfg)) return "";  // not available
   if (use_decode_split(cfg)) return "ttt_decode_split_d64";
   return use_decode_stream(cfg) ? "ttt_decode_stream_d64" : "ttt_decode_generic";
 }

@@ -864,8 +864,9 @@ fwd_mfma_pair_kernel(ScanParams p, Pair q) {
 }
 
 // The key-side output rule: one workgroup per (batch, head) running the producer alone (its
-// hand-off code is compiled out, so the flags and ring are never touched).
-template <int GELU_KIND>
+// hand-off code is compiled out, so the flags and ring are never touched); LARGE for
+// mini-batches above 16 tokens, as in the paired kernel.
+template <int GELU_KIND, bool LARGE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_key_kernel(ScanParams p) {
   __shared__ ProdSmem sm;
@@ -880,7 +881,7 @@ fwd_mfma_key_kernel(ScanParams p) {
   x.hs = x.w * HS;
   x.T = p.T;
   x.nchunks = p.T / BC;
-  x.m = 1;
+  x.m = p.chunk / BC;
   x.flags = nullptr;
   x.ring = nullptr;
   const size_t io_off = static_cast<size_t>(x.head) * p.T * D;
@@ -888,7 +889,7 @@ fwd_mfma_key_kernel(ScanParams p) {
   x.Xg = static_cast<const __bf16*>(p.V) + io_off;
   x.Zg = static_cast<__bf16*>(p.Z) + io_off;
   x.etag = p.eta + static_cast<size_t>(x.head) * p.T;
-  producer_body<GELU_KIND, true, false, true>(p, x, sm);
+  producer_body<GELU_KIND, true, LARGE, true>(p, x, sm);
 }
 
 __global__ void pair_reset_kernel(unsigned* flags, int n) {
@@ -955,15 +956,23 @@ hipError_t launch_fwd_mfma_pair(const ScanParams& p, hipStream_t stream) {
 }
 
 bool fwd_key_supported(const ScanParams& p) {
-  return fwd_pair_supported(p) && p.chunk == BC && (p.flags & TTT_OUTPUT_KEY);
+  return fwd_pair_supported(p) && (p.flags & TTT_OUTPUT_KEY);
 }
 
 hipError_t launch_fwd_mfma_key(const ScanParams& p, hipStream_t stream) {
   const int nheads = p.B * p.H;
-  if (p.gelu == TTT_GELU_TANH)
-    hipLaunchKernelGGL(fwd_mfma_key_kernel<TTT_GELU_TANH>, dim3(nheads), dim3(NT), 0, stream, p);
-  else
-    hipLaunchKernelGGL(fwd_mfma_key_kernel<TTT_GELU_ERF>, dim3(nheads), dim3(NT), 0, stream, p);
+  const bool large = p.chunk > BC;
+  if (p.gelu == TTT_GELU_TANH) {
+    if (large)
+      hipLaunchKernelGGL((fwd_mfma_key_kernel<TTT_GELU_TANH, true>), dim3(nheads), dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_mfma_key_kernel<TTT_GELU_TANH, false>), dim3(nheads), dim3(NT), 0, stream, p);
+  } else {
+    if (large)
+      hipLaunchKernelGGL((fwd_mfma_key_kernel<TTT_GELU_ERF, true>), dim3(nheads), dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((fwd_mfma_key_kernel<TTT_GELU_ERF, false>), dim3(nheads), dim3(NT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

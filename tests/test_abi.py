@@ -130,6 +130,14 @@ def test_kernel_selection_names():
     assert ops.fwd_kernel_name(mlp_d64(output_key=True, B=64)) == "ttt_fwd_mfma_key_d64"
     assert ops.fwd_kernel_name(mlp_d64(output_key=True, io="f32")) == "ttt_fwd_generic"
     assert ops.fwd_kernel_name(mlp_d64(output_key=True, force_generic=True)) == "ttt_fwd_generic"
+    # ... and with mini-batches above 16 tokens (any head count); no decode or backward there
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, chunk=256)) == "ttt_fwd_mfma_key_d64"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, chunk=1024, B=64)) == "ttt_fwd_mfma_key_d64"
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, chunk=256, one_wg_per_head=True)) == "ttt_fwd_mfma_key_d64"
+    assert ops.workspace_size(mlp_d64(output_key=True, chunk=256)) == 256
+    assert ops.decode_kernel_name(mlp_d64(output_key=True, chunk=256)) == ""
+    assert ops.bwd_kernel_name(mlp_d64(output_key=True, chunk=256)) == ""
+    assert ops.fwd_kernel_name(mlp_d64(output_key=True, chunk=256, force_generic=True)) == ""
     assert ops.bwd_kernel_name(mlp_d64(output_key=True)) == "ttt_bwd_generic"
     assert ops.decode_kernel_name(mlp_d64(output_key=True)) == "ttt_decode_generic"
     assert ops.validate(mlp_d64(output_key=True)) == 0

@@ -22,8 +22,8 @@ def _run(cfg, d, **kw):
     return res
 
 
-def _check(res, inp, pairs, chunk, tol=TOL["bf16"]):
-    Z, WT, L = oracle_heads(inp, pairs, "mlp", chunk)
+def _check(res, inp, pairs, chunk, tol=TOL["bf16"], **cfg_kw):
+    Z, WT, L = oracle_heads(inp, pairs, "mlp", chunk, **cfg_kw)
     gz = torch.stack([res["Z"][b, h] for b, h in pairs]).cpu()
     assert_parity(gz, Z, tol, f"Z b={chunk}")
     for k, wt in enumerate(WT):
@@ -142,3 +142,17 @@ def test_large_chunk_bitwise_deterministic():
     a = _run(cfg, inp, want_loss=True)
     b = _run(cfg, inp, want_loss=True)
     assert torch.equal(a["Z"], b["Z"]) and torch.equal(a["loss"], b["loss"])
+
+
+@pytest.mark.parametrize("chunk,T", [(32, 512), (256, 1024), (1024, 2048)])
+def test_large_chunk_key_output(chunk, T):
+    """The key-side output rule (z_t = f(K_t; W at the mini-batch start)) with large
+    mini-batches on the key-output kernel (the producer alone), 144 heads (above the paired
+    kernel's head limit) of which six are checked at full T."""
+    B, H = 9, 16
+    inp = make_inputs(W, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
+    cfg = ops_config(W, B=B, H=H, T=T, chunk=chunk, output_key=True)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_key_d64"
+    note(f"large chunk key output b={chunk} B={B} H={H} T={T}")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    _check(res, inp, [(0, 0), (2, 5), (4, 9), (6, 13), (8, 15), (8, 0)], chunk, output="key")
