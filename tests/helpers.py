@@ -64,7 +64,8 @@ def fresh_inputs(w, **kw):
 
 
 # Localised bounds, on top of the whole-tensor relative L2. Calibrated on the oracle itself:
-# perturbing the inputs and W0 of configs 1-3 by relative noise (2^-9 and 1e-7) moves the
+# perturbing the inputs and W0 of the MLP d=16 fp32, Linear d=64 fp32 and MLP d=64 bf16 T=8192
+# workloads by relative noise (2^-9 and 1e-7) moves the
 # worst 16-token chunk by at most 1.9x the whole-tensor relative error and the worst single
 # token by at most 6.2x (outer gradients: 1.5x and 4.4x); the factors below leave 2x on top.
 # One entirely wrong token in a chunk moves that chunk by ~0.25 and itself by ~1, so both
