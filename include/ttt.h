@@ -250,8 +250,9 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
  *  W_T (nullable) [B,H,..], the weights after the last chunk.
  *  workspace: ttt_workspace_size(.., TTT_OP_LACT, ..) bytes (status word, then two weight
  *  buffers and the W2 column sums of every head, about 385 KiB per (batch, head)).
- *  Runs one launch per chunk (plus one) of the kernel "ttt_lact_fwd_d64" (bf16 MFMA
- *  products, fp32 weights and sums) and a copy-out for W_T. Errors as for ttt_scan_fwd;
+ *  Runs one launch per chunk plus one of the kernel
+ *  "ttt_lact_fwd_d64" (bf16 MFMA products, fp32 weights and sums); the W_T copy-out joins the
+ *  last launch (with TTT_LACT_READ_BEFORE it takes one more). Errors as for ttt_scan_fwd;
  *  a non-finite weight norm sets TTT_ERR_NONFINITE in the status word. */
 ttt_status ttt_lact_fwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
                         const float* eta, const ttt_swiglu_weights* W0, void* Z,

@@ -22,6 +22,8 @@
 //  - read-out blocks, one per (head, up to 512 tokens of a chunk): the weights as bf16 MFMA
 //    operands in LDS (96 KiB), each of the 8 waves computing z for 64 tokens at a time:
 //      A^Q^T = W1^T Q^T, C^Q^T = W3^T Q^T, U^T = SiLU(A^Q^T) C^Q^T, z^T = W2^T U^T.
+//  - copy-out blocks: W_T from the last state, in the launch that reads out the last chunk
+//    (or in a launch of their own when the read-out comes before the update).
 // The weights live in two state buffers of the workspace: the step that runs the gradient of
 // chunk i reads buffer i and writes buffer i + 1 while the read-out of chunk i - 1 (or, reading
 // before the update, of chunk i) reads buffer i, so both roles share one launch. Buffer 0 of
@@ -44,6 +46,7 @@ constexpr int ST = 128;          // tokens staged per barrier (64 when the chunk
 constexpr int KRS = D + 8;       // LDS row stride of staged K / V rows (bf16)
 constexpr int W_FLOATS = 3 * D * LH;  // W1, W3 [d][h] then W2 [h][d], fp32
 constexpr int OR = 64;           // tokens per read-out round of a wave
+constexpr int FP = 8;            // copy-out blocks per head
 
 struct GStage {
   alignas(16) __bf16 K[ST * KRS];
@@ -84,7 +87,12 @@ struct LactParams {
   int o_chunk;    // chunk this launch reads out (-1: none)
   int o_state;    // state the read-out uses (o_chunk or o_chunk + 1)
   int nG;         // gradient blocks (heads rounded up to 8, times NHB)
+  int nO;         // read-out blocks
   int tbo;        // tokens per read-out block
+  int f_state;    // state the copy-out blocks write to W_T (-1: none)
+  float* wt1;
+  float* wt2;
+  float* wt3;
 };
 
 // Weights of state k of a head: W1, W3 [d][h], W2 [h][d] (unnormalised for k >= 1) and the
@@ -466,6 +474,25 @@ __device__ void o_role(const LactParams& p, int head, int tb, LSmem& sm) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// copy-out role: W_T from the last state (W1, W3 as stored, W2 scaled by its column norms);
+// block (head, part) copies an eighth of each matrix as float4s
+// ---------------------------------------------------------------------------------------
+__device__ void f_role(const LactParams& p, int head, int part) {
+  const WRef in = wref(p, p.f_state, head);
+  const int f = part * NT + threadIdx.x;  // float4 index, D * LH / 4 = 4096 per matrix
+  const size_t o = static_cast<size_t>(head) * D * LH / 4 + f;
+  reinterpret_cast<float4*>(p.wt1)[o] = reinterpret_cast<const float4*>(in.w1)[f];
+  reinterpret_cast<float4*>(p.wt3)[o] = reinterpret_cast<const float4*>(in.w3)[f];
+  float4 v = reinterpret_cast<const float4*>(in.w2)[f];
+  const int d = (f & 15) * 4;  // W2 [h][d]: float4 f covers d .. d + 3 of row f / 16
+  v.x *= col_scale(in, d);
+  v.y *= col_scale(in, d + 1);
+  v.z *= col_scale(in, d + 2);
+  v.w *= col_scale(in, d + 3);
+  reinterpret_cast<float4*>(p.wt2)[o] = v;
+}
+
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 lact_step_kernel(LactParams p) {
   __shared__ LSmem sm;
@@ -474,29 +501,13 @@ lact_step_kernel(LactParams p) {
   if (b < p.nG) {
     xcd_map(b, NHB, head, sub);
     if (head < p.nheads) g_role(p, head, sub, sm);
-  } else {
+  } else if (b < p.nG + p.nO) {
     xcd_map(b - p.nG, p.chunk / p.tbo, head, sub);
     if (head < p.nheads) o_role(p, head, sub, sm);
+  } else {
+    const int f = b - p.nG - p.nO;
+    f_role(p, f / FP, f % FP);
   }
-}
-
-// W_T from the last state: W1, W3 as stored, W2 scaled by its column norms. Block (head, part)
-// copies a sixteenth of each matrix as float4s.
-__global__ void __launch_bounds__(256) lact_final_kernel(LactParams p, int k, float* wt1, float* wt2,
-                                                         float* wt3) {
-  const int head = blockIdx.x >> 4, part = blockIdx.x & 15;
-  const WRef in = wref(p, k, head);
-  const int f = part * 256 + threadIdx.x;  // float4 index, D * LH / 4 = 4096 per matrix
-  const size_t o = static_cast<size_t>(head) * D * LH / 4 + f;
-  reinterpret_cast<float4*>(wt1)[o] = reinterpret_cast<const float4*>(in.w1)[f];
-  reinterpret_cast<float4*>(wt3)[o] = reinterpret_cast<const float4*>(in.w3)[f];
-  float4 v = reinterpret_cast<const float4*>(in.w2)[f];
-  const int d = (f & 15) * 4;  // W2 [h][d]: float4 f covers d .. d + 3 of row f / 16
-  v.x *= col_scale(in, d);
-  v.y *= col_scale(in, d + 1);
-  v.z *= col_scale(in, d + 2);
-  v.w *= col_scale(in, d + 3);
-  reinterpret_cast<float4*>(wt2)[o] = v;
 }
 
 // Tokens per read-out block: the largest power-of-two multiple of 64 up to 512 that divides the
@@ -539,23 +550,34 @@ hipError_t launch_lact_fwd(const LactLaunch& L, hipStream_t stream) {
   p.state = L.work;
   p.part = L.work + 2 * static_cast<size_t>(p.nheads) * W_FLOATS;
   p.tbo = read_tokens(L.chunk);
+  p.wt1 = L.wt_1;
+  p.wt2 = L.wt_2;
+  p.wt3 = L.wt_3;
   const int nchunks = L.T / L.chunk;
   const int hpad = (p.nheads + 7) / 8 * 8;
   const bool before = (L.flags & TTT_LACT_READ_BEFORE) != 0;
   const int steps = before ? nchunks : nchunks + 1;
+  // the copy-out of W_T joins the launch that reads out the last chunk after its update; when
+  // the read-out comes first, the last state is written by the last launch and the copy-out
+  // takes a launch of its own
+  const int nF = L.wt_1 ? p.nheads * FP : 0;
   for (int s = 0; s < steps; ++s) {
     p.g_chunk = s < nchunks ? s : -1;
     p.o_chunk = before ? s : s - 1;
     p.o_state = s;  // chunk s read before its update, or chunk s - 1 after it: state s
     p.nG = p.g_chunk >= 0 ? hpad * NHB : 0;
-    const int nO = p.o_chunk >= 0 ? hpad * (L.chunk / p.tbo) : 0;
-    hipLaunchKernelGGL(lact_step_kernel, dim3(p.nG + nO), dim3(NT), 0, stream, p);
+    p.nO = p.o_chunk >= 0 ? hpad * (L.chunk / p.tbo) : 0;
+    const bool copy = !before && s == steps - 1 && nF > 0;
+    p.f_state = copy ? nchunks : -1;
+    hipLaunchKernelGGL(lact_step_kernel, dim3(p.nG + p.nO + (copy ? nF : 0)), dim3(NT), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (L.wt_1) {
-    hipLaunchKernelGGL(lact_final_kernel, dim3(p.nheads * 16), dim3(256), 0, stream, p, nchunks, L.wt_1,
-                       L.wt_2, L.wt_3);
+  if (before && nF > 0) {
+    p.g_chunk = p.o_chunk = -1;
+    p.nG = p.nO = 0;
+    p.f_state = nchunks;
+    hipLaunchKernelGGL(lact_step_kernel, dim3(nF), dim3(NT), 0, stream, p);
     return hipGetLastError();
   }
   return hipSuccess;
