@@ -31,7 +31,7 @@
  *    after a call returns.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
  *    Every call only enqueues work on it and returns; nothing synchronises the
- *    stream except ttt_read_status.
+ *    stream except ttt_read_status, and the debug mode below.
  *  - Errors: every argument, shape, dtype, alignment (16 bytes) and workspace check
  *    runs on the host before anything is enqueued, so a non-OK return means nothing
  *    ran. A failed launch returns TTT_ERR_HIP. A non-finite loss or output detected
@@ -41,6 +41,11 @@
  *    workgroups per head; the split d = 128 kernel, four) bound every wait; an expired
  *    wait sets TTT_ERR_TIMEOUT in the same word (the outputs of that call are then
  *    undefined).
+ *  - Debug mode: with the environment variable TTT_DEBUG set (to anything but "" or
+ *    "0"; read at every call), each entry point that enqueues work then synchronises
+ *    its stream and returns the device-side outcome itself: TTT_ERR_HIP if the stream
+ *    reports an error, else TTT_ERR_TIMEOUT or TTT_ERR_NONFINITE from the status word
+ *    (which stays set as usual), else TTT_OK.
  *  - No C++ exception crosses this interface. Calls that share a workspace must be
  *    ordered on one stream.
  */

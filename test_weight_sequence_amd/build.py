@@ -1,9 +1,10 @@
 """Build libttt.so (the gfx950 HIP kernels and the C-ABI host layer) in-tree.
 
-    python -m test_weight_sequence_amd.build
+    python -m test_weight_sequence_amd.build [--poison]
 
 Compiles every translation unit under csrc/ with hipcc for gfx950 and links them
-into test_weight_sequence_amd/libttt.so. Packed fp32 instructions are disabled for
+into test_weight_sequence_amd/libttt.so (with --poison, also the LDS-poisoning test
+build libttt_poison.so). Packed fp32 instructions are disabled for
 the device code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -18,6 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttt.so")
 BUILD = os.path.join(PKG, "_build")
+# Test build with every kernel's LDS filled with NaN bit patterns at entry (TTT_LDS_POISON);
+# tests/test_lds_poison_gpu.py runs parity cases on it. Never loaded by the product path.
+LIB_POISON = os.path.join(PKG, "libttt_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -60,6 +64,13 @@ def build(verbose: bool = True, lib: str = LIB, build_dir: str = BUILD, extra=()
     return lib
 
 
+def build_poison(verbose: bool = True) -> str:
+    """The LDS-poisoning test build of the same sources (libttt_poison.so)."""
+    return build(verbose, lib=LIB_POISON, build_dir=os.path.join(BUILD, "poison"), extra=("-DTTT_LDS_POISON",))
+
+
 if __name__ == "__main__":
     build()
+    if "--poison" in sys.argv[1:]:
+        build_poison()
     sys.exit(0)

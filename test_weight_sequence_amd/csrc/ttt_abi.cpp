@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -187,6 +188,23 @@ size_t bwd_ws_bytes(const ttt_config* c) {
 
 ttt_status map_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// TTT_DEBUG (an environment variable, set to anything but "" or "0"): every entry point that
+// enqueues work waits for it and returns the device-side outcome as its own status:
+// TTT_ERR_HIP if the stream reports an error, else TTT_ERR_TIMEOUT or TTT_ERR_NONFINITE from
+// the status word, else TTT_OK. Read at every call, so it can be switched while running.
+bool debug_mode() {
+  const char* e = std::getenv("TTT_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+ttt_status debug_finish(ttt_status st, const void* status_word, hipStream_t s) {
+  if (st != TTT_OK || !debug_mode()) return st;
+  if (hipStreamSynchronize(s) != hipSuccess) return TTT_ERR_HIP;
+  unsigned word = 0;
+  if (hipMemcpy(&word, status_word, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return TTT_ERR_HIP;
+  if (word & kStatusTimeout) return TTT_ERR_TIMEOUT;
+  return (word & kStatusNonFinite) ? TTT_ERR_NONFINITE : TTT_OK;
+}
+
 // Workspace of ttt_scan_fwd_static: a file-scope device array, one per GPU, held until the
 // process ends. In host code its name is only a stand-in; the device address of each GPU's
 // copy comes from hipGetSymbolAddress, taken once per device (with that device current) on
@@ -271,7 +289,8 @@ ttt_status ttt_lact_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   L.wt_3 = W_T ? W_T->w3 : nullptr;
   L.status = static_cast<unsigned*>(workspace);
   L.work = reinterpret_cast<float*>(static_cast<char*>(workspace) + kStatusBytes);
-  return map_hip(launch_lact_fwd(L, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return debug_finish(map_hip(launch_lact_fwd(L, s)), workspace, s);
 }
 
 bool use_mom(const ttt_config* c) {
@@ -407,8 +426,9 @@ ttt_status ttt_scan_fwd(const ttt_config* cfg, const void* Q, const void* K, con
   if (!workspace) return TTT_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TTT_ERR_ALIGN;
   if (ws_bytes < fwd_ws_bytes(cfg)) return TTT_ERR_WORKSPACE;
-  return fwd_launch(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved, workspace,
-                    static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return debug_finish(fwd_launch(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved, workspace, s),
+                      workspace, s);
 }
 
 ttt_status ttt_scan_fwd_static(const ttt_config* cfg, const void* Q, const void* K, const void* V,
@@ -426,8 +446,8 @@ ttt_status ttt_scan_fwd_static(const ttt_config* cfg, const void* Q, const void*
   // every kernel that uses the rest of the region clears or initialises what it reads
   if (launch_reset_status(ws, s) != hipSuccess) return TTT_ERR_HIP;
   st = fwd_launch(cfg, Q, K, V, eta, ln_gamma, ln_beta, W0, Z, W_T, loss, saved, ws, s);
-  if (st != TTT_OK || !status_out) return st;
-  return map_hip(launch_copy_status(ws, status_out, s));
+  if (st == TTT_OK && status_out) st = map_hip(launch_copy_status(ws, status_out, s));
+  return debug_finish(st, ws, s);
 }
 
 ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const void* K, const void* V,
@@ -481,8 +501,8 @@ ttt_status ttt_scan_fwd_momentum(const ttt_config* cfg, const void* Q, const voi
   p.st_1 = S_T ? S_T->w1 : nullptr;
   p.st_2 = (S_T && mlp) ? S_T->w2 : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_mom(cfg) && fwd_mom_fits()) return map_hip(launch_fwd_mfma_mom(p, s));
-  return map_hip(launch_fwd_generic(p, s));
+  if (use_mom(cfg) && fwd_mom_fits()) return debug_finish(map_hip(launch_fwd_mfma_mom(p, s)), workspace, s);
+  return debug_finish(map_hip(launch_fwd_generic(p, s)), workspace, s);
 }
 
 ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, const void* V,
@@ -557,7 +577,7 @@ ttt_status ttt_scan_bwd(const ttt_config* cfg, const void* Q, const void* K, con
     e = tuned ? launch_bwd_mfma(p, s) : launch_bwd_generic(p, s);
   }
   if (e != hipSuccess) return TTT_ERR_HIP;
-  return map_hip(launch_bwd_finalize(p, s));
+  return debug_finish(map_hip(launch_bwd_finalize(p, s)), workspace, s);
 }
 
 ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, const void* v,
@@ -608,8 +628,8 @@ ttt_status ttt_decode_step(const ttt_config* cfg, const void* q, const void* k, 
   p.status = static_cast<unsigned*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_decode_split(cfg))
-    return map_hip(launch_decode_split(p, static_cast<char*>(workspace) + kStatusBytes, s));
-  return map_hip(use_decode_stream(cfg) ? launch_decode_stream(p, s) : launch_decode(p, s));
+    return debug_finish(map_hip(launch_decode_split(p, static_cast<char*>(workspace) + kStatusBytes, s)), workspace, s);
+  return debug_finish(map_hip(use_decode_stream(cfg) ? launch_decode_stream(p, s) : launch_decode(p, s)), workspace, s);
 }
 
 ttt_status ttt_read_status(const void* workspace, void* stream) {

@@ -34,6 +34,7 @@ static_assert(A_COUNT == kBwdArrays, "per-head workspace layout");
 struct LdsB {
   float *K, *V, *Q, *dO, *XK, *R, *D2, *E2, *XQ, *DZQ, *DE2, *DZK, *DQ, *DK, *DV;
   float *rk, *rq, *eta, *mgx, *P1, *P2, *dP1, *dP2, *red;
+  float* end;  // one past the last float used
 };
 
 __device__ __forceinline__ LdsB carve_b(float* p, int b, int d) {
@@ -53,6 +54,7 @@ __device__ __forceinline__ LdsB carve_b(float* p, int b, int d) {
   s.dP1 = p; p += b * b;
   s.dP2 = p; p += b * b;
   s.red = p;  // 2 * NT floats for the final gamma/beta reduction
+  s.end = p + 2 * NT;
   return s;
 }
 
@@ -73,6 +75,8 @@ __global__ void __launch_bounds__(NT) bwd_generic_kernel(BwdParams p) {
   const size_t nW2 = KIND == TTT_MLP ? static_cast<size_t>(h) * d : 0;
   const size_t nW = nW1 + nW2;
   LdsB s = carve_b(lds_raw, b, d);
+  TTT_POISON_BYTES(lds_raw, (s.end - lds_raw) * sizeof(float));
+  TTT_POISON_DONE();
   float* work = p.work + static_cast<size_t>(bh) * bwd_work_floats_per_head(KIND, d, h, b);
   float* dW1 = work;
   float* dW2 = work + nW1;

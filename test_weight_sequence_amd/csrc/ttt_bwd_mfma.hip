@@ -168,6 +168,8 @@ template <int GELU_KIND>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_mfma_kernel(BwdParams p) {
   __shared__ BSmem sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;

@@ -241,6 +241,8 @@ template <int GELU_KIND>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_split_kernel(BwdParams p, BSplit x) {
   __shared__ BSmem sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   // block -> (head, part): the parts of a head are 8 blocks apart (same XCD)
   const int b = blockIdx.x;
   const int s = (b >> 3) % S;

@@ -21,6 +21,17 @@ __global__ void __launch_bounds__(NT) decode_kernel(DecodeParams p) {
   __shared__ float sA[MAXH], sG[MAXH], sAQ[MAXH];
   __shared__ float sPart[NT];
   __shared__ float sEta;
+  TTT_POISON(sq);
+  TTT_POISON(sk);
+  TTT_POISON(sv);
+  TTT_POISON(sZ);
+  TTT_POISON(sE);
+  TTT_POISON(sA);
+  TTT_POISON(sG);
+  TTT_POISON(sAQ);
+  TTT_POISON(sPart);
+  TTT_POISON(sEta);
+  TTT_POISON_DONE();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x, hidx = bh % p.H;
   const int d = p.d, h = p.hid;

@@ -173,6 +173,22 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(DecodeParams p, unsign
   __shared__ float4 red2[NWV][D / 4];   // [wave][d/4]: A W2 partials
   __shared__ float sEta, sQK;
   __shared__ unsigned sh_local;
+  TTT_POISON(sq);
+  TTT_POISON(sk);
+  TTT_POISON(sv);
+  TTT_POISON(sE2);
+  TTT_POISON(sA);
+  TTT_POISON(sG);
+  TTT_POISON(sE1);
+  TTT_POISON(sPQ);
+  TTT_POISON(sAQ);
+  TTT_POISON(red1);
+  TTT_POISON(redq);
+  TTT_POISON(red2);
+  TTT_POISON(sEta);
+  TTT_POISON(sQK);
+  TTT_POISON(sh_local);
+  TTT_POISON_DONE();
   // block -> (head, part): the parts of a head are 8 blocks apart (same XCD)
   const int blk = blockIdx.x;
   const int s = (blk >> 3) % SP;

@@ -44,6 +44,21 @@ __global__ void __launch_bounds__(NT) decode_stream_kernel(DecodeParams p) {
   __shared__ float4 redq[NWV][HID / 4];  // [row block][h]: q (W1 - acc1) partials (acc1 before this token)
   __shared__ float4 red2[NWV][D / 4];    // [wave][d]: A W2 partials
   __shared__ float sEta, sQK;
+  TTT_POISON(sq);
+  TTT_POISON(sk);
+  TTT_POISON(sv);
+  TTT_POISON(sE2);
+  TTT_POISON(sA);
+  TTT_POISON(sG);
+  TTT_POISON(sE1);
+  TTT_POISON(sPQ);
+  TTT_POISON(sAQ);
+  TTT_POISON(red1);
+  TTT_POISON(redq);
+  TTT_POISON(red2);
+  TTT_POISON(sEta);
+  TTT_POISON(sQK);
+  TTT_POISON_DONE();
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.x, hidx = bh % p.H;
   const bool commit = p.pos == p.chunk - 1;

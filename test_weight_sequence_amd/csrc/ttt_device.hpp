@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "ttt_internal.h"
+#include "ttt_poison.hpp"  // test-build instrumentation (TTT_POISON)
 
 #define TTT_HD __device__ __forceinline__
 #define TTT_EXP2(x) __builtin_amdgcn_exp2f(x)

@@ -40,6 +40,7 @@ constexpr int MAXB = kMaxChunk;
 struct Lds {
   float *K, *V, *Q, *E, *A, *G, *AQ, *Z, *ZQ, *S;
   float *C, *Dl, *Av, *Bv;  // momentum coefficients: C [b x b], last row of D, A_t, B_t, P_b
+  float* end;               // one past the last float used
 };
 
 __device__ __forceinline__ Lds carve(float* base, int kind, int b, int d, int h, bool mom) {
@@ -67,6 +68,7 @@ __device__ __forceinline__ Lds carve(float* base, int kind, int b, int d, int h,
   } else {
     s.C = s.Dl = s.Av = s.Bv = nullptr;
   }
+  s.end = p;
   return s;
 }
 
@@ -99,6 +101,8 @@ __global__ void __launch_bounds__(NT) fwd_generic_kernel(ScanParams p) {
   const size_t nW2 = KIND == TTT_MLP ? static_cast<size_t>(h) * d : 0;
   const size_t nW = nW1 + nW2;
   Lds s = carve(lds_raw, KIND, b, d, h, MOM);
+  TTT_POISON_BYTES(lds_raw, (s.end - lds_raw) * sizeof(float));
+  TTT_POISON_DONE();
 
   float* W1 = p.wbuf + static_cast<size_t>(bh) * (MOM ? 2 * nW : nW);
   float* W2 = W1 + nW1;

@@ -55,6 +55,8 @@ fwd_mfma_kernel(ScanParams p) {
   using LdT = typename SV::T;
 
   __shared__ Smem<NW> sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;

@@ -265,6 +265,8 @@ template <int GELU_KIND>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mom_kernel(ScanParams p, Split x) {
   __shared__ Smem sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   // block -> (head, part): the S parts of a head are 8 blocks apart (same XCD)
   const int b = blockIdx.x;
   const int s = (b >> 3) % S;
@@ -277,6 +279,8 @@ fwd_mom_kernel(ScanParams p, Split x) {
   const int T = p.T, nchunks = T / BC;
   const bool per_seq = (p.flags & TTT_W0_PER_SEQ) != 0;
   __shared__ unsigned sh_local;
+  TTT_POISON(sh_local);
+  TTT_POISON_DONE();
   XMem m;
   m.xz = x.xbuf + static_cast<size_t>(bh) * kHeadXFloats;
   m.xq = m.xz + 2 * 2 * S * kPartFloats;

@@ -815,6 +815,8 @@ template <int GELU_KIND, bool LARGE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_pair_kernel(ScanParams p, Pair q) {
   __shared__ SmemP sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   Ctx x;
   x.tid = threadIdx.x;
   x.lane = x.tid & 63;
@@ -870,6 +872,8 @@ template <int GELU_KIND, bool LARGE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_mfma_key_kernel(ScanParams p) {
   __shared__ ProdSmem sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   Ctx x;
   x.tid = threadIdx.x;
   x.lane = x.tid & 63;

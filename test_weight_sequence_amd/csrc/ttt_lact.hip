@@ -496,6 +496,8 @@ __device__ void f_role(const LactParams& p, int head, int part) {
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 lact_step_kernel(LactParams p) {
   __shared__ LSmem sm;
+  TTT_POISON(sm);
+  TTT_POISON_DONE();
   const int b = blockIdx.x;
   int head, sub;
   if (b < p.nG) {

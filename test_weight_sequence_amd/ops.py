@@ -10,6 +10,7 @@ decode_kernel_name.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -63,48 +64,71 @@ class CSwiGLUWeights(ctypes.Structure):
 
 
 _lib = None
+_loaded = {}
+
+
+def _load(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` and declare its entry points (raises if the
+    file has not been built)."""
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m test_weight_sequence_amd.build`")
+    L = ctypes.CDLL(path)
+    P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    cfgp = ctypes.POINTER(CConfig)
+    wp = ctypes.POINTER(CWeights)
+    L.ttt_validate.argtypes = [cfgp]
+    L.ttt_workspace_size.argtypes = [cfgp, I32, ctypes.POINTER(S)]
+    L.ttt_saved_size.argtypes = [cfgp, ctypes.POINTER(S)]
+    L.ttt_scan_fwd.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, S, P]
+    L.ttt_scan_fwd_static.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, P]
+    L.ttt_scan_fwd_momentum.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, wp, P, wp, wp, P, P, S, P]
+    L.ttt_scan_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, P, P, P, P, wp, P, P, P, S, P]
+    L.ttt_decode_step.argtypes = [cfgp, P, P, P, P, P, P, wp, wp, I32, P, P, S, P]
+    sp = ctypes.POINTER(CSwiGLUWeights)
+    L.ttt_lact_fwd.argtypes = [cfgp, P, P, P, P, sp, P, sp, P, S, P]
+    L.ttt_read_status.argtypes = [P, P]
+    L.ttt_reset_status.argtypes = [P, P]
+    L.ttt_fwd_kernel_name.argtypes = [cfgp]
+    L.ttt_fwd_kernel_name.restype = ctypes.c_char_p
+    L.ttt_fwd_momentum_kernel_name.argtypes = [cfgp]
+    L.ttt_fwd_momentum_kernel_name.restype = ctypes.c_char_p
+    L.ttt_bwd_kernel_name.argtypes = [cfgp]
+    L.ttt_bwd_kernel_name.restype = ctypes.c_char_p
+    L.ttt_decode_kernel_name.argtypes = [cfgp]
+    L.ttt_decode_kernel_name.restype = ctypes.c_char_p
+    L.ttt_status_str.argtypes = [I32]
+    L.ttt_status_str.restype = ctypes.c_char_p
+    for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
+                 "ttt_scan_fwd_static", "ttt_scan_fwd_momentum",
+                 "ttt_scan_bwd", "ttt_decode_step", "ttt_lact_fwd", "ttt_read_status",
+                 "ttt_reset_status", "ttt_abi_version"):
+        getattr(L, name).restype = I32
+    _loaded[path] = L
+    return L
 
 
 def lib() -> ctypes.CDLL:
     """Load libttt.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
-                               "`python -m test_weight_sequence_amd.build`")
-        L = ctypes.CDLL(_LIB_PATH)
-        P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
-        cfgp = ctypes.POINTER(CConfig)
-        wp = ctypes.POINTER(CWeights)
-        L.ttt_validate.argtypes = [cfgp]
-        L.ttt_workspace_size.argtypes = [cfgp, I32, ctypes.POINTER(S)]
-        L.ttt_saved_size.argtypes = [cfgp, ctypes.POINTER(S)]
-        L.ttt_scan_fwd.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, S, P]
-        L.ttt_scan_fwd_static.argtypes = [cfgp, P, P, P, P, P, P, wp, P, wp, P, P, P, P]
-        L.ttt_scan_fwd_momentum.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, wp, P, wp, wp, P, P, S, P]
-        L.ttt_scan_bwd.argtypes = [cfgp, P, P, P, P, P, P, P, P, wp, P, P, P, P, wp, P, P, P, S, P]
-        L.ttt_decode_step.argtypes = [cfgp, P, P, P, P, P, P, wp, wp, I32, P, P, S, P]
-        sp = ctypes.POINTER(CSwiGLUWeights)
-        L.ttt_lact_fwd.argtypes = [cfgp, P, P, P, P, sp, P, sp, P, S, P]
-        L.ttt_read_status.argtypes = [P, P]
-        L.ttt_reset_status.argtypes = [P, P]
-        L.ttt_fwd_kernel_name.argtypes = [cfgp]
-        L.ttt_fwd_kernel_name.restype = ctypes.c_char_p
-        L.ttt_fwd_momentum_kernel_name.argtypes = [cfgp]
-        L.ttt_fwd_momentum_kernel_name.restype = ctypes.c_char_p
-        L.ttt_bwd_kernel_name.argtypes = [cfgp]
-        L.ttt_bwd_kernel_name.restype = ctypes.c_char_p
-        L.ttt_decode_kernel_name.argtypes = [cfgp]
-        L.ttt_decode_kernel_name.restype = ctypes.c_char_p
-        L.ttt_status_str.argtypes = [I32]
-        L.ttt_status_str.restype = ctypes.c_char_p
-        for name in ("ttt_validate", "ttt_workspace_size", "ttt_saved_size", "ttt_scan_fwd",
-                     "ttt_scan_fwd_static", "ttt_scan_fwd_momentum",
-                     "ttt_scan_bwd", "ttt_decode_step", "ttt_lact_fwd", "ttt_read_status",
-                     "ttt_reset_status", "ttt_abi_version"):
-            getattr(L, name).restype = I32
-        _lib = L
+        _lib = _load(_LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Inside the with-block every call of this module goes to the build of the library at
+    `path` (tests use it for the LDS-poisoning test build); afterwards to libttt.so again."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 @dataclass(frozen=True)

@@ -700,6 +700,27 @@ def test_nonfinite_input_sets_status(force_generic):
     assert ops.read_status(ws) == 0
 
 
+def test_debug_mode_returns_device_status(monkeypatch):
+    """With TTT_DEBUG set, an entry point waits for its kernels and returns the status word's
+    outcome itself: the NaN-injected forward fails with TTT_ERR_NONFINITE at the call, a clean
+    one returns TTT_OK; without it the call returns TTT_OK and the status word holds the error."""
+    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"]
+    bad = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
+    bad["K"][0, 0, 21, 9] = float("nan")
+    clean = make_inputs(w, batch_idx=[0], head_idx=[0, 1], T=64)
+    cfg = ops_config(w, T=64, B=1, H=2)
+    note("TTT_DEBUG on the paired forward")
+    monkeypatch.setenv("TTT_DEBUG", "1")
+    with pytest.raises(ops.TTTError) as err:
+        _run(cfg, to_dev(bad))
+    assert err.value.code == 8
+    res = _run(cfg, to_dev(clean))
+    assert ops.read_status(res["workspace"]) == 0
+    monkeypatch.setenv("TTT_DEBUG", "0")
+    res = _run(cfg, to_dev(bad))
+    assert ops.read_status(res["workspace"]) == 8
+
+
 @pytest.mark.parametrize("kernel", ["pair", "split"])
 def test_device_scope_handoff(kernel):
     """The tuned forwards with their cross-workgroup hand-offs forced onto the device-scope
