@@ -69,6 +69,44 @@ def test_lact_small(chunk, T, read_before, per_seq, eta_scale):
     _check(res, Zo, WTo, B * H)
 
 
+def test_lact_one_chunk_spans_the_sequence():
+    """chunk = T = 4096: one gradient over the whole sequence (32 staging rounds per gradient
+    block), then the read-out of every token with the updated weights."""
+    inp = make_inputs(W.with_(chunk=4096), batch_idx=[1], head_idx=[0, 6], T=4096)
+    cfg = _config(1, 2, 4096, 4096)
+    note("lact chunk = T = 4096")
+    res = _run(cfg, to_dev(inp))
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    Zo, WTo = _oracle(inp, 4096)
+    _check(res, Zo, WTo, 2)
+
+
+def test_lact_many_heads_sampled():
+    """192 (batch, head) pairs (B = 16, H = 12; more than the 128 a paired launch may hold, and
+    not a multiple of the block grouping per XCD in the last group), T = 512, chunks of 256;
+    the oracle checks four heads spread over the grid."""
+    B, H, T, chunk = 16, 12, 512, 256
+    inp = make_inputs(W.with_(chunk=chunk, B=B), batch_idx=list(range(B)), T=T)
+    cfg = _config(B, H, T, chunk)
+    note("lact 192 heads")
+    res = _run(cfg, to_dev(inp))
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    pairs = [(0, 0), (5, 11), (10, 3), (15, 7)]
+    Zs, WTs = [], []
+    for b, h in pairs:
+        sub = make_inputs(W.with_(chunk=chunk, B=B), batch_idx=[b], head_idx=[h], T=T)
+        Zo, WTo = _oracle(sub, chunk)
+        Zs.append(Zo[0])
+        WTs.append(WTo)
+    gz = torch.stack([res["Z"][b, h] for b, h in pairs]).cpu()
+    assert_parity(gz, torch.stack(Zs), TOL["bf16"], "Z")
+    for k in range(3):
+        g = torch.stack([res["W_T"][k][b, h] for b, h in pairs]).cpu()
+        assert_parity(g, torch.stack([wt[k][0] for wt in WTs]), TOL["bf16"], f"W_T[{k}]", time_axis=False)
+
+
 def test_lact_full_size_sampled_heads():
     """The full launch at B=8, H=12, T=8192, chunks of 2048; the oracle checks three heads at
     full T (heads are independent)."""
