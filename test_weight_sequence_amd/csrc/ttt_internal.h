@@ -135,10 +135,10 @@ hipError_t launch_lact_fwd(const LactLaunch& L, hipStream_t s);
 bool fwd_key_supported(const ScanParams& p);
 hipError_t launch_fwd_mfma_key(const ScanParams& p, hipStream_t s);
 // Forward for the d = 128, hidden = 512 head: each head split by hidden units over four
-// workgroups that exchange [chunk x d] partial sums through the workspace.
+// workgroups that exchange [chunk x d] partial sums through the workspace; up to the heads one
+// launch holds, four more workgroups per head take the query side (producer/consumer form).
 bool fwd_split_supported(const ScanParams& p);
 size_t fwd_split_workspace_bytes(int nheads);
-int fwd_split_blocks(int nheads);
 bool fwd_split_fits(int nheads);
 hipError_t launch_fwd_mfma_split(const ScanParams& p, hipStream_t s);
 // Momentum / forget-gate forward for the d = 64, hidden = 256 bf16 head: each head split by

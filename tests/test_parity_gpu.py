@@ -229,6 +229,27 @@ def test_split_more_heads_than_one_launch():
     _check_heads(res, inp, [(0, 0), (3, 5), (7, 7), (8, 0), (8, 7)], w, TOL["bf16"])
 
 
+@pytest.mark.parametrize("B,H", [(4, 8), (5, 8)])
+def test_split_forms_at_the_launch_boundary(B, H):
+    """The d=128 kernel takes its producer/consumer form (eight workgroups per head) while all
+    heads fit in one launch of it (32 heads on 256 CUs) and the form with both sides in every
+    workgroup above that: 32 heads fill a whole launch of the first, 40 heads take the second.
+    Heads from the first and the last group of eight against the oracle. The inputs are this
+    head shape's without the AR(1) drift: over the first chunks of the drifting inputs the
+    oracle itself moves by 5-24% on some heads when they are perturbed at the bf16 scale, which
+    would leave a whole-tensor bound nothing to decide; here it moves by about 0.5%."""
+    w = WORKLOADS["ttt_mlp_bf16_d128_T128k"].with_(drift=0.0)
+    T = 48
+    inp = make_inputs(w.with_(B=B, H=H), T=T)
+    cfg = ops_config(w, T=T, B=B, H=H)
+    assert ops.fwd_kernel_name(cfg) == "ttt_fwd_mfma_split_d128"
+    note(f"split {B * H} heads")
+    res = _run(cfg, to_dev(inp), want_loss=True)
+    torch.cuda.synchronize()
+    assert ops.read_status(res["workspace"]) == 0
+    _check_heads(res, inp, [(0, 0), (1, 7), (B - 1, 0), (B - 1, H - 1)], w, TOL["bf16"])
+
+
 def test_split_saved_chunk_start_weights():
     """The split kernel's saved buffer: W0 exactly at chunk 0, and at chunk 2 the W_T of a
     scan over the first two chunks."""
