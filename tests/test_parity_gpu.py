@@ -742,14 +742,21 @@ def test_debug_mode_returns_device_status(monkeypatch):
     assert ops.read_status(res["workspace"]) == 8
 
 
-@pytest.mark.parametrize("kernel", ["pair", "split"])
+@pytest.mark.parametrize("kernel", ["pair", "split", "split_wide"])
 def test_device_scope_handoff(kernel):
     """The tuned forwards with their cross-workgroup hand-offs forced onto the device-scope
     path (atomics and fences, as when the workgroups of a head sit on different XCDs): same
     kernel, status clean, every head against the oracle, and the same result as the default
     same-XCD path up to bf16 noise."""
-    w = WORKLOADS["ttt_mlp_bf16_d64_T8k"] if kernel == "pair" else WORKLOADS["ttt_mlp_bf16_d128_T128k"]
-    B, H, T = (2, 5, 96) if kernel == "pair" else (1, 3, 64)
+    # split: the d = 128 kernel's producer/consumer form (3 heads); split_wide: its form with
+    # both sides in every workgroup (40 heads, more than one launch of the other form holds;
+    # drift-free inputs, see test_split_forms_at_the_launch_boundary)
+    if kernel == "pair":
+        w, (B, H, T) = WORKLOADS["ttt_mlp_bf16_d64_T8k"], (2, 5, 96)
+    elif kernel == "split":
+        w, (B, H, T) = WORKLOADS["ttt_mlp_bf16_d128_T128k"], (1, 3, 64)
+    else:
+        w, (B, H, T) = WORKLOADS["ttt_mlp_bf16_d128_T128k"].with_(drift=0.0, B=5, H=8), (5, 8, 32)
     inp = make_inputs(w, batch_idx=list(range(B)), head_idx=list(range(H)), T=T)
     cfg = ops_config(w, B=B, H=H, T=T, device_scope=True)
     name = "ttt_fwd_mfma_pair_d64" if kernel == "pair" else "ttt_fwd_mfma_split_d128"
@@ -759,7 +766,8 @@ def test_device_scope_handoff(kernel):
     res = _run(cfg, d, want_loss=True)
     torch.cuda.synchronize()
     assert ops.read_status(res["workspace"]) == 0
-    _check_heads(res, inp, [(b, h) for b in range(B) for h in range(H)], w, TOL["bf16"])
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    _check_heads(res, inp, pairs if kernel != "split_wide" else [(0, 0), (2, 3), (4, 7)], w, TOL["bf16"])
     ref = _run(ops_config(w, B=B, H=H, T=T), d)
     torch.cuda.synchronize()
     # the two paths move the same values; only the hand-off mechanism differs
