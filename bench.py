@@ -60,12 +60,16 @@ KERNEL_SOURCES = {
 
 
 def _source_hash(kernel: str) -> str:
-    """Hash of the kernel's product source. Lines of the LDS-poisoning test instrumentation
-    (those naming TTT_POISON) compile to nothing in the product library and are left out."""
+    """Hash of the kernel's product source and of the scheduler flags it is built with beyond
+    the common ones. Lines of the LDS-poisoning test instrumentation (those naming TTT_POISON)
+    compile to nothing in the product library and are left out."""
+    from test_weight_sequence_amd.build import ITER_ILP, ITER_ILP_FLAGS
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "test_weight_sequence_amd", "csrc", name), "rb") as fh:
             h.update(b"".join(l for l in fh.read().splitlines(keepends=True) if b"TTT_POISON" not in l))
+    if KERNEL_SOURCES[kernel][0] in ITER_ILP:
+        h.update(" ".join(ITER_ILP_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,11 +33,27 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
 # with this option the compiler crashes in its AGPR-copy rewrite pass on that kernel.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 NO_VGPR_FORM = {"ttt_bwd_mfma.hip"}
+# The machine scheduler's iterative ILP strategy for the chunk-scan kernels: their time is a
+# chain of dependent phases per chunk, and this strategy orders each phase for latency rather
+# than register pressure. Interleaved A/Bs of the two builds on one MI355X (kernel ms by
+# hipEvents, same outputs to the parity tolerances): paired d=64 1.046 -> 1.020, key output
+# 0.996 -> 0.959, one workgroup per head at B=16 1.608 -> 1.580, momentum 2.487 -> 2.455,
+# backward 5.244 -> 5.190, split d=128 39.53 -> 37.52, large-chunk layer 0.450 -> 0.445. The
+# decode kernel measured no better (11.2 vs 11.3 us) and keeps the default.
+ITER_ILP = {"ttt_fwd_mfma_pair.hip", "ttt_fwd_mfma.hip", "ttt_fwd_mfma_mom.hip",
+            "ttt_fwd_mfma_split.hip", "ttt_bwd_mfma_split.hip", "ttt_lact.hip"}
+ITER_ILP_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+
+
+def source_flags(name: str) -> list:
+    """Compiler flags of the product build of csrc/<name> beyond COMMON."""
+    return (([] if name in NO_VGPR_FORM else VGPR_FORM) +
+            (ITER_ILP_FLAGS if name in ITER_ILP else []))
 
 
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    flags = COMMON + list(extra) + ([] if os.path.basename(src) in NO_VGPR_FORM else VGPR_FORM)
+    flags = COMMON + list(extra) + source_flags(os.path.basename(src))
     cmd = [HIPCC, *flags, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *flags, "-x", "hip", "-c", src, "-o", obj]
